@@ -1,0 +1,130 @@
+// C ABI of libkda (declared in include/kda.h): argument validation, workspace
+// sizing and dispatch to the kernel launchers. No device work is enqueued
+// unless every argument checks out.
+#include "kda.h"
+#include "kda_internal.h"
+
+#include <limits.h>
+
+#include <initializer_list>
+
+namespace {
+
+bool supported_dims(int32_t Dk, int32_t Dv) { return Dk == Dv && (Dk == 16 || Dk == 128); }
+
+// Validates cu_seqlens_host; on success returns total tokens and chunks.
+bool scan_lengths(const int32_t* cu, int32_t num_seqs, int64_t* tokens, int64_t* chunks) {
+  if (!cu || num_seqs < 0 || cu[0] != 0) return false;
+  int64_t c = 0;
+  for (int32_t n = 0; n < num_seqs; ++n) {
+    if (cu[n + 1] < cu[n]) return false;
+    c += (cu[n + 1] - cu[n] + KDA_CHUNK - 1) / KDA_CHUNK;
+  }
+  *tokens = cu[num_seqs];
+  *chunks = c;
+  return c <= INT32_MAX;
+}
+
+kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+// Every tensor pointer must be 16-byte aligned (NULL passes).
+bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if ((uintptr_t)p & 15) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: unsupported head size or dtype";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP runtime error";
+  }
+  return "KDA: unknown status";
+}
+
+int64_t kda_prefill_num_checkpoints(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                    int32_t ckpt_interval) {
+  int64_t tokens, chunks;
+  if (!scan_lengths(cu_seqlens_host, num_seqs, &tokens, &chunks)) return -1;
+  if (ckpt_interval <= 0) return 0;
+  int64_t total = 0;
+  for (int32_t n = 0; n < num_seqs; ++n)
+    total += (cu_seqlens_host[n + 1] - cu_seqlens_host[n]) / ckpt_interval;
+  return total;
+}
+
+size_t kda_prefill_workspace_size(const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
+                                  int32_t Dk, int32_t Dv) {
+  int64_t tokens, chunks;
+  if (H <= 0 || !supported_dims(Dk, Dv) || !scan_lengths(cu_seqlens_host, num_seqs, &tokens, &chunks))
+    return 0;
+  return kda::prefill_layout(num_seqs, chunks, H, Dk).total;
+}
+
+kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_dtype dtype,
+                               const float* g, const float* beta, const int32_t* cu_seqlens,
+                               const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
+                               int32_t Dk, int32_t Dv, float scale, float g_min,
+                               const float* initial_state, float* final_state,
+                               int32_t ckpt_interval, float* checkpoints, void* o,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
+  if (!supported_dims(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+  int64_t tokens, chunks;
+  if (H <= 0 || num_seqs < 0 || !cu_seqlens || !scan_lengths(cu_seqlens_host, num_seqs, &tokens, &chunks))
+    return KDA_ERR_INVALID_ARG;
+  if ((int64_t)num_seqs * H * (Dv / 16) > INT32_MAX || tokens * (int64_t)H > INT32_MAX)
+    return KDA_ERR_INVALID_ARG;
+  if (tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARG;
+  if (ckpt_interval < 0 || (ckpt_interval > 0 && ckpt_interval % KDA_CHUNK != 0))
+    return KDA_ERR_INVALID_ARG;
+  const int64_t nck = kda_prefill_num_checkpoints(cu_seqlens_host, num_seqs, ckpt_interval);
+  if (nck > 0 && !checkpoints) return KDA_ERR_INVALID_ARG;
+  if (!aligned16({q, k, v, g, beta, cu_seqlens, initial_state, final_state, checkpoints, o}))
+    return KDA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return KDA_OK;
+  const kda::PrefillLayout L = kda::prefill_layout(num_seqs, chunks, H, Dk);
+  if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255)) return KDA_ERR_WORKSPACE;
+
+  kda::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs; a.H = H; a.D = Dk;
+  a.total_tokens = tokens; a.total_chunks = chunks;
+  a.scale = scale; a.g_min = g_min;
+  a.initial_state = initial_state; a.final_state = final_state;
+  a.ckpt_interval = nck > 0 ? ckpt_interval : 0;
+  a.checkpoints = checkpoints;
+  a.o = o; a.workspace = workspace;
+  a.bf16 = dtype == KDA_BF16;
+  a.stream = stream;
+  return from_hip(kda::launch_prefill(a));
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype dtype,
+                           const float* g, const float* beta, float* state, void* o, int32_t N,
+                           int32_t H, int32_t Dk, int32_t Dv, float scale, float g_min,
+                           hipStream_t stream) {
+  if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
+  if (!supported_dims(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+  if (N < 0 || H <= 0 || (int64_t)N * H > INT32_MAX) return KDA_ERR_INVALID_ARG;
+  if (N == 0) return KDA_OK;
+  if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
+  if (!aligned16({q, k, v, g, beta, state, o})) return KDA_ERR_INVALID_ARG;
+  kda::DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
+  a.N = N; a.H = H; a.D = Dk;
+  a.scale = scale; a.g_min = g_min;
+  a.bf16 = dtype == KDA_BF16;
+  a.stream = stream;
+  return from_hip(kda::launch_decode(a));
+}
+
+}  // extern "C"

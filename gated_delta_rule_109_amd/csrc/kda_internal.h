@@ -1,0 +1,55 @@
+// Host-side interface between the C ABI (kda_api.hip) and the kernel launchers.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+  const void *q, *k, *v;
+  const float *g, *beta;
+  float* state;
+  void* o;
+  int32_t N, H, D;
+  float scale, g_min;
+  bool bf16;
+  hipStream_t stream;
+};
+
+struct PrefillArgs {
+  const void *q, *k, *v;
+  const float *g, *beta;
+  const int32_t* cu_seqlens;  // device
+  int32_t num_seqs, H, D;
+  int64_t total_tokens;
+  int64_t total_chunks;       // sum_n ceil(L_n / 16), from the host copy
+  float scale, g_min;
+  const float* initial_state;
+  float* final_state;
+  int32_t ckpt_interval;
+  float* checkpoints;
+  void* o;
+  void* workspace;
+  bool bf16;
+  hipStream_t stream;
+};
+
+// Workspace layout of the prefill (all offsets 256-byte aligned).
+struct PrefillLayout {
+  size_t seq_chunk_off;   // int32 [N + 1]
+  size_t seq_ck_off;      // int32 [N + 1]
+  size_t chunk_info;      // int2  [total_chunks] (first token, valid tokens)
+  size_t records;         // per (chunk, head) operand records
+  size_t record_bytes;    // bytes of one record
+  size_t total;
+};
+
+PrefillLayout prefill_layout(int32_t num_seqs, int64_t total_chunks, int32_t H, int32_t D);
+
+hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_prefill(const PrefillArgs& a);
+
+}  // namespace kda

@@ -1,0 +1,163 @@
+"""Thin ctypes binding of libkda (include/kda.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libkda.so. PyTorch supplies device memory and the current stream.
+The library must be built (``python -m gated_delta_rule_109_amd.build`` or
+``__graft_entry__.build()``); there is no fallback of any kind when it is
+missing.
+"""
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
+KDA_BF16, KDA_F32 = 0, 1
+CHUNK = 16
+LN_HALF = math.log(0.5)
+
+EXPORTED = ("kda_status_string", "kda_prefill_num_checkpoints", "kda_prefill_workspace_size",
+            "kda_prefill_chunked", "kda_decode_step")
+
+_lib = None
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {lib().kda_status_string(status).decode()}")
+
+
+def lib():
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_status_string.argtypes = [ctypes.c_int]
+        L.kda_prefill_num_checkpoints.restype = ctypes.c_int64
+        L.kda_prefill_num_checkpoints.argtypes = [_i32p, _i32, _i32]
+        L.kda_prefill_workspace_size.restype = ctypes.c_size_t
+        L.kda_prefill_workspace_size.argtypes = [_i32p, _i32, _i32, _i32, _i32]
+        L.kda_prefill_chunked.restype = ctypes.c_int
+        L.kda_prefill_chunked.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i32p, _i32,
+                                          _i32, _i32, _i32, ctypes.c_float, ctypes.c_float, _vp,
+                                          _vp, _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.kda_decode_step.restype = ctypes.c_int
+        L.kda_decode_step.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _i32, _i32,
+                                      _i32, _i32, ctypes.c_float, ctypes.c_float, _vp]
+        _lib = L
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor):
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _host_cu(cu_seqlens):
+    cu = torch.as_tensor(cu_seqlens, dtype=torch.int32).cpu().contiguous()
+    return cu, cu.numpy().ctypes.data_as(_i32p)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def num_checkpoints(cu_seqlens, ckpt_interval: int) -> int:
+    cu, p = _host_cu(cu_seqlens)
+    r = lib().kda_prefill_num_checkpoints(p, len(cu) - 1, int(ckpt_interval))
+    if r < 0:
+        raise KdaError(KDA_ERR_INVALID_ARG, "kda_prefill_num_checkpoints")
+    return int(r)
+
+
+def workspace_size(cu_seqlens, H: int, D: int) -> int:
+    cu, p = _host_cu(cu_seqlens)
+    return int(lib().kda_prefill_workspace_size(p, len(cu) - 1, H, D, D))
+
+
+@dataclass
+class PrefillPlan:
+    """Host and device copies of cu_seqlens plus a workspace sized for them."""
+    cu_host: torch.Tensor
+    cu_dev: torch.Tensor
+    workspace: torch.Tensor
+    num_ckpt: int
+    ckpt_interval: int
+
+
+def make_plan(cu_seqlens, H: int, D: int, device, ckpt_interval: int = 0) -> PrefillPlan:
+    cu_host, p = _host_cu(cu_seqlens)
+    ws = workspace_size(cu_host, H, D)
+    workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+    return PrefillPlan(cu_host, cu_host.to(device), workspace,
+                       num_checkpoints(cu_host, ckpt_interval) if ckpt_interval else 0,
+                       int(ckpt_interval))
+
+
+def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, scale=1.0, g_min=LN_HALF,
+            ckpt_interval=0, out_final_state=True, plan: Optional[PrefillPlan] = None,
+            o=None, final_state=None, checkpoints=None):
+    """kda_prefill_chunked on packed [T, H, D] tensors.
+
+    Returns (o, final_state or None, checkpoints or None)."""
+    T, H, D = q.shape
+    if plan is None:
+        plan = make_plan([0, T] if cu_seqlens is None else cu_seqlens, H, D, q.device, ckpt_interval)
+    N = len(plan.cu_host) - 1
+    _check_dev(q, k, v, g, beta, initial_state)
+    if o is None:
+        o = torch.empty_like(v)
+    if final_state is None and out_final_state:
+        final_state = torch.empty(N, H, D, D, dtype=torch.float32, device=q.device)
+    if checkpoints is None and plan.num_ckpt > 0:
+        checkpoints = torch.empty(plan.num_ckpt, H, D, D, dtype=torch.float32, device=q.device)
+    st = lib().kda_prefill_chunked(
+        _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta), _ptr(plan.cu_dev),
+        plan.cu_host.numpy().ctypes.data_as(_i32p), N, H, D, v.shape[2], float(scale),
+        float(g_min), _ptr(initial_state), _ptr(final_state), plan.ckpt_interval,
+        _ptr(checkpoints), _ptr(o), _ptr(plan.workspace), plan.workspace.numel(),
+        _stream(q.device))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_prefill_chunked")
+    return o, final_state, checkpoints
+
+
+def decode_step(q, k, v, g, beta, state, scale=1.0, g_min=LN_HALF, o=None):
+    """kda_decode_step: q,k,g [N,H,D]; v [N,H,D]; beta [N,H]; state [N,H,D,D]
+    updated in place. Returns o [N,H,D]."""
+    N, H, D = q.shape
+    _check_dev(q, k, v, g, beta, state)
+    if o is None:
+        o = torch.empty_like(v)
+    st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta),
+                               _ptr(state), _ptr(o), N, H, D, v.shape[2], float(scale),
+                               float(g_min), _stream(q.device))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_decode_step")
+    return o

@@ -125,3 +125,32 @@ def make_inputs(T, H, Dk, Dv=None, seed=0, bf16=True, num_seqs=None, lengths=Non
 def workload_inputs(w: Workload) -> Inputs:
     return make_inputs(w.total_tokens, w.H, w.D, seed=w.seed, bf16=w.bf16, lengths=w.lengths,
                        initial_state=w.initial_state)
+
+
+def make_inputs_device(T, H, D, seed, device, lengths=None, initial_state=False, bf16=True):
+    """Same recipe as make_inputs, drawn with a seeded torch generator on the
+    device (for the large workloads, where host generation would dominate).
+    Returns torch tensors: q, k, v (bf16 or fp32), g, beta (fp32), cu (int32,
+    host), s0 (fp32 or None)."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    lengths = [T] if lengths is None else list(lengths)
+    assert sum(lengths) == T
+
+    def normal(*shape):
+        return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
+
+    q = normal(T, H, D)
+    q = q / q.norm(dim=-1, keepdim=True)
+    k = normal(T, H, D)
+    k = k / k.norm(dim=-1, keepdim=True)
+    v = normal(T, H, D)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    q, k, v = q.to(dt), k.to(dt), v.to(dt)
+    beta = torch.sigmoid(normal(T, H))
+    g = (-torch.nn.functional.softplus(normal(T, H, D))).clamp_(min=LN_HALF, max=0.0)
+    s0 = 0.02 * normal(len(lengths), H, D, D) if initial_state else None
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    return q, k, v, g, beta, cu, s0

@@ -1,0 +1,140 @@
+/*
+ * kda.h -- C ABI of libkda: Kimi Delta Attention (KDA) prefill and decode on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (by title and section):
+ *   [K3-SA] "LLM - Semianalysis, Kimi K3 아키텍처" (charstring.tistory.com/2557)
+ *   [K3-DD] "MoonshotAI/Kimi-K3 딥다이브" (fiv.co.kr/repos/kimi-k3-deep-dive.html)
+ *
+ * The operation (per sequence n and head h, token by token; [K3-SA] 배경 /
+ * Background: delta rule on the L2 value-retrieval loss, Gated DeltaNet's
+ * forget gate turned into a diagonal, i.e. one decay per key channel;
+ * [K3-DD] 4-1 KDA, first bullet: the per-channel decay has a lower bound):
+ *
+ *     alpha_t = exp(clamp(g_t, g_min, 0))            per key channel
+ *     S'      = Diag(alpha_t) S_{t-1}
+ *     S_t     = S' + beta_t k_t (v_t - S'^T k_t)^T   = (I - b k k^T) S' + b k v^T
+ *     o_t     = scale * S_t^T q_t                     (read out after the update)
+ *
+ * S is a Dk x Dv fp32 matrix (row = key channel, Dv contiguous). Prefill
+ * evaluates this recurrence in chunks of 16 tokens with dense products inside
+ * a chunk and a recurrence between chunks ([K3-SA] Methods 1) FlashKDA;
+ * [K3-DD] 4-1 KDA, second bullet); decode runs one step directly ([K3-SA]
+ * Methods 1) FlashKDA, first bullet). Both give the recurrence's result up to
+ * floating-point rounding; the MFMA operands of prefill are bf16 (with a
+ * two-term bf16 split where precision needs it), accumulation is fp32 and the
+ * state is always fp32.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is DEVICE memory owned by the caller, row-major
+ *     and contiguous, 16-byte aligned. Only the *_host arrays are host memory.
+ *   - Supported head sizes: Dk == Dv == D with D in {16, 128}; anything else
+ *     returns KDA_ERR_UNSUPPORTED.
+ *   - All work is enqueued on `stream` (NULL = the default stream) and the
+ *     calls are asynchronous. The library allocates nothing and keeps no
+ *     global state.
+ *   - Arguments are validated before any device work; on an error status no
+ *     work has been enqueued. A fault inside a kernel surfaces later, as
+ *     KDA_ERR_HIP from a later call or as an error of the caller's sync.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = 1, /* null required pointer, bad size, bad cu_seqlens */
+  KDA_ERR_UNSUPPORTED = 2, /* head size or dtype this build does not handle  */
+  KDA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required      */
+  KDA_ERR_HIP = 4          /* a HIP runtime call failed (launch or earlier)  */
+} kda_status;
+
+/* Storage type of q, k, v and o. g, beta and every state are always fp32. */
+typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
+
+/* Chunk length of the prefill ([K3-DD] 4-1 KDA, second bullet: 16-token tiles). */
+#define KDA_CHUNK 16
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kda_status_string(kda_status status);
+
+/* Number of state checkpoints a prefill call writes:
+ * sum_n floor(L_n / ckpt_interval), L_n = cu_seqlens_host[n+1] - cu_seqlens_host[n].
+ * Returns 0 when ckpt_interval <= 0, -1 when the arguments are invalid. */
+int64_t kda_prefill_num_checkpoints(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                    int32_t ckpt_interval);
+
+/* Bytes of device workspace kda_prefill_chunked needs for these lengths and
+ * shapes (0 if the arguments are invalid). The workspace holds per-chunk
+ * tables and the per-chunk decayed operands of the chunked form; its contents
+ * are scratch and need no initialisation. */
+size_t kda_prefill_workspace_size(const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                  int32_t H, int32_t Dk, int32_t Dv);
+
+/* Chunked prefill over packed variable-length sequences.
+ *
+ * Inputs (T = cu_seqlens_host[num_seqs] packed tokens):
+ *   q, k        [T, H, Dk]  dtype      (q, k are used as given: no normalisation)
+ *   v           [T, H, Dv]  dtype
+ *   g           [T, H, Dk]  fp32 log-decay, clamped to [g_min, 0] on load
+ *   beta        [T, H]      fp32
+ *   cu_seqlens       [num_seqs + 1] int32, DEVICE copy of the offsets
+ *   cu_seqlens_host  [num_seqs + 1] int32, HOST copy (same values; used for
+ *                    validation and launch sizes): cu[0] = 0, non-decreasing.
+ *                    A sequence of length 0 is allowed (its final state equals
+ *                    its initial state, it has no outputs).
+ *   scale       readout scale (1.0 reproduces o_t = S_t^T q_t)
+ *   g_min       decay floor in log space (ln 0.5 for the configurations here;
+ *               [K3-DD] 4-1 KDA, first bullet)
+ *   initial_state  [num_seqs, H, Dk, Dv] fp32, or NULL for zero states
+ * Outputs:
+ *   o              [T, H, Dv] dtype
+ *   final_state    [num_seqs, H, Dk, Dv] fp32, or NULL to skip
+ *   checkpoints    fp32 [kda_prefill_num_checkpoints(...), H, Dk, Dv], ordered
+ *                  by (sequence, index within the sequence): checkpoint j >= 1 of
+ *                  sequence n is the state after its first j * ckpt_interval
+ *                  tokens, so any checkpoint is a valid initial_state for
+ *                  resuming ([K3-SA] Methods 3) KV cache efficiency: the
+ *                  recurrent state is kept only at sparse token intervals).
+ *                  Ignored when ckpt_interval == 0.
+ *   ckpt_interval  0 (no checkpoints) or a positive multiple of KDA_CHUNK.
+ *   workspace      device scratch of at least kda_prefill_workspace_size bytes,
+ *                  256-byte aligned.
+ * initial_state may alias final_state (the state is read before it is written).
+ * Errors: KDA_ERR_INVALID_ARG (null required pointer, negative sizes,
+ * malformed cu_seqlens_host, bad ckpt_interval), KDA_ERR_UNSUPPORTED,
+ * KDA_ERR_WORKSPACE, KDA_ERR_HIP (launch failure). */
+kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_dtype dtype,
+                               const float* g, const float* beta, const int32_t* cu_seqlens,
+                               const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
+                               int32_t Dk, int32_t Dv, float scale, float g_min,
+                               const float* initial_state, float* final_state,
+                               int32_t ckpt_interval, float* checkpoints, void* o,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One recurrent decode step for N independent sequences ([K3-SA] Methods 1)
+ * FlashKDA, first bullet: decode runs the state update directly; about 7 D^2
+ * FLOPs and 8 D^2 bytes of fp32 state traffic per head-token).
+ *   q, k   [N, H, Dk] dtype;  v [N, H, Dv] dtype
+ *   g      [N, H, Dk] fp32 log-decay (clamped to [g_min, 0]);  beta [N, H] fp32
+ *   state  [N, H, Dk, Dv] fp32, read and updated IN PLACE
+ *   o      [N, H, Dv] dtype
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP. */
+kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype dtype,
+                           const float* g, const float* beta, float* state, void* o,
+                           int32_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
+                           float g_min, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+symbol include/kda.h declares, sizes workspaces and checkpoints, and rejects
+bad arguments with the documented status before any device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_109_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|int64_t|size_t|kda_status)\s+(kda_\w+)\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kda.LIB_PATH):
+        from gated_delta_rule_109_amd import build
+        build.build()
+    return kda.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert set(names) == set(kda.EXPORTED)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code in range(5):
+        assert L.kda_status_string(code).startswith(b"KDA_")
+    assert L.kda_status_string(99) == b"KDA: unknown status"
+
+
+def cu(*lengths):
+    out = [0]
+    for x in lengths:
+        out.append(out[-1] + x)
+    return out
+
+
+def test_checkpoint_counts(L):
+    assert kda.num_checkpoints(cu(131072), 32768) == 4
+    assert kda.num_checkpoints(cu(48, 47, 16, 0, 33), 16) == 3 + 2 + 1 + 0 + 2
+    assert kda.num_checkpoints(cu(100), 0) == 0
+    with pytest.raises(kda.KdaError):
+        kda.num_checkpoints([1, 5], 16)            # cu[0] != 0
+    with pytest.raises(kda.KdaError):
+        kda.num_checkpoints([0, 9, 3], 16)         # decreasing
+
+
+def test_workspace_size(L):
+    # per (chunk, head) record: 19 KiB at D = 128, 6 KiB at D = 16, plus tables
+    w = kda.workspace_size(cu(8192), 32, 128)
+    assert 512 * 32 * 19 * 1024 <= w < 512 * 32 * 19 * 1024 + 8192
+    w16 = kda.workspace_size(cu(64), 2, 16)
+    assert 4 * 2 * 6 * 1024 <= w16 < 4 * 2 * 6 * 1024 + 2048
+    assert kda.workspace_size(cu(10), 2, 64) == 0          # unsupported D
+    assert kda.workspace_size([0, 5, 2], 2, 128) == 0       # malformed offsets
+
+
+def _prefill_status(L, **over):
+    """Call kda_prefill_chunked with dummy non-null pointers; every case here
+    must fail validation before touching them."""
+    host = (ctypes.c_int32 * 3)(*cu(20, 12))
+    fake = ctypes.c_void_p(0x1000)
+    args = dict(q=fake, k=fake, v=fake, dtype=kda.KDA_BF16, g=fake, beta=fake, cu=fake,
+                cu_host=ctypes.cast(host, ctypes.POINTER(ctypes.c_int32)), N=2, H=4, Dk=128, Dv=128,
+                scale=1.0, g_min=-0.69, s0=None, fin=None, ckpt=0, ckpts=None, o=fake, ws=fake,
+                ws_bytes=0, stream=None)
+    args.update(over)
+    return L.kda_prefill_chunked(*args.values())
+
+
+def test_prefill_argument_errors(L):
+    E = kda
+    assert _prefill_status(L, Dk=64, Dv=64) == E.KDA_ERR_UNSUPPORTED
+    assert _prefill_status(L, Dk=128, Dv=16) == E.KDA_ERR_UNSUPPORTED
+    assert _prefill_status(L, dtype=7) == E.KDA_ERR_UNSUPPORTED
+    assert _prefill_status(L, H=0) == E.KDA_ERR_INVALID_ARG
+    assert _prefill_status(L, cu=None) == E.KDA_ERR_INVALID_ARG
+    assert _prefill_status(L, q=None) == E.KDA_ERR_INVALID_ARG
+    assert _prefill_status(L, o=None) == E.KDA_ERR_INVALID_ARG
+    assert _prefill_status(L, ckpt=24) == E.KDA_ERR_INVALID_ARG      # not a multiple of 16
+    assert _prefill_status(L, ckpt=-16) == E.KDA_ERR_INVALID_ARG
+    assert _prefill_status(L, ckpt=16, ckpts=None) == E.KDA_ERR_INVALID_ARG
+    bad = (ctypes.c_int32 * 3)(0, 9, 3)
+    assert _prefill_status(L, cu_host=ctypes.cast(bad, ctypes.POINTER(ctypes.c_int32))) == E.KDA_ERR_INVALID_ARG
+    assert _prefill_status(L) == E.KDA_ERR_WORKSPACE                  # no workspace bytes
+    assert _prefill_status(L, ws=None, ws_bytes=1 << 30) == E.KDA_ERR_WORKSPACE
+    assert _prefill_status(L, ws=ctypes.c_void_p(0x1010), ws_bytes=1 << 30) == E.KDA_ERR_WORKSPACE
+    assert _prefill_status(L, v=ctypes.c_void_p(0x1002)) == E.KDA_ERR_INVALID_ARG   # misaligned
+    empty = (ctypes.c_int32 * 1)(0)
+    assert _prefill_status(L, N=0, cu_host=ctypes.cast(empty, ctypes.POINTER(ctypes.c_int32))) == E.KDA_OK
+
+
+def test_decode_argument_errors(L):
+    fake = ctypes.c_void_p(0x1000)
+    call = lambda **o: L.kda_decode_step(*dict(dict(q=fake, k=fake, v=fake, dtype=0, g=fake, beta=fake,
+                                                    state=fake, o=fake, N=4, H=2, Dk=128, Dv=128,
+                                                    scale=1.0, g_min=-0.69, stream=None), **o).values())
+    assert call(Dk=32, Dv=32) == kda.KDA_ERR_UNSUPPORTED
+    assert call(dtype=3) == kda.KDA_ERR_UNSUPPORTED
+    assert call(N=-1) == kda.KDA_ERR_INVALID_ARG
+    assert call(H=0) == kda.KDA_ERR_INVALID_ARG
+    assert call(state=None) == kda.KDA_ERR_INVALID_ARG
+    assert call(state=ctypes.c_void_p(0x1004)) == kda.KDA_ERR_INVALID_ARG
+    assert call(N=0) == kda.KDA_OK                                    # nothing to do
