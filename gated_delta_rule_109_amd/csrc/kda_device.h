@@ -4,11 +4,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kda {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_bits;  // bf16 as stored in memory
 
 constexpr int kChunk = 16;      // tokens per chunk
@@ -92,6 +96,16 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = A .. B-1, so
+// that array indices derived from I are constants (keeps arrays in registers).
+template <int A, int B, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (A < B) {
+    f(std::integral_constant<int, A>{});
+    static_for<A + 1, B>(f);
+  }
 }
 
 // Workgroup barrier that does not drain outstanding vector-memory operations

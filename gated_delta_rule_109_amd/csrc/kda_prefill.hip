@@ -43,15 +43,16 @@
 namespace kda {
 
 // ---- record layout ----------------------------------------------------------
-// One record per (chunk, head), byte offsets (1 KiB = one DMA wave-load):
+// One record per (chunk, head), stored head-major (record h * total_chunks + c);
+// byte offsets within a record (1 KiB = one 16-byte-per-lane wave load):
 //   Kp  : NP blocks. Block p, lane l (token m = l%16, g = l/16):
 //         Kp[m][32p + 4g + 0..3], Kp[m][32p + 16 + 4g + 0..3]   (bf16 x 8)
 //   Qt  : same for Qt.
 //   Kh  : NT blocks. Block t, lane l (channel 16t + l%16, g = l/16):
 //         Kh_hi[4g + 0..3][ch], Kh_lo[4g + 0..3][ch]            (bf16 x 8)
 //   TL  : 2 blocks. Lane l (row r = l%16, g = l/16), 32 bytes:
-//         T_hi[r][4g + 0..3], T_lo[r][4g + 0..3], L[r][4g + 0..3], 4 x 0
-//   Pc  : 1 block, fp32 [D] (zero padded).
+//         T_hi[r][4g + 0..3], T_lo[r][4g + 0..3], L[r][4g + 0..3] (bf16 x 12),
+//         then the chunk decay Pc[2l], Pc[2l + 1] of channels 2l, 2l + 1 (fp32).
 // The 32-wide k index of the Kp/Qt fragments interleaves two 16-row tiles of
 // S (k = 8g + j <-> channel 32p + 4g + j for j < 4, 32p + 16 + 4g + j - 4
 // otherwise), matching the order in which the MFMA accumulator layout holds S,
@@ -64,8 +65,7 @@ struct Rec {
   static constexpr int kQt = NP * 1024;
   static constexpr int kKh = 2 * NP * 1024;
   static constexpr int kTL = (2 * NP + NT) * 1024;
-  static constexpr int kPc = (2 * NP + NT + 2) * 1024;
-  static constexpr int kBlocks = 2 * NP + NT + 3;
+  static constexpr int kBlocks = 2 * NP + NT + 2;
   static constexpr int kBytes = kBlocks * 1024;
 };
 
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(D >= 64 ? D : 64) void prep_kernel(
   const int tid = threadIdx.x;
   const int2 ci = chunk_info[c];
   const int tok0 = ci.x, cnt = ci.y;
-  char* rec = records + ((size_t)c * H + h) * R::kBytes;
+  char* rec = records + ((size_t)h * gridDim.x + c) * R::kBytes;   // head-major: a head's chunks are contiguous
 
   if (tid < kChunk) sBeta[tid] = tid < cnt ? beta[(size_t)(tok0 + tid) * H + h] : 0.f;
 
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(D >= 64 ? D : 64) void prep_kernel(
       split_bf16(x, hi, lo);
       *(bf16x8*)(rec + R::kKh + rt * 1024 + (16 * gq + mm) * 16) = cat(hi, lo);
     }
-    ((float*)(rec + R::kPc))[ch] = Pc;
+    ((float*)(rec + R::kTL + (ch / 2) * 32 + 24))[ch % 2] = Pc;
   }
   __syncthreads();
 
@@ -271,92 +271,212 @@ __global__ __launch_bounds__(D >= 64 ? D : 64) void prep_kernel(
     const f32x4 l4 = *(const f32x4*)&sL[r][4 * gq];
     bf16x4 hi, lo;
     split_bf16(t4, hi, lo);
-    const bf16x4 zero = {};
     *(bf16x8*)(rec + R::kTL + tid * 32) = cat(hi, lo);
-    *(bf16x8*)(rec + R::kTL + tid * 32 + 16) = cat(to_bf16x4(l4), zero);
+    *(bf16x4*)(rec + R::kTL + tid * 32 + 16) = to_bf16x4(l4);
   }
 }
 
 // ---- 3. the recurrence over chunks ------------------------------------------------------
-constexpr int kRing = 6;               // LDS slots per workgroup
-constexpr int kAhead = kRing - 2;      // chunks issued beyond the one being consumed
-constexpr int kLoaders = 3;            // waves 1..3 issue the DMA loads
+// A workgroup owns kSlices 16-column slices of one (sequence, head) state.
+//  - compute waves (one per slice) hold the slice's D x 16 fp32 state in MFMA
+//    accumulator layout and run the whole chunk step for it, without talking
+//    to other waves (columns of S evolve independently);
+//  - kLoaders loader waves stream each chunk's record plus the V columns of
+//    the workgroup from L2/HBM with 16-byte vector loads, keeping kInFlight
+//    chunks in flight in their registers, and publish chunk j + 1 into a small
+//    LDS ring before barrier j. The record is fetched once per workgroup and
+//    shared by its compute waves. (Global->LDS DMA was measured to move only
+//    about 16 B per clock per CU on gfx950, too slow for this stream.)
+//  - one writer wave copies each chunk's output tile from LDS to global
+//    memory with 16-byte stores, off the compute waves' dependent chain.
+// One barrier per chunk. The compute step is branch-free: it always reads the
+// next slot and forms the next chunk's partial products right after the
+// state update (past the last chunk those results are simply unused).
+//
+// Slot reuse: chunk c is written to slot c % kRing in loader iteration c - 1
+// and read by the compute waves in iterations c - 1 and c; its slot is next
+// written in loader iteration c + kRing - 1, after barrier c + kRing - 2,
+// which follows iteration c when kRing >= 3. Output tiles alternate between
+// two LDS buffers: chunk j's tile is written in compute iteration j and read
+// by the writer in its iteration j + 1, before barrier j + 2 lets the compute
+// waves overwrite it with chunk j + 2.
+constexpr int kLoaders = 4;            // loader waves per workgroup
+constexpr int kInFlight = 6;           // chunks each loader keeps in flight
+constexpr int kRing = 4;               // LDS slots
 
 template <int D, typename TIn>
 struct ChainCfg {
   using R = Rec<D>;
-  static constexpr int kVBytes = kChunk * 16 * (int)sizeof(TIn);     // V slice of a chunk
-  static constexpr int kSlot = R::kBytes + 1024;                      // record + V (<= 1 KiB)
-  // DMA instructions per chunk: one per record block, V as 4-byte (bf16 pairs)
-  // or 16-byte (fp32 quads) lane loads.
-  static constexpr int kVLaneBytes = sizeof(TIn) == 2 ? 4 : 16;
-  static constexpr int kVInstr = kVBytes / (kWave * kVLaneBytes);
-  static constexpr int kInstr = R::kBlocks + kVInstr;
-  static constexpr int kMinPerLoader = kInstr / kLoaders;
-  static constexpr int kWait = kMinPerLoader * kAhead;
-  static_assert(kWait < 64, "vmcnt field");
-  static_assert(kVBytes <= 1024, "V slice fits its slot area");
+  static constexpr int kSlices = D / 16 < 2 ? D / 16 : 2;           // compute waves
+  static constexpr int kWaves = kSlices + kLoaders + 1;             // + the output writer
+  static constexpr int kThreads = kWave * kWaves;
+  static constexpr int kVSlice = kChunk * 16 * (int)sizeof(TIn);     // V (or O) bytes of one slice
+  static constexpr int kVRow = 16 * (int)sizeof(TIn);                // bytes of one token row
+  static constexpr int kVBytes = kVSlice * kSlices;
+  static constexpr int kVBlocks = (kVBytes + 1023) / 1024;
+  static constexpr int kBlocks = R::kBlocks + kVBlocks;              // 1 KiB wave-loads per chunk
+  static constexpr int kPerLoader = (kBlocks + kLoaders - 1) / kLoaders;
+  static constexpr int kSlot = kBlocks * 1024;
+  static_assert(kRing >= 3, "slot reuse");
+  static_assert(kRing * kSlot + 2 * kVBytes <= 128 * 1024, "LDS");
+  static_assert(kInFlight * kPerLoader < 64, "vmcnt field");
+};
+
+// Operands a compute wave copies to registers one chunk ahead.
+template <int D>
+struct Ops {
+  bf16x8 kp[Rec<D>::NP], qt[Rec<D>::NP];
+  bf16x8 tl0, tl1;
+  f32x4 vv;
 };
 
 template <int D, typename TIn>
-__global__ __launch_bounds__(256) void chain_kernel(
+__device__ __forceinline__ void read_ops(Ops<D>& f, const char* slot, int sl, int lane, int gq,
+                                         int mm) {
+  using R = Rec<D>;
+  using Cfg = ChainCfg<D, TIn>;
+#pragma unroll
+  for (int p = 0; p < R::NP; ++p) {
+    f.kp[p] = *(const bf16x8*)(slot + R::kKp + p * 1024 + lane * 16);
+    f.qt[p] = *(const bf16x8*)(slot + R::kQt + p * 1024 + lane * 16);
+  }
+  f.tl0 = *(const bf16x8*)(slot + R::kTL + lane * 32);
+  f.tl1 = *(const bf16x8*)(slot + R::kTL + lane * 32 + 16);
+  const char* vb = slot + R::kBytes + sl * Cfg::kVSlice;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.vv[i] = Elem<TIn>::load((const TIn*)(vb + (4 * gq + i) * Cfg::kVRow) + mm);
+}
+
+template <int D, typename TIn>
+__global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     const TIn* __restrict__ v, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ seq_chunk_off, const int32_t* __restrict__ seq_ck_off,
     const char* __restrict__ records, const float* initial_state, float* final_state,
     float* __restrict__ ckpts, TIn* __restrict__ o, int N, int H, int ckpt_interval,
-    float scale) {
+    float scale, int total_chunks) {
   using Cfg = ChainCfg<D, TIn>;
   using R = Rec<D>;
-  constexpr int NT = R::NT, NP = R::NP;
+  constexpr int NT = R::NT, NP = R::NP, SPW = Cfg::kSlices;
   __shared__ __attribute__((aligned(1024))) char ring[kRing * Cfg::kSlot];
+  __shared__ __attribute__((aligned(16))) char obuf[2][Cfg::kVBytes];   // output tiles [slice][token][16]
 
   const int NH = N * H;
   const int b = blockIdx.x;
-  const int s = b / NH, nh = b % NH;   // slices of one head share an XCD when NH % 8 == 0
+  const int sg = b / NH, nh = b % NH;   // slice groups of one head share an XCD when NH % 8 == 0
   const int n = nh / H, h = nh % H;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int t_begin = cu[n];
   const int len = cu[n + 1] - t_begin;
   const int nchunks = (len + kChunk - 1) / kChunk;
-  const size_t rec_stride = (size_t)H * R::kBytes;
-  const char* rec0 = records + ((size_t)seq_chunk_off[n] * H + h) * R::kBytes;
+  if (nchunks == 0 && wave >= SPW) return;   // only the initial -> final state copy remains
+  const char* rec0 = records + ((size_t)h * total_chunks + seq_chunk_off[n]) * R::kBytes;
 
-  if (wave > 0) {
-    // ---------------- loader waves ----------------
-    const int lw = wave - 1;
-    auto issue = [&](int j) {
-      const char* rec = rec0 + (size_t)j * rec_stride;
-      char* slot = ring + (j % kRing) * Cfg::kSlot;
+  if (wave == SPW + kLoaders) {
+    // ---------------- output writer ----------------
+    // Lane l covers 16 bytes of the tile: slice e / kVSlice, token row
+    // (e % kVSlice) / kVRow, columns from (e % kVRow) / sizeof(TIn).
+    auto flush = [&](int j) {
       const int tok0 = t_begin + kChunk * j;
       const int cnt = min(kChunk, len - kChunk * j);
-      for (int i = lw; i < Cfg::kInstr; i += kLoaders) {
-        if (i < R::kBlocks) {
-          dma_to_lds<16>(rec + i * 1024 + lane * 16, slot + i * 1024);
-        } else {
-          const int iv = i - R::kBlocks;
-          int tt, c0;
-          if constexpr (sizeof(TIn) == 2) { tt = 8 * iv + lane / 8; c0 = 2 * (lane % 8); }
-          else { tt = lane / 4; c0 = 4 * (lane % 4); }
-          tt = min(tt, cnt - 1);   // padding lanes re-read a valid token; masked later
-          const TIn* src = v + ((size_t)(tok0 + tt) * H + h) * D + 16 * s + c0;
-          dma_to_lds<Cfg::kVLaneBytes>(src, slot + R::kBlocks * 1024 + iv * kWave * Cfg::kVLaneBytes);
+      for (int e = lane * 16; e < Cfg::kVBytes; e += kWave * 16) {
+        const int vs = e / Cfg::kVSlice, rem = e % Cfg::kVSlice;
+        const int tt = rem / Cfg::kVRow, c0 = (rem % Cfg::kVRow) / (int)sizeof(TIn);
+        if (tt < cnt) {
+          const u32x4 val = *(const u32x4*)(&obuf[j & 1][e]);
+          *(u32x4*)(o + ((size_t)(tok0 + tt) * H + h) * D + 16 * (sg * SPW + vs) + c0) = val;
         }
       }
     };
-    for (int j = 0; j < kAhead && j < nchunks; ++j) issue(j);
+    lds_barrier();
     for (int j = 0; j < nchunks; ++j) {
-      if (j + kAhead < nchunks) {
-        issue(j + kAhead);
-        wait_vmcnt<Cfg::kWait>();
-      } else {
-        wait_vmcnt<0>();
-      }
       lds_barrier();
+      if (j >= 1) flush(j - 1);
     }
+    lds_barrier();
+    flush(nchunks - 1);
     return;
   }
 
-  // ---------------- compute wave ----------------
+  if (wave >= SPW) {
+    // ---------------- loader waves ----------------
+    const int lw = wave - SPW;
+    u32x4 buf[kInFlight][Cfg::kPerLoader];
+    // Every loader issues exactly kPerLoader 16-byte loads per chunk (blocks
+    // past the end re-read the last valid address and are not stored), so the
+    // loads of one chunk form one contiguous group in the vmcnt order. V rows
+    // past the end of the sequence are loaded from a valid row and replaced by
+    // zeros when the chunk is written to LDS, after its loads have completed
+    // (selecting right after the load would force a wait on it).
+    auto v_byte = [&](int blk) __attribute__((always_inline)) {
+      return min((blk - R::kBlocks) * 1024 + lane * 16, Cfg::kVBytes - 16);   // V-area byte
+    };
+    auto load_chunk = [&](u32x4 (&dst)[Cfg::kPerLoader], int j) __attribute__((always_inline)) {
+      const char* rec = rec0 + (size_t)j * R::kBytes;
+      const int tok0 = t_begin + kChunk * j;
+      const int cnt = min(kChunk, len - kChunk * j);
+#pragma unroll
+      for (int i = 0; i < Cfg::kPerLoader; ++i) {
+        const int blk = lw + kLoaders * i;
+        const char* src;
+        if (blk < R::kBlocks) {
+          src = rec + blk * 1024 + lane * 16;
+        } else {
+          const int e = v_byte(blk);
+          const int vs = e / Cfg::kVSlice, rem = e % Cfg::kVSlice;
+          const int tt = min(rem / Cfg::kVRow, cnt - 1);
+          const int c0 = (rem % Cfg::kVRow) / (int)sizeof(TIn);
+          src = (const char*)(v + ((size_t)(tok0 + tt) * H + h) * D + 16 * (sg * SPW + vs) + c0);
+        }
+        dst[i] = *(const u32x4*)src;
+      }
+    };
+    auto store_chunk = [&](const u32x4 (&src)[Cfg::kPerLoader], int j) __attribute__((always_inline)) {
+      char* slot = ring + (j % kRing) * Cfg::kSlot;
+      const int cnt = min(kChunk, len - kChunk * j);
+#pragma unroll
+      for (int i = 0; i < Cfg::kPerLoader; ++i) {
+        const int blk = lw + kLoaders * i;
+        if (blk < R::kBlocks) {
+          *(u32x4*)(slot + blk * 1024 + lane * 16) = src[i];
+        } else if (blk < Cfg::kBlocks) {
+          const u32x4 zero = {0u, 0u, 0u, 0u};
+          const int tt = (v_byte(blk) % Cfg::kVSlice) / Cfg::kVRow;
+          *(u32x4*)(slot + blk * 1024 + lane * 16) = tt < cnt ? src[i] : zero;
+        }
+      }
+    };
+    // The steady-state loop is branch-free (stores past the last chunk land in
+    // a slot nobody reads any more; loads past it re-read the last chunk), so
+    // the compiler's vmcnt bookkeeping keeps all kInFlight chunks in flight.
+    const int last = nchunks - 1;
+    static_for<0, kInFlight>([&](auto A) __attribute__((always_inline)) {
+      load_chunk(buf[A.value], min(A.value, last));
+    });
+    store_chunk(buf[0], 0);
+    load_chunk(buf[0], min(kInFlight, last));
+    lds_barrier();
+    auto step = [&](auto A, int j) __attribute__((always_inline)) {
+      // publish chunk j + 1 before barrier j, then refill its registers
+      constexpr int set = (decltype(A)::value + 1) % kInFlight;
+      const int c = j + 1;
+      store_chunk(buf[set], c);
+      load_chunk(buf[set], min(c + kInFlight, last));
+      lds_barrier();
+    };
+    int j0 = 0;
+    for (; j0 + kInFlight <= nchunks; j0 += kInFlight)
+      static_for<0, kInFlight>([&](auto A) __attribute__((always_inline)) { step(A, j0 + A.value); });
+    static_for<0, kInFlight>([&](auto A) __attribute__((always_inline)) {
+      if (j0 + A.value < nchunks) step(A, j0 + A.value);
+    });
+    lds_barrier();
+    return;
+  }
+
+  // ---------------- compute waves ----------------
+  const int sl = wave;                    // slice within the group
+  const int s = sg * SPW + sl;
   const int mm = lane % 16, gq = lane / 16;
   const int col = 16 * s + mm;
   const size_t state_base = (size_t)nh * D * D;
@@ -371,74 +491,75 @@ __global__ __launch_bounds__(256) void chain_kernel(
         acc[rt][i] = initial_state[state_base + (size_t)(16 * rt + 4 * gq + i) * D + col];
   }
 
-  const int ck_base = ckpt_interval > 0 ? seq_ck_off[n] : 0;
-  for (int j = 0; j < nchunks; ++j) {
-    lds_barrier();
-    const char* slot = ring + (j % kRing) * Cfg::kSlot;
-    const int tok0 = t_begin + kChunk * j;
-    const int cnt = min(kChunk, len - kChunk * j);
-
-    // state as bf16 B operands (two 16-row tiles per 32-deep block)
-    bf16x8 Bs[NP];
+  if (nchunks > 0) {
+    const int ck_base = ckpt_interval > 0 ? seq_ck_off[n] : 0;
+    // Partial products K~+ S and Q~ S of a chunk (two independent
+    // accumulation chains each), formed right after the previous update.
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 UA, UB, PA, PB;
+    auto partials = [&](const Ops<D>& f) __attribute__((always_inline)) {
+      bf16x8 Bs[NP];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const bf16x4 zero = {};
-      Bs[p] = cat(to_bf16x4(acc[2 * p]), 2 * p + 1 < NT ? to_bf16x4(acc[2 * p + 1]) : zero);
-    }
-    f32x4 U = {0.f, 0.f, 0.f, 0.f}, P = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const bf16x8 kp = *(const bf16x8*)(slot + R::kKp + p * 1024 + lane * 16);
-      const bf16x8 qt = *(const bf16x8*)(slot + R::kQt + p * 1024 + lane * 16);
-      U = mfma32(kp, Bs[p], U);
-      P = mfma32(qt, Bs[p], P);
-    }
-    // V slice of this chunk (token rows 4g..4g+3, column mm)
-    f32x4 vv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tt = 4 * gq + i;
-      const char* vb = slot + R::kBlocks * 1024;
-      float x;
-      if constexpr (sizeof(TIn) == 2) x = bf16_to_f32(*(const bf16_bits*)(vb + tt * 32 + mm * 2));
-      else x = *(const float*)(vb + tt * 64 + mm * 4);
-      vv[i] = tt < cnt ? x : 0.f;
-    }
-    bf16x4 r_hi, r_lo;
-    split_bf16(vv - U, r_hi, r_lo);
-    const bf16x8 tl0 = *(const bf16x8*)(slot + R::kTL + lane * 32);
-    const bf16x8 tl1 = *(const bf16x8*)(slot + R::kTL + lane * 32 + 16);
-    f32x4 dl = {0.f, 0.f, 0.f, 0.f};
-    dl = mfma32(tl0, cat(r_hi, r_hi), dl);
-    dl = mfma32(tl0, cat(r_lo, r_lo), dl);
-    bf16x4 d_hi, d_lo;
-    split_bf16(dl, d_hi, d_lo);
-    const bf16x4 l4 = lo_half(tl1);
-    const f32x4 out = mfma32(cat(l4, l4), cat(d_hi, d_lo), P);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tt = 4 * gq + i;
-      if (tt < cnt) Elem<TIn>::store(o + ((size_t)(tok0 + tt) * H + h) * D + col, scale * out[i]);
-    }
-    const bf16x8 dh2 = cat(d_hi, d_hi), dl2 = cat(d_lo, d_lo);
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt) {
-      const f32x4 pc = *(const f32x4*)(slot + R::kPc + (16 * rt + 4 * gq) * 4);
-      const bf16x8 kh = *(const bf16x8*)(slot + R::kKh + rt * 1024 + lane * 16);
-      acc[rt] *= pc;
-      acc[rt] = mfma32(kh, dh2, acc[rt]);
-      acc[rt] = mfma32(kh, dl2, acc[rt]);
-    }
-    if (ckpt_interval > 0) {
-      const int done = kChunk * (j + 1);
-      if (done <= len && done % ckpt_interval == 0) {
-        float* dst = ckpts + ((size_t)(ck_base + done / ckpt_interval - 1) * H + h) * D * D;
-#pragma unroll
-        for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dst[(size_t)(16 * rt + 4 * gq + i) * D + col] = acc[rt][i];
+      for (int p = 0; p < NP; ++p) {
+        const bf16x4 zero = {};
+        Bs[p] = cat(to_bf16x4(acc[2 * p]), 2 * p + 1 < NT ? to_bf16x4(acc[2 * p + 1]) : zero);
       }
+      UA = z; UB = z; PA = z; PB = z;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        if (p < (NP + 1) / 2) { UA = mfma32(f.kp[p], Bs[p], UA); PA = mfma32(f.qt[p], Bs[p], PA); }
+        else { UB = mfma32(f.kp[p], Bs[p], UB); PB = mfma32(f.qt[p], Bs[p], PB); }
+      }
+    };
+    char* otile = nullptr;
+    Ops<D> cur;
+    lds_barrier();
+    read_ops<D, TIn>(cur, ring, sl, lane, gq, mm);
+    partials(cur);
+    for (int j = 0; j < nchunks; ++j) {
+      lds_barrier();
+      const char* slot = ring + (j % kRing) * Cfg::kSlot;
+      bf16x8 kh[NT];
+      f32x4 pc[NT];
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        kh[rt] = *(const bf16x8*)(slot + R::kKh + rt * 1024 + lane * 16);
+        // Pc of rows 16rt + 4g .. +3 sits in the TL padding of lanes 8rt + 2g, +1
+        const char* pp = slot + R::kTL + (8 * rt + 2 * gq) * 32 + 24;
+        const f32x2 lo2 = *(const f32x2*)pp, hi2 = *(const f32x2*)(pp + 32);
+        pc[rt] = f32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+      }
+      Ops<D> nxt;
+      read_ops<D, TIn>(nxt, ring + ((j + 1) % kRing) * Cfg::kSlot, sl, lane, gq, mm);
+
+      const f32x4 U = UA + UB, P = PA + PB;
+      bf16x4 r_hi, r_lo;
+      split_bf16(cur.vv - U, r_hi, r_lo);
+      const f32x4 dl = mfma32(cur.tl0, cat(r_hi, r_hi), z) + mfma32(cur.tl0, cat(r_lo, r_lo), z);
+      bf16x4 d_hi, d_lo;
+      split_bf16(dl, d_hi, d_lo);
+      const bf16x8 dh2 = cat(d_hi, d_hi), dl2 = cat(d_lo, d_lo);
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) acc[rt] = mfma32(kh[rt], dl2, mfma32(kh[rt], dh2, acc[rt] * pc[rt]));
+      const bf16x4 l4 = lo_half(cur.tl1);
+      const f32x4 out = mfma32(cat(l4, l4), cat(d_hi, d_lo), P);
+      partials(nxt);
+      otile = &obuf[j & 1][sl * Cfg::kVSlice];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Elem<TIn>::store((TIn*)(otile + (4 * gq + i) * Cfg::kVRow) + mm, scale * out[i]);
+      if (ckpt_interval > 0) {
+        const int done = kChunk * (j + 1);
+        if (done <= len && done % ckpt_interval == 0) {
+          float* dst = ckpts + ((size_t)(ck_base + done / ckpt_interval - 1) * H + h) * D * D;
+#pragma unroll
+          for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(size_t)(16 * rt + 4 * gq + i) * D + col] = acc[rt][i];
+        }
+      }
+      cur = nxt;
     }
+    lds_barrier();
   }
   if (final_state) {
 #pragma unroll
@@ -470,11 +591,12 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const unsigned blocks = (unsigned)((int64_t)a.num_seqs * a.H * (D / 16));
-  hipLaunchKernelGGL((chain_kernel<D, TIn>), dim3(blocks), dim3(256), 0, a.stream, (const TIn*)a.v,
+  using Cfg = ChainCfg<D, TIn>;
+  const unsigned blocks = (unsigned)((int64_t)a.num_seqs * a.H * (D / 16 / Cfg::kSlices));
+  hipLaunchKernelGGL((chain_kernel<D, TIn>), dim3(blocks), dim3(Cfg::kThreads), 0, a.stream, (const TIn*)a.v,
                      a.cu_seqlens, seq_chunk_off, seq_ck_off, records, a.initial_state,
                      a.final_state, a.checkpoints, (TIn*)a.o, a.num_seqs, a.H, a.ckpt_interval,
-                     a.scale);
+                     a.scale, (int)a.total_chunks);
   return hipGetLastError();
 }
 

@@ -58,11 +58,11 @@ def test_checkpoint_counts(L):
 
 
 def test_workspace_size(L):
-    # per (chunk, head) record: 19 KiB at D = 128, 6 KiB at D = 16, plus tables
+    # per (chunk, head) record: 18 KiB at D = 128, 5 KiB at D = 16, plus tables
     w = kda.workspace_size(cu(8192), 32, 128)
-    assert 512 * 32 * 19 * 1024 <= w < 512 * 32 * 19 * 1024 + 8192
+    assert 512 * 32 * 18 * 1024 <= w < 512 * 32 * 18 * 1024 + 8192
     w16 = kda.workspace_size(cu(64), 2, 16)
-    assert 4 * 2 * 6 * 1024 <= w16 < 4 * 2 * 6 * 1024 + 2048
+    assert 4 * 2 * 5 * 1024 <= w16 < 4 * 2 * 5 * 1024 + 2048
     assert kda.workspace_size(cu(10), 2, 64) == 0          # unsupported D
     assert kda.workspace_size([0, 5, 2], 2, 128) == 0       # malformed offsets
 
