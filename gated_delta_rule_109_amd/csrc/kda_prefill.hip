@@ -297,9 +297,10 @@ __global__ __launch_bounds__(D >= 64 ? D : 64) void prep_kernel(
 // and read by the compute waves in iterations c - 1 and c; its slot is next
 // written in loader iteration c + kRing - 1, after barrier c + kRing - 2,
 // which follows iteration c when kRing >= 3. Output tiles alternate between
-// two LDS buffers: chunk j's tile is written in compute iteration j and read
-// by the writer in its iteration j + 1, before barrier j + 2 lets the compute
-// waves overwrite it with chunk j + 2.
+// two LDS buffers: chunk j's tile is written in compute iteration j + 1 (or
+// after the loop for the last chunk) and read by the writer after barrier
+// j + 2 (or the final barrier), before barrier j + 3 lets the compute waves
+// overwrite it with chunk j + 2's tile.
 constexpr int kLoaders = 4;            // loader waves per workgroup
 constexpr int kInFlight = 6;           // chunks each loader keeps in flight
 constexpr int kRing = 4;               // LDS slots
@@ -307,8 +308,12 @@ constexpr int kRing = 4;               // LDS slots
 template <int D, typename TIn>
 struct ChainCfg {
   using R = Rec<D>;
-  static constexpr int kSlices = D / 16 < 2 ? D / 16 : 2;           // compute waves
-  static constexpr int kWaves = kSlices + kLoaders + 1;             // + the output writer
+  static constexpr int kSlices = D / 16 < 2 ? D / 16 : 2;           // 16-column slices per workgroup
+  static constexpr int kHalves = R::NT >= 2 ? 2 : 1;                // compute waves per slice (row split)
+  static constexpr int kTilesPerWave = R::NT / kHalves;             // 16-row tiles per compute wave
+  static constexpr int kBlocksPerWave = (kTilesPerWave + 1) / 2;    // 32-deep k blocks per compute wave
+  static constexpr int kCompute = kSlices * kHalves;                // compute waves
+  static constexpr int kWaves = kCompute + kLoaders + 1;            // + the output writer
   static constexpr int kThreads = kWave * kWaves;
   static constexpr int kVSlice = kChunk * 16 * (int)sizeof(TIn);     // V (or O) bytes of one slice
   static constexpr int kVRow = 16 * (int)sizeof(TIn);                // bytes of one token row
@@ -322,32 +327,6 @@ struct ChainCfg {
   static_assert(kInFlight * kPerLoader < 64, "vmcnt field");
 };
 
-// Operands a compute wave copies to registers one chunk ahead.
-template <int D>
-struct Ops {
-  bf16x8 kp[Rec<D>::NP], qt[Rec<D>::NP];
-  bf16x8 tl0, tl1;
-  f32x4 vv;
-};
-
-template <int D, typename TIn>
-__device__ __forceinline__ void read_ops(Ops<D>& f, const char* slot, int sl, int lane, int gq,
-                                         int mm) {
-  using R = Rec<D>;
-  using Cfg = ChainCfg<D, TIn>;
-#pragma unroll
-  for (int p = 0; p < R::NP; ++p) {
-    f.kp[p] = *(const bf16x8*)(slot + R::kKp + p * 1024 + lane * 16);
-    f.qt[p] = *(const bf16x8*)(slot + R::kQt + p * 1024 + lane * 16);
-  }
-  f.tl0 = *(const bf16x8*)(slot + R::kTL + lane * 32);
-  f.tl1 = *(const bf16x8*)(slot + R::kTL + lane * 32 + 16);
-  const char* vb = slot + R::kBytes + sl * Cfg::kVSlice;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    f.vv[i] = Elem<TIn>::load((const TIn*)(vb + (4 * gq + i) * Cfg::kVRow) + mm);
-}
-
 template <int D, typename TIn>
 __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     const TIn* __restrict__ v, const int32_t* __restrict__ cu,
@@ -357,9 +336,10 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     float scale, int total_chunks) {
   using Cfg = ChainCfg<D, TIn>;
   using R = Rec<D>;
-  constexpr int NT = R::NT, NP = R::NP, SPW = Cfg::kSlices;
+  constexpr int SPW = Cfg::kSlices;
   __shared__ __attribute__((aligned(1024))) char ring[kRing * Cfg::kSlot];
   __shared__ __attribute__((aligned(16))) char obuf[2][Cfg::kVBytes];   // output tiles [slice][token][16]
+  __shared__ f32x4 xbuf[2][Cfg::kSlices][Cfg::kHalves][2][kWave];      // partial K~+S, Q~S by chunk parity
 
   const int NH = N * H;
   const int b = blockIdx.x;
@@ -369,10 +349,11 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   const int t_begin = cu[n];
   const int len = cu[n + 1] - t_begin;
   const int nchunks = (len + kChunk - 1) / kChunk;
-  if (nchunks == 0 && wave >= SPW) return;   // only the initial -> final state copy remains
+  constexpr int NCW = Cfg::kCompute;
+  if (nchunks == 0 && wave >= NCW) return;   // only the initial -> final state copy remains
   const char* rec0 = records + ((size_t)h * total_chunks + seq_chunk_off[n]) * R::kBytes;
 
-  if (wave == SPW + kLoaders) {
+  if (wave == NCW + kLoaders) {
     // ---------------- output writer ----------------
     // Lane l covers 16 bytes of the tile: slice e / kVSlice, token row
     // (e % kVSlice) / kVRow, columns from (e % kVRow) / sizeof(TIn).
@@ -391,16 +372,17 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     lds_barrier();
     for (int j = 0; j < nchunks; ++j) {
       lds_barrier();
-      if (j >= 1) flush(j - 1);
+      if (j >= 2) flush(j - 2);   // chunk j - 2's tile was completed in compute iteration j - 1
     }
     lds_barrier();
+    if (nchunks >= 2) flush(nchunks - 2);
     flush(nchunks - 1);
     return;
   }
 
-  if (wave >= SPW) {
+  if (wave >= NCW) {
     // ---------------- loader waves ----------------
-    const int lw = wave - SPW;
+    const int lw = wave - NCW;
     u32x4 buf[kInFlight][Cfg::kPerLoader];
     // Every loader issues exactly kPerLoader 16-byte loads per chunk (blocks
     // past the end re-read the last valid address and are not stored), so the
@@ -475,64 +457,97 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   }
 
   // ---------------- compute waves ----------------
-  const int sl = wave;                    // slice within the group
+  // Compute wave w holds rows [hf * D/kHalves, (hf + 1) * D/kHalves) of slice
+  // sl (hf = w % kHalves). Its partial K~+ S and Q~ S over those rows go to LDS
+  // right after the state update; after the next barrier both halves add the
+  // two partials in the same order, so they derive bitwise the same delta.
+  // The operands of chunk j (resident since barrier j - 1) are copied to
+  // registers during iteration j - 1, and chunk j's output tile is formed in
+  // iteration j + 1, so neither sits on the dependent chain of the recurrence.
+  const int sl = wave / Cfg::kHalves, hf = wave % Cfg::kHalves;
   const int s = sg * SPW + sl;
   const int mm = lane % 16, gq = lane / 16;
   const int col = 16 * s + mm;
   const size_t state_base = (size_t)nh * D * D;
-  f32x4 acc[NT];
+  constexpr int TW = Cfg::kTilesPerWave, PW = Cfg::kBlocksPerWave;
+  const int t0 = hf * TW;                 // first row tile of this wave
+  f32x4 acc[TW];
 #pragma unroll
-  for (int rt = 0; rt < NT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (initial_state) {
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt)
+    for (int t = 0; t < TW; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        acc[rt][i] = initial_state[state_base + (size_t)(16 * rt + 4 * gq + i) * D + col];
+        acc[t][i] = initial_state[state_base + (size_t)(16 * (t0 + t) + 4 * gq + i) * D + col];
   }
 
   if (nchunks > 0) {
     const int ck_base = ckpt_interval > 0 ? seq_ck_off[n] : 0;
-    // Partial products K~+ S and Q~ S of a chunk (two independent
-    // accumulation chains each), formed right after the previous update.
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    f32x4 UA, UB, PA, PB;
-    auto partials = [&](const Ops<D>& f) __attribute__((always_inline)) {
-      bf16x8 Bs[NP];
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const bf16x4 zero = {};
-        Bs[p] = cat(to_bf16x4(acc[2 * p]), 2 * p + 1 < NT ? to_bf16x4(acc[2 * p + 1]) : zero);
-      }
-      UA = z; UB = z; PA = z; PB = z;
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        if (p < (NP + 1) / 2) { UA = mfma32(f.kp[p], Bs[p], UA); PA = mfma32(f.qt[p], Bs[p], PA); }
-        else { UB = mfma32(f.kp[p], Bs[p], UB); PB = mfma32(f.qt[p], Bs[p], PB); }
-      }
+    struct ChunkOps {
+      bf16x8 kh[TW];
+      f32x4 pc[TW];
+      bf16x8 tl0, tl1;
+      f32x4 vv;
     };
-    char* otile = nullptr;
-    Ops<D> cur;
-    lds_barrier();
-    read_ops<D, TIn>(cur, ring, sl, lane, gq, mm);
-    partials(cur);
-    for (int j = 0; j < nchunks; ++j) {
-      lds_barrier();
-      const char* slot = ring + (j % kRing) * Cfg::kSlot;
-      bf16x8 kh[NT];
-      f32x4 pc[NT];
+    auto read_ops = [&](ChunkOps& f, const char* slot) __attribute__((always_inline)) {
 #pragma unroll
-      for (int rt = 0; rt < NT; ++rt) {
-        kh[rt] = *(const bf16x8*)(slot + R::kKh + rt * 1024 + lane * 16);
+      for (int t = 0; t < TW; ++t) {
+        const int rt = t0 + t;
+        f.kh[t] = *(const bf16x8*)(slot + R::kKh + rt * 1024 + lane * 16);
         // Pc of rows 16rt + 4g .. +3 sits in the TL padding of lanes 8rt + 2g, +1
         const char* pp = slot + R::kTL + (8 * rt + 2 * gq) * 32 + 24;
         const f32x2 lo2 = *(const f32x2*)pp, hi2 = *(const f32x2*)(pp + 32);
-        pc[rt] = f32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+        f.pc[t] = f32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
       }
-      Ops<D> nxt;
-      read_ops<D, TIn>(nxt, ring + ((j + 1) % kRing) * Cfg::kSlot, sl, lane, gq, mm);
+      f.tl0 = *(const bf16x8*)(slot + R::kTL + lane * 32);
+      f.tl1 = *(const bf16x8*)(slot + R::kTL + lane * 32 + 16);
+      const char* vb = slot + R::kBytes + sl * Cfg::kVSlice;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f.vv[i] = Elem<TIn>::load((const TIn*)(vb + (4 * gq + i) * Cfg::kVRow) + mm);
+    };
+    // partial products of a chunk over this wave's rows -> LDS
+    auto partials = [&](const char* slot, int parity) __attribute__((always_inline)) {
+      f32x4 U = z, P = z;
+#pragma unroll
+      for (int q = 0; q < PW; ++q) {
+        const int p = hf * PW + q;        // 32-deep k block (two row tiles)
+        const bf16x4 zero = {};
+        const bf16x8 Bs = cat(to_bf16x4(acc[2 * q]), 2 * q + 1 < TW ? to_bf16x4(acc[2 * q + 1]) : zero);
+        U = mfma32(*(const bf16x8*)(slot + R::kKp + p * 1024 + lane * 16), Bs, U);
+        P = mfma32(*(const bf16x8*)(slot + R::kQt + p * 1024 + lane * 16), Bs, P);
+      }
+      xbuf[parity][sl][hf][0][lane] = U;
+      xbuf[parity][sl][hf][1][lane] = P;
+    };
+    // output tile of chunk jo from its P and delta, to the LDS tile buffer
+    auto out_tile = [&](int jo, const bf16x8& tl1, const f32x4& P, const bf16x4& d_hi,
+                        const bf16x4& d_lo) __attribute__((always_inline)) {
+      const bf16x4 l4 = lo_half(tl1);
+      const f32x4 out = mfma32(cat(l4, l4), cat(d_hi, d_lo), P);
+      char* otile = &obuf[jo & 1][sl * Cfg::kVSlice];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Elem<TIn>::store((TIn*)(otile + (4 * gq + i) * Cfg::kVRow) + mm, scale * out[i]);
+    };
 
-      const f32x4 U = UA + UB, P = PA + PB;
+    ChunkOps cur;
+    lds_barrier();
+    partials(ring, 0);
+    read_ops(cur, ring);
+    // the previous chunk's output inputs (formed one iteration late)
+    bf16x8 o_tl1 = {};
+    f32x4 o_P = z;
+    bf16x4 o_dhi = {}, o_dlo = {};
+    for (int j = 0; j < nchunks; ++j) {
+      lds_barrier();
+      const int parity = j & 1;
+      f32x4 U = xbuf[parity][sl][0][0][lane], P = xbuf[parity][sl][0][1][lane];
+#pragma unroll
+      for (int w = 1; w < Cfg::kHalves; ++w) {
+        U += xbuf[parity][sl][w][0][lane];
+        P += xbuf[parity][sl][w][1][lane];
+      }
       bf16x4 r_hi, r_lo;
       split_bf16(cur.vv - U, r_hi, r_lo);
       const f32x4 dl = mfma32(cur.tl0, cat(r_hi, r_hi), z) + mfma32(cur.tl0, cat(r_lo, r_lo), z);
@@ -540,33 +555,32 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       split_bf16(dl, d_hi, d_lo);
       const bf16x8 dh2 = cat(d_hi, d_hi), dl2 = cat(d_lo, d_lo);
 #pragma unroll
-      for (int rt = 0; rt < NT; ++rt) acc[rt] = mfma32(kh[rt], dl2, mfma32(kh[rt], dh2, acc[rt] * pc[rt]));
-      const bf16x4 l4 = lo_half(cur.tl1);
-      const f32x4 out = mfma32(cat(l4, l4), cat(d_hi, d_lo), P);
-      partials(nxt);
-      otile = &obuf[j & 1][sl * Cfg::kVSlice];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Elem<TIn>::store((TIn*)(otile + (4 * gq + i) * Cfg::kVRow) + mm, scale * out[i]);
+      for (int t = 0; t < TW; ++t) acc[t] = mfma32(cur.kh[t], dl2, mfma32(cur.kh[t], dh2, acc[t] * cur.pc[t]));
+      const char* nslot = ring + ((j + 1) % kRing) * Cfg::kSlot;
+      partials(nslot, parity ^ 1);
+      if (hf == 0 && j > 0) out_tile(j - 1, o_tl1, o_P, o_dhi, o_dlo);
+      o_tl1 = cur.tl1; o_P = P; o_dhi = d_hi; o_dlo = d_lo;
+      read_ops(cur, nslot);
       if (ckpt_interval > 0) {
         const int done = kChunk * (j + 1);
         if (done <= len && done % ckpt_interval == 0) {
           float* dst = ckpts + ((size_t)(ck_base + done / ckpt_interval - 1) * H + h) * D * D;
 #pragma unroll
-          for (int rt = 0; rt < NT; ++rt)
+          for (int t = 0; t < TW; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(size_t)(16 * rt + 4 * gq + i) * D + col] = acc[rt][i];
+            for (int i = 0; i < 4; ++i) dst[(size_t)(16 * (t0 + t) + 4 * gq + i) * D + col] = acc[t][i];
         }
       }
-      cur = nxt;
     }
+    if (hf == 0) out_tile(nchunks - 1, o_tl1, o_P, o_dhi, o_dlo);
     lds_barrier();
   }
   if (final_state) {
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt)
+    for (int t = 0; t < TW; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        final_state[state_base + (size_t)(16 * rt + 4 * gq + i) * D + col] = acc[rt][i];
+        final_state[state_base + (size_t)(16 * (t0 + t) + 4 * gq + i) * D + col] = acc[t][i];
   }
 }
 
