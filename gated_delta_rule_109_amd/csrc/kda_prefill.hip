@@ -149,36 +149,76 @@ __global__ __launch_bounds__(D >= 64 ? D : 64) void prep_kernel(
     char* __restrict__ records) {
   using R = Rec<D>;
   constexpr int kThreads = D >= 64 ? D : 64;
-  __shared__ __attribute__((aligned(16))) __bf16 sKp[kChunk][D];
-  __shared__ __attribute__((aligned(16))) __bf16 sQt[kChunk][D];
-  __shared__ __attribute__((aligned(16))) __bf16 sKm[kChunk][D];
+  // Rows padded by 16 bytes so that the 16 token rows of a fragment read fall
+  // on different LDS banks.
+  constexpr int DP = D + 8;
+  // The input staging rows (q, k, g) and the decayed operands (Kp, Qt, Km)
+  // share one LDS buffer; a barrier separates the last staging read from the
+  // first operand write. Keeping LDS small lets more workgroups overlap their
+  // load latency.
+  constexpr int kStageBytes = 2 * kChunk * DP * (int)sizeof(TIn) + kChunk * (D + 4) * 4;
+  constexpr int kOpBytes = 3 * kChunk * DP * 2;
+  __shared__ __attribute__((aligned(16))) char lds_raw[kStageBytes > kOpBytes ? kStageBytes : kOpBytes];
+  __bf16(*sKp)[DP] = (__bf16(*)[DP])lds_raw;
+  __bf16(*sQt)[DP] = (__bf16(*)[DP])(lds_raw + kChunk * DP * 2);
+  __bf16(*sKm)[DP] = (__bf16(*)[DP])(lds_raw + 2 * kChunk * DP * 2);
   __shared__ __attribute__((aligned(16))) float sA[kChunk][kChunk];
   __shared__ __attribute__((aligned(16))) float sL[kChunk][kChunk];
   __shared__ __attribute__((aligned(16))) float sT[kChunk][kChunk];
   __shared__ float sBeta[kChunk];
 
-  const int c = blockIdx.x, h = blockIdx.y;
+  // Heads vary fastest across consecutive workgroups: the H heads of one token
+  // row are contiguous in q, k, v and g, so neighbouring workgroups read
+  // neighbouring memory.
+  const int h = blockIdx.x, c = blockIdx.y;
   const int tid = threadIdx.x;
   const int2 ci = chunk_info[c];
   const int tok0 = ci.x, cnt = ci.y;
-  char* rec = records + ((size_t)h * gridDim.x + c) * R::kBytes;   // head-major: a head's chunks are contiguous
+  char* rec = records + ((size_t)h * gridDim.y + c) * R::kBytes;   // head-major: a head's chunks are contiguous
 
   if (tid < kChunk) sBeta[tid] = tid < cnt ? beta[(size_t)(tok0 + tid) * H + h] : 0.f;
 
-  if (tid < D) {
-    const int ch = tid;
-    float kf[kChunk], qf[kChunk], a[kChunk];
-#pragma unroll
-    for (int t = 0; t < kChunk; ++t) {
-      if (t < cnt) {
-        const size_t idx = ((size_t)(tok0 + t) * H + h) * D + ch;
-        kf[t] = Elem<TIn>::load(k + idx);
-        qf[t] = Elem<TIn>::load(q + idx);
-        a[t] = gate_alpha(g[idx], g_min);
+  // Stage the chunk's q, k and g rows in LDS with 16-byte loads (a token row
+  // of one head is contiguous), then read them back one channel per thread.
+  // Rows past the end of the sequence are zero (g = 0 gives alpha = 1).
+  TIn(*sQin)[DP] = (TIn(*)[DP])lds_raw;
+  TIn(*sKin)[DP] = (TIn(*)[DP])(lds_raw + kChunk * DP * sizeof(TIn));
+  float(*sGin)[D + 4] = (float(*)[D + 4])(lds_raw + 2 * kChunk * DP * sizeof(TIn));
+  {
+    constexpr int kVec = 16 / (int)sizeof(TIn);        // elements per 16-byte load
+    constexpr int kQK = kChunk * D / kVec;              // 16-byte pieces of q (and of k)
+    constexpr int kG = kChunk * D / 4;                  // 16-byte pieces of g
+    for (int e = tid; e < 2 * kQK + kG; e += kThreads) {
+      if (e < 2 * kQK) {
+        const int which = e / kQK, r = e % kQK;
+        const int t = r / (D / kVec), c = (r % (D / kVec)) * kVec;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (t < cnt) x = *(const u32x4*)((which ? k : q) + ((size_t)(tok0 + t) * H + h) * D + c);
+        *(u32x4*)&(which ? sKin : sQin)[t][c] = x;
       } else {
-        kf[t] = 0.f; qf[t] = 0.f; a[t] = 1.f;
+        const int r = e - 2 * kQK;
+        const int t = r / (D / 4), c = (r % (D / 4)) * 4;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (t < cnt) x = *(const f32x4*)(g + ((size_t)(tok0 + t) * H + h) * D + c);
+        *(f32x4*)&sGin[t][c] = x;
       }
     }
+  }
+  __syncthreads();
+
+  float kf[kChunk], qf[kChunk], a[kChunk];
+  if (tid < D) {
+    const int ch = tid;
+#pragma unroll
+    for (int t = 0; t < kChunk; ++t) {
+      kf[t] = Elem<TIn>::load(&sKin[t][ch]);
+      qf[t] = Elem<TIn>::load(&sQin[t][ch]);
+      a[t] = gate_alpha(sGin[t][ch], g_min);
+    }
+  }
+  __syncthreads();   // staging reads done before the operand rows overwrite them
+  if (tid < D) {
+    const int ch = tid;
     float P = 1.f;
 #pragma unroll
     for (int t = 0; t < kChunk; ++t) {
@@ -212,7 +252,7 @@ __global__ __launch_bounds__(D >= 64 ? D : 64) void prep_kernel(
   for (int r = tid; r < 2 * R::NP * kWave; r += kThreads) {
     const int which = r / (R::NP * kWave), rr = r % (R::NP * kWave);
     const int p = rr / kWave, l = rr % kWave, mm = l % 16, gq = l / 16;
-    const __bf16(*src)[D] = which ? sQt : sKp;
+    const __bf16(*src)[DP] = which ? sQt : sKp;
     const int ch0 = 32 * p + 4 * gq, ch1 = 32 * p + 16 + 4 * gq;
     const bf16x4 zero = {};
     const bf16x4 a0 = ch0 < D ? *(const bf16x4*)&src[mm][ch0] : zero;
@@ -228,7 +268,7 @@ __global__ __launch_bounds__(D >= 64 ? D : 64) void prep_kernel(
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       if (!(wave == which || (kWaves == 1 && wave == 0))) continue;
-      const __bf16(*src)[D] = which ? sQt : sKp;
+      const __bf16(*src)[DP] = which ? sQt : sKp;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int p = 0; p < R::NP; ++p) {
@@ -599,7 +639,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   if (e != hipSuccess) return e;
   if (a.total_chunks > 0) {
     constexpr int threads = D >= 64 ? D : 64;
-    hipLaunchKernelGGL((prep_kernel<D, TIn>), dim3((unsigned)a.total_chunks, (unsigned)a.H),
+    hipLaunchKernelGGL((prep_kernel<D, TIn>), dim3((unsigned)a.H, (unsigned)a.total_chunks),
                        dim3(threads), 0, a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g, a.beta,
                        (const int2*)chunk_info, a.H, a.g_min, records);
     e = hipGetLastError();
