@@ -341,7 +341,7 @@ __global__ __launch_bounds__(D >= 64 ? D : 64) void prep_kernel(
 // after the loop for the last chunk) and read by the writer after barrier
 // j + 2 (or the final barrier), before barrier j + 3 lets the compute waves
 // overwrite it with chunk j + 2's tile.
-constexpr int kLoaders = 4;            // loader waves per workgroup
+constexpr int kLoaders = 3;            // loader waves per workgroup
 constexpr int kInFlight = 6;           // chunks each loader keeps in flight
 constexpr int kRing = 4;               // LDS slots
 
@@ -501,9 +501,9 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   // sl (hf = w % kHalves). Its partial K~+ S and Q~ S over those rows go to LDS
   // right after the state update; after the next barrier both halves add the
   // two partials in the same order, so they derive bitwise the same delta.
-  // The operands of chunk j (resident since barrier j - 1) are copied to
-  // registers during iteration j - 1, and chunk j's output tile is formed in
-  // iteration j + 1, so neither sits on the dependent chain of the recurrence.
+  // All operands of chunk j + 1 are copied from LDS to registers right after
+  // barrier j (two register sets alternate), so no LDS latency sits on the
+  // dependent chain; chunk j's output tile is formed in iteration j + 1.
   const int sl = wave / Cfg::kHalves, hf = wave % Cfg::kHalves;
   const int s = sg * SPW + sl;
   const int mm = lane % 16, gq = lane / 16;
@@ -526,12 +526,19 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     const int ck_base = ckpt_interval > 0 ? seq_ck_off[n] : 0;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     struct ChunkOps {
+      bf16x8 kp[PW], qt[PW];
       bf16x8 kh[TW];
       f32x4 pc[TW];
       bf16x8 tl0, tl1;
       f32x4 vv;
     };
     auto read_ops = [&](ChunkOps& f, const char* slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < PW; ++q) {
+        const int p = hf * PW + q;        // 32-deep k block (two row tiles)
+        f.kp[q] = *(const bf16x8*)(slot + R::kKp + p * 1024 + lane * 16);
+        f.qt[q] = *(const bf16x8*)(slot + R::kQt + p * 1024 + lane * 16);
+      }
 #pragma unroll
       for (int t = 0; t < TW; ++t) {
         const int rt = t0 + t;
@@ -548,39 +555,33 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       for (int i = 0; i < 4; ++i) f.vv[i] = Elem<TIn>::load((const TIn*)(vb + (4 * gq + i) * Cfg::kVRow) + mm);
     };
     // partial products of a chunk over this wave's rows -> LDS
-    auto partials = [&](const char* slot, int parity) __attribute__((always_inline)) {
+    auto partials = [&](const ChunkOps& f, int parity) __attribute__((always_inline)) {
       f32x4 U = z, P = z;
 #pragma unroll
       for (int q = 0; q < PW; ++q) {
-        const int p = hf * PW + q;        // 32-deep k block (two row tiles)
         const bf16x4 zero = {};
         const bf16x8 Bs = cat(to_bf16x4(acc[2 * q]), 2 * q + 1 < TW ? to_bf16x4(acc[2 * q + 1]) : zero);
-        U = mfma32(*(const bf16x8*)(slot + R::kKp + p * 1024 + lane * 16), Bs, U);
-        P = mfma32(*(const bf16x8*)(slot + R::kQt + p * 1024 + lane * 16), Bs, P);
+        U = mfma32(f.kp[q], Bs, U);
+        P = mfma32(f.qt[q], Bs, P);
       }
       xbuf[parity][sl][hf][0][lane] = U;
       xbuf[parity][sl][hf][1][lane] = P;
     };
     // output tile of chunk jo from its P and delta, to the LDS tile buffer
-    auto out_tile = [&](int jo, const bf16x8& tl1, const f32x4& P, const bf16x4& d_hi,
-                        const bf16x4& d_lo) __attribute__((always_inline)) {
-      const bf16x4 l4 = lo_half(tl1);
-      const f32x4 out = mfma32(cat(l4, l4), cat(d_hi, d_lo), P);
+    bf16x8 o_tl1 = {};
+    f32x4 o_P = z;
+    bf16x4 o_dhi = {}, o_dlo = {};
+    auto out_tile = [&](int jo) __attribute__((always_inline)) {
+      const bf16x4 l4 = lo_half(o_tl1);
+      const f32x4 out = mfma32(cat(l4, l4), cat(o_dhi, o_dlo), o_P);
       char* otile = &obuf[jo & 1][sl * Cfg::kVSlice];
 #pragma unroll
       for (int i = 0; i < 4; ++i) Elem<TIn>::store((TIn*)(otile + (4 * gq + i) * Cfg::kVRow) + mm, scale * out[i]);
     };
-
-    ChunkOps cur;
-    lds_barrier();
-    partials(ring, 0);
-    read_ops(cur, ring);
-    // the previous chunk's output inputs (formed one iteration late)
-    bf16x8 o_tl1 = {};
-    f32x4 o_P = z;
-    bf16x4 o_dhi = {}, o_dlo = {};
-    for (int j = 0; j < nchunks; ++j) {
+    // one chunk step: cur holds chunk j's operands; nxt receives chunk j + 1's
+    auto step = [&](int j, ChunkOps& cur, ChunkOps& nxt) __attribute__((always_inline)) {
       lds_barrier();
+      read_ops(nxt, ring + ((j + 1) % kRing) * Cfg::kSlot);
       const int parity = j & 1;
       f32x4 U = xbuf[parity][sl][0][0][lane], P = xbuf[parity][sl][0][1][lane];
 #pragma unroll
@@ -596,11 +597,9 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       const bf16x8 dh2 = cat(d_hi, d_hi), dl2 = cat(d_lo, d_lo);
 #pragma unroll
       for (int t = 0; t < TW; ++t) acc[t] = mfma32(cur.kh[t], dl2, mfma32(cur.kh[t], dh2, acc[t] * cur.pc[t]));
-      const char* nslot = ring + ((j + 1) % kRing) * Cfg::kSlot;
-      partials(nslot, parity ^ 1);
-      if (hf == 0 && j > 0) out_tile(j - 1, o_tl1, o_P, o_dhi, o_dlo);
+      partials(nxt, parity ^ 1);
+      if (hf == 0 && j > 0) out_tile(j - 1);
       o_tl1 = cur.tl1; o_P = P; o_dhi = d_hi; o_dlo = d_lo;
-      read_ops(cur, nslot);
       if (ckpt_interval > 0) {
         const int done = kChunk * (j + 1);
         if (done <= len && done % ckpt_interval == 0) {
@@ -611,8 +610,19 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
             for (int i = 0; i < 4; ++i) dst[(size_t)(16 * (t0 + t) + 4 * gq + i) * D + col] = acc[t][i];
         }
       }
+    };
+
+    ChunkOps opsA, opsB;
+    lds_barrier();
+    read_ops(opsA, ring);
+    partials(opsA, 0);
+    int j = 0;
+    for (; j + 2 <= nchunks; j += 2) {
+      step(j, opsA, opsB);
+      step(j + 1, opsB, opsA);
     }
-    if (hf == 0) out_tile(nchunks - 1, o_tl1, o_P, o_dhi, o_dlo);
+    if (j < nchunks) step(j, opsA, opsB);
+    if (hf == 0) out_tile(nchunks - 1);
     lds_barrier();
   }
   if (final_state) {
