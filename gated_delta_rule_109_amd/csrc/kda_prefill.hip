@@ -29,9 +29,10 @@
 //  3. chain_kernel  (one workgroup per sequence, head and 16-column slice of the
 //                   state): the sequential recurrence over chunks. Columns of S
 //                   evolve independently, so each slice runs on its own. The
-//                   fp32 state slice lives in MFMA accumulators; three loader
-//                   waves stream records into an LDS ring several chunks ahead
-//                   with global->LDS DMA while wave 0 runs the products.
+//                   fp32 state slice lives in the MFMA accumulators of two
+//                   compute waves (half the rows each); loader waves stream
+//                   records into an LDS ring several chunks ahead and an
+//                   output wave forms and stores the output tiles.
 //
 // Precision: MFMA operands are bf16 with fp32 accumulation. The decayed key of
 // the state update (Kh), T, V - Kp S and delta enter as two-term bf16 splits
@@ -317,53 +318,51 @@ __global__ __launch_bounds__(D >= 64 ? D : 64) void prep_kernel(
 }
 
 // ---- 3. the recurrence over chunks ------------------------------------------------------
-// A workgroup owns kSlices 16-column slices of one (sequence, head) state.
-//  - compute waves (one per slice) hold the slice's D x 16 fp32 state in MFMA
-//    accumulator layout and run the whole chunk step for it, without talking
-//    to other waves (columns of S evolve independently);
-//  - kLoaders loader waves stream each chunk's record plus the V columns of
-//    the workgroup from L2/HBM with 16-byte vector loads, keeping kInFlight
-//    chunks in flight in their registers, and publish chunk j + 1 into a small
-//    LDS ring before barrier j. The record is fetched once per workgroup and
-//    shared by its compute waves. (Global->LDS DMA was measured to move only
-//    about 16 B per clock per CU on gfx950, too slow for this stream.)
-//  - one writer wave copies each chunk's output tile from LDS to global
-//    memory with 16-byte stores, off the compute waves' dependent chain.
-// One barrier per chunk. The compute step is branch-free: it always reads the
-// next slot and forms the next chunk's partial products right after the
-// state update (past the last chunk those results are simply unused).
+// A workgroup owns one 16-column slice of one (sequence, head) state (columns
+// of S evolve independently, so slices never talk to each other).
+//  - kHalves compute waves split the slice's D rows: each holds D / kHalves
+//    rows of the fp32 state in MFMA accumulator layout. They exchange only
+//    their partial K~+ S through LDS, once per chunk.
+//  - kLoaders loader waves stream each chunk's record plus the slice's V
+//    columns from L2/HBM with 16-byte vector loads, keeping kInFlight chunks
+//    in flight in their registers, and publish chunk j + 1 into a small LDS
+//    ring before barrier j. (Global->LDS DMA was measured to move only about
+//    16 B per clock per CU on gfx950, too slow for this stream.)
+//  - one output wave forms each chunk's output tile from the partial Q~ S
+//    products and delta the compute waves leave in LDS, and stores it, so the
+//    output product sits off the compute waves' dependent chain.
+// One barrier per chunk. Barrier B0 ends the prologue; chunk j's compute step
+// runs between barriers B(j+1) and B(j+2); a final barrier follows the last.
 //
-// Slot reuse: chunk c is written to slot c % kRing in loader iteration c - 1
-// and read by the compute waves in iterations c - 1 and c; its slot is next
-// written in loader iteration c + kRing - 1, after barrier c + kRing - 2,
-// which follows iteration c when kRing >= 3. Output tiles alternate between
-// two LDS buffers: chunk j's tile is written in compute iteration j + 1 (or
-// after the loop for the last chunk) and read by the writer after barrier
-// j + 2 (or the final barrier), before barrier j + 3 lets the compute waves
-// overwrite it with chunk j + 2's tile.
-constexpr int kLoaders = 3;            // loader waves per workgroup
+// Buffer lifetimes (kRing = 4 ring slots, 4 partial-product sets, 2 delta
+// sets):
+//  - chunk c is stored to slot c % kRing before B(c) and read by the compute
+//    waves after B(c) (as the next chunk's operands) and by the output wave
+//    after B(c + 2); it is overwritten only after B(c + kRing - 1) = B(c + 3);
+//  - the partials of chunk c (xbuf[c % 4]) are written before B(c + 1), read
+//    by the compute waves after B(c + 1) and by the output wave after B(c + 2),
+//    and overwritten after B(c + 4);
+//  - delta of chunk c (dbuf[c % 2]) is written before B(c + 2), read after it
+//    and overwritten after B(c + 3).
+constexpr int kLoaders = 4;            // loader waves per workgroup
 constexpr int kInFlight = 6;           // chunks each loader keeps in flight
 constexpr int kRing = 4;               // LDS slots
 
 template <int D, typename TIn>
 struct ChainCfg {
   using R = Rec<D>;
-  static constexpr int kSlices = D / 16 < 2 ? D / 16 : 2;           // 16-column slices per workgroup
-  static constexpr int kHalves = R::NT >= 2 ? 2 : 1;                // compute waves per slice (row split)
+  static constexpr int kHalves = R::NT >= 2 ? 2 : 1;                // compute waves (row split)
   static constexpr int kTilesPerWave = R::NT / kHalves;             // 16-row tiles per compute wave
   static constexpr int kBlocksPerWave = (kTilesPerWave + 1) / 2;    // 32-deep k blocks per compute wave
-  static constexpr int kCompute = kSlices * kHalves;                // compute waves
-  static constexpr int kWaves = kCompute + kLoaders + 1;            // + the output writer
+  static constexpr int kWaves = kHalves + kLoaders + 1;             // + the output wave
   static constexpr int kThreads = kWave * kWaves;
-  static constexpr int kVSlice = kChunk * 16 * (int)sizeof(TIn);     // V (or O) bytes of one slice
-  static constexpr int kVRow = 16 * (int)sizeof(TIn);                // bytes of one token row
-  static constexpr int kVBytes = kVSlice * kSlices;
-  static constexpr int kVBlocks = (kVBytes + 1023) / 1024;
-  static constexpr int kBlocks = R::kBlocks + kVBlocks;              // 1 KiB wave-loads per chunk
+  static constexpr int kVBytes = kChunk * 16 * (int)sizeof(TIn);    // V columns of the slice, one chunk
+  static constexpr int kBlocks = R::kBlocks + 1;                     // 1 KiB wave-loads per chunk (+ V)
   static constexpr int kPerLoader = (kBlocks + kLoaders - 1) / kLoaders;
   static constexpr int kSlot = kBlocks * 1024;
-  static_assert(kRing >= 3, "slot reuse");
-  static_assert(kRing * kSlot + 2 * kVBytes <= 128 * 1024, "LDS");
+  static_assert(kVBytes <= 1024, "one V block");
+  static_assert(kRing == 4, "buffer lifetimes");
+  static_assert(kRing * kSlot <= 96 * 1024, "LDS");
   static_assert(kInFlight * kPerLoader < 64, "vmcnt field");
 };
 
@@ -376,47 +375,49 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     float scale, int total_chunks) {
   using Cfg = ChainCfg<D, TIn>;
   using R = Rec<D>;
-  constexpr int SPW = Cfg::kSlices;
+  constexpr int NCW = Cfg::kHalves;
   __shared__ __attribute__((aligned(1024))) char ring[kRing * Cfg::kSlot];
-  __shared__ __attribute__((aligned(16))) char obuf[2][Cfg::kVBytes];   // output tiles [slice][token][16]
-  __shared__ f32x4 xbuf[2][Cfg::kSlices][Cfg::kHalves][2][kWave];      // partial K~+S, Q~S by chunk parity
+  __shared__ f32x4 xbuf[4][NCW][2][kWave];     // partial K~+ S (0) and (Q~ S)^T (1) per chunk
+  __shared__ bf16x8 dbuf[2][kWave];            // delta hi | lo per chunk
 
   const int NH = N * H;
   const int b = blockIdx.x;
-  const int sg = b / NH, nh = b % NH;   // slice groups of one head share an XCD when NH % 8 == 0
+  const int s = b / NH, nh = b % NH;   // the slices of one head share an XCD when NH % 8 == 0
   const int n = nh / H, h = nh % H;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int mm = lane % 16, gq = lane / 16;
   const int t_begin = cu[n];
   const int len = cu[n + 1] - t_begin;
   const int nchunks = (len + kChunk - 1) / kChunk;
-  constexpr int NCW = Cfg::kCompute;
   if (nchunks == 0 && wave >= NCW) return;   // only the initial -> final state copy remains
   const char* rec0 = records + ((size_t)h * total_chunks + seq_chunk_off[n]) * R::kBytes;
+  auto slot_of = [&](int c) __attribute__((always_inline)) { return ring + (c % kRing) * Cfg::kSlot; };
 
   if (wave == NCW + kLoaders) {
-    // ---------------- output writer ----------------
-    // Lane l covers 16 bytes of the tile: slice e / kVSlice, token row
-    // (e % kVSlice) / kVRow, columns from (e % kVRow) / sizeof(TIn).
-    auto flush = [&](int j) {
-      const int tok0 = t_begin + kChunk * j;
-      const int cnt = min(kChunk, len - kChunk * j);
-      for (int e = lane * 16; e < Cfg::kVBytes; e += kWave * 16) {
-        const int vs = e / Cfg::kVSlice, rem = e % Cfg::kVSlice;
-        const int tt = rem / Cfg::kVRow, c0 = (rem % Cfg::kVRow) / (int)sizeof(TIn);
-        if (tt < cnt) {
-          const u32x4 val = *(const u32x4*)(&obuf[j & 1][e]);
-          *(u32x4*)(o + ((size_t)(tok0 + tt) * H + h) * D + 16 * (sg * SPW + vs) + c0) = val;
-        }
+    // ---------------- output wave ----------------
+    // O^T = (Q~ S)^T + delta^T L^T: with the operands of L delta swapped the
+    // accumulator holds token mm, columns 4gq .. 4gq + 3 in each lane.
+    auto out_tile = [&](int c) __attribute__((always_inline)) {
+      f32x4 P = xbuf[c % 4][0][1][lane];
+#pragma unroll
+      for (int w = 1; w < NCW; ++w) P += xbuf[c % 4][w][1][lane];
+      const bf16x8 dd = dbuf[c % 2][lane];
+      const bf16x4 l4 = *(const bf16x4*)(slot_of(c) + R::kTL + lane * 32 + 16);
+      const f32x4 out = scale * mfma32(dd, cat(l4, l4), P);
+      const int cnt = min(kChunk, len - kChunk * c);
+      if (mm < cnt) {
+        TIn* dst = o + ((size_t)(t_begin + kChunk * c + mm) * H + h) * D + 16 * s + 4 * gq;
+        if constexpr (sizeof(TIn) == 2) *(bf16x4*)dst = to_bf16x4(out);
+        else *(f32x4*)dst = out;
       }
     };
     lds_barrier();
     for (int j = 0; j < nchunks; ++j) {
       lds_barrier();
-      if (j >= 2) flush(j - 2);   // chunk j - 2's tile was completed in compute iteration j - 1
+      if (j >= 1) out_tile(j - 1);
     }
     lds_barrier();
-    if (nchunks >= 2) flush(nchunks - 2);
-    flush(nchunks - 1);
+    out_tile(nchunks - 1);
     return;
   }
 
@@ -425,17 +426,21 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     const int lw = wave - NCW;
     u32x4 buf[kInFlight][Cfg::kPerLoader];
     // Every loader issues exactly kPerLoader 16-byte loads per chunk (blocks
-    // past the end re-read the last valid address and are not stored), so the
-    // loads of one chunk form one contiguous group in the vmcnt order. V rows
-    // past the end of the sequence are loaded from a valid row and replaced by
-    // zeros when the chunk is written to LDS, after its loads have completed
-    // (selecting right after the load would force a wait on it).
-    auto v_byte = [&](int blk) __attribute__((always_inline)) {
-      return min((blk - R::kBlocks) * 1024 + lane * 16, Cfg::kVBytes - 16);   // V-area byte
-    };
+    // past the end re-read a valid address and are not stored), so the loads
+    // of one chunk form one contiguous group in the vmcnt order. The V block
+    // holds the slice's 16 columns of the chunk's token rows; lane l reads
+    // bytes 16l .. 16l + 15 of the row-major [token][16] tile (clamped), and
+    // stores them transposed ([column][token]) so that a compute lane finds
+    // its four tokens of one column side by side. Rows past the end of the
+    // sequence are loaded from a valid row and written as zeros, after the
+    // loads have completed (selecting right after the load would force a
+    // wait on it).
+    constexpr int kVRow = 16 * (int)sizeof(TIn);
+    constexpr int kVec = 16 / (int)sizeof(TIn);
+    const int v_e = min(lane * 16, Cfg::kVBytes - 16);
+    const int v_tt = v_e / kVRow, v_c0 = (v_e % kVRow) / (int)sizeof(TIn);
     auto load_chunk = [&](u32x4 (&dst)[Cfg::kPerLoader], int j) __attribute__((always_inline)) {
       const char* rec = rec0 + (size_t)j * R::kBytes;
-      const int tok0 = t_begin + kChunk * j;
       const int cnt = min(kChunk, len - kChunk * j);
 #pragma unroll
       for (int i = 0; i < Cfg::kPerLoader; ++i) {
@@ -444,27 +449,28 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
         if (blk < R::kBlocks) {
           src = rec + blk * 1024 + lane * 16;
         } else {
-          const int e = v_byte(blk);
-          const int vs = e / Cfg::kVSlice, rem = e % Cfg::kVSlice;
-          const int tt = min(rem / Cfg::kVRow, cnt - 1);
-          const int c0 = (rem % Cfg::kVRow) / (int)sizeof(TIn);
-          src = (const char*)(v + ((size_t)(tok0 + tt) * H + h) * D + 16 * (sg * SPW + vs) + c0);
+          const int tt = min(v_tt, cnt - 1);
+          src = (const char*)(v + ((size_t)(t_begin + kChunk * j + tt) * H + h) * D + 16 * s + v_c0);
         }
         dst[i] = *(const u32x4*)src;
       }
     };
     auto store_chunk = [&](const u32x4 (&src)[Cfg::kPerLoader], int j) __attribute__((always_inline)) {
-      char* slot = ring + (j % kRing) * Cfg::kSlot;
+      char* slot = slot_of(j);
       const int cnt = min(kChunk, len - kChunk * j);
 #pragma unroll
       for (int i = 0; i < Cfg::kPerLoader; ++i) {
         const int blk = lw + kLoaders * i;
         if (blk < R::kBlocks) {
           *(u32x4*)(slot + blk * 1024 + lane * 16) = src[i];
-        } else if (blk < Cfg::kBlocks) {
+        } else if (blk < Cfg::kBlocks && lane * 16 < Cfg::kVBytes) {
           const u32x4 zero = {0u, 0u, 0u, 0u};
-          const int tt = (v_byte(blk) % Cfg::kVSlice) / Cfg::kVRow;
-          *(u32x4*)(slot + blk * 1024 + lane * 16) = tt < cnt ? src[i] : zero;
+          const u32x4 x = v_tt < cnt ? src[i] : zero;
+          TIn* vt = (TIn*)(slot + R::kBytes);
+          TIn e[kVec];
+          __builtin_memcpy(e, &x, 16);
+#pragma unroll
+          for (int u = 0; u < kVec; ++u) vt[(v_c0 + u) * kChunk + v_tt] = e[u];
         }
       }
     };
@@ -479,7 +485,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     load_chunk(buf[0], min(kInFlight, last));
     lds_barrier();
     auto step = [&](auto A, int j) __attribute__((always_inline)) {
-      // publish chunk j + 1 before barrier j, then refill its registers
+      // publish chunk j + 1 before barrier B(j + 1), then refill its registers
       constexpr int set = (decltype(A)::value + 1) % kInFlight;
       const int c = j + 1;
       store_chunk(buf[set], c);
@@ -497,16 +503,15 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   }
 
   // ---------------- compute waves ----------------
-  // Compute wave w holds rows [hf * D/kHalves, (hf + 1) * D/kHalves) of slice
-  // sl (hf = w % kHalves). Its partial K~+ S and Q~ S over those rows go to LDS
-  // right after the state update; after the next barrier both halves add the
-  // two partials in the same order, so they derive bitwise the same delta.
-  // All operands of chunk j + 1 are copied from LDS to registers right after
-  // barrier j (two register sets alternate), so no LDS latency sits on the
-  // dependent chain; chunk j's output tile is formed in iteration j + 1.
-  const int sl = wave / Cfg::kHalves, hf = wave % Cfg::kHalves;
-  const int s = sg * SPW + sl;
-  const int mm = lane % 16, gq = lane / 16;
+  // Compute wave hf holds rows [hf * D/kHalves, (hf + 1) * D/kHalves) of the
+  // slice. Right after the state update it forms the next chunk's partial
+  // K~+ S over its rows (kept in a register and published to LDS) and partial
+  // (Q~ S)^T (for the output wave). After the next barrier each wave adds its
+  // partner's K~+ S partial to its own; with two halves that sum is the same
+  // bitwise in both waves (fp32 addition commutes), so both derive the same
+  // delta. The next chunk's operands are read from LDS right after the
+  // partner's partial, into the other of two register sets.
+  const int hf = wave;
   const int col = 16 * s + mm;
   const size_t state_base = (size_t)nh * D * D;
   constexpr int TW = Cfg::kTilesPerWave, PW = Cfg::kBlocksPerWave;
@@ -529,7 +534,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       bf16x8 kp[PW], qt[PW];
       bf16x8 kh[TW];
       f32x4 pc[TW];
-      bf16x8 tl0, tl1;
+      bf16x8 tl0;
       f32x4 vv;
     };
     auto read_ops = [&](ChunkOps& f, const char* slot) __attribute__((always_inline)) {
@@ -549,57 +554,45 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
         f.pc[t] = f32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
       }
       f.tl0 = *(const bf16x8*)(slot + R::kTL + lane * 32);
-      f.tl1 = *(const bf16x8*)(slot + R::kTL + lane * 32 + 16);
-      const char* vb = slot + R::kBytes + sl * Cfg::kVSlice;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) f.vv[i] = Elem<TIn>::load((const TIn*)(vb + (4 * gq + i) * Cfg::kVRow) + mm);
+      const TIn* vt = (const TIn*)(slot + R::kBytes) + mm * kChunk + 4 * gq;   // V^T[mm][4gq ..]
+      if constexpr (sizeof(TIn) == 2) f.vv = from_bf16x4(*(const bf16x4*)vt);
+      else f.vv = *(const f32x4*)vt;
     };
-    // partial products of a chunk over this wave's rows -> LDS
-    auto partials = [&](const ChunkOps& f, int parity) __attribute__((always_inline)) {
+    // partial products of a chunk over this wave's rows: K~+ S stays in u_own
+    // and goes to LDS for the partner, (Q~ S)^T goes to LDS for the output wave
+    f32x4 u_own;
+    auto partials = [&](const ChunkOps& f, int c) __attribute__((always_inline)) {
       f32x4 U = z, P = z;
 #pragma unroll
       for (int q = 0; q < PW; ++q) {
         const bf16x4 zero = {};
         const bf16x8 Bs = cat(to_bf16x4(acc[2 * q]), 2 * q + 1 < TW ? to_bf16x4(acc[2 * q + 1]) : zero);
         U = mfma32(f.kp[q], Bs, U);
-        P = mfma32(f.qt[q], Bs, P);
+        P = mfma32(Bs, f.qt[q], P);
       }
-      xbuf[parity][sl][hf][0][lane] = U;
-      xbuf[parity][sl][hf][1][lane] = P;
-    };
-    // output tile of chunk jo from its P and delta, to the LDS tile buffer
-    bf16x8 o_tl1 = {};
-    f32x4 o_P = z;
-    bf16x4 o_dhi = {}, o_dlo = {};
-    auto out_tile = [&](int jo) __attribute__((always_inline)) {
-      const bf16x4 l4 = lo_half(o_tl1);
-      const f32x4 out = mfma32(cat(l4, l4), cat(o_dhi, o_dlo), o_P);
-      char* otile = &obuf[jo & 1][sl * Cfg::kVSlice];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Elem<TIn>::store((TIn*)(otile + (4 * gq + i) * Cfg::kVRow) + mm, scale * out[i]);
+      u_own = U;
+      if (NCW > 1) xbuf[c % 4][hf][0][lane] = U;
+      xbuf[c % 4][hf][1][lane] = P;
     };
     // one chunk step: cur holds chunk j's operands; nxt receives chunk j + 1's
     auto step = [&](int j, ChunkOps& cur, ChunkOps& nxt) __attribute__((always_inline)) {
       lds_barrier();
-      read_ops(nxt, ring + ((j + 1) % kRing) * Cfg::kSlot);
-      const int parity = j & 1;
-      f32x4 U = xbuf[parity][sl][0][0][lane], P = xbuf[parity][sl][0][1][lane];
-#pragma unroll
-      for (int w = 1; w < Cfg::kHalves; ++w) {
-        U += xbuf[parity][sl][w][0][lane];
-        P += xbuf[parity][sl][w][1][lane];
-      }
+      f32x4 U = u_own;
+      if (NCW > 1) U += xbuf[j % 4][hf ^ 1][0][lane];
+      // the partner's partial is read before the next chunk's operands, so
+      // the wait for it does not include theirs (LDS returns in order)
+      __builtin_amdgcn_sched_barrier(0);
+      read_ops(nxt, slot_of(j + 1));
       bf16x4 r_hi, r_lo;
       split_bf16(cur.vv - U, r_hi, r_lo);
       const f32x4 dl = mfma32(cur.tl0, cat(r_hi, r_hi), z) + mfma32(cur.tl0, cat(r_lo, r_lo), z);
       bf16x4 d_hi, d_lo;
       split_bf16(dl, d_hi, d_lo);
+      if (hf == NCW - 1) dbuf[j % 2][lane] = cat(d_hi, d_lo);
       const bf16x8 dh2 = cat(d_hi, d_hi), dl2 = cat(d_lo, d_lo);
 #pragma unroll
       for (int t = 0; t < TW; ++t) acc[t] = mfma32(cur.kh[t], dl2, mfma32(cur.kh[t], dh2, acc[t] * cur.pc[t]));
-      partials(nxt, parity ^ 1);
-      if (hf == 0 && j > 0) out_tile(j - 1);
-      o_tl1 = cur.tl1; o_P = P; o_dhi = d_hi; o_dlo = d_lo;
+      partials(nxt, j + 1);
       if (ckpt_interval > 0) {
         const int done = kChunk * (j + 1);
         if (done <= len && done % ckpt_interval == 0) {
@@ -614,7 +607,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
 
     ChunkOps opsA, opsB;
     lds_barrier();
-    read_ops(opsA, ring);
+    read_ops(opsA, slot_of(0));
     partials(opsA, 0);
     int j = 0;
     for (; j + 2 <= nchunks; j += 2) {
@@ -622,7 +615,6 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       step(j + 1, opsB, opsA);
     }
     if (j < nchunks) step(j, opsA, opsB);
-    if (hf == 0) out_tile(nchunks - 1);
     lds_barrier();
   }
   if (final_state) {
@@ -656,7 +648,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     if (e != hipSuccess) return e;
   }
   using Cfg = ChainCfg<D, TIn>;
-  const unsigned blocks = (unsigned)((int64_t)a.num_seqs * a.H * (D / 16 / Cfg::kSlices));
+  const unsigned blocks = (unsigned)((int64_t)a.num_seqs * a.H * (D / 16));   // one per 16-column slice
   hipLaunchKernelGGL((chain_kernel<D, TIn>), dim3(blocks), dim3(Cfg::kThreads), 0, a.stream, (const TIn*)a.v,
                      a.cu_seqlens, seq_chunk_off, seq_ck_off, records, a.initial_state,
                      a.final_state, a.checkpoints, (TIn*)a.o, a.num_seqs, a.H, a.ckpt_interval,
