@@ -12,20 +12,28 @@ namespace {
 
 bool supported_dims(int32_t Dk, int32_t Dv) { return Dk == Dv && (Dk == 16 || Dk == 128); }
 
-// Validates cu_seqlens_host; on success returns total tokens and chunks.
-bool scan_lengths(const int32_t* cu, int32_t num_seqs, int64_t* tokens, int64_t* chunks) {
+// Validates cu_seqlens_host; on success returns total tokens and prefill
+// blocks (kda::kBlockTokens tokens each).
+bool scan_lengths(const int32_t* cu, int32_t num_seqs, int64_t* tokens, int64_t* blocks) {
   if (!cu || num_seqs < 0 || cu[0] != 0) return false;
   int64_t c = 0;
   for (int32_t n = 0; n < num_seqs; ++n) {
     if (cu[n + 1] < cu[n]) return false;
-    c += (cu[n + 1] - cu[n] + KDA_CHUNK - 1) / KDA_CHUNK;
+    c += (cu[n + 1] - cu[n] + kda::kBlockTokens - 1) / kda::kBlockTokens;
   }
   *tokens = cu[num_seqs];
-  *chunks = c;
+  *blocks = c;
   return c <= INT32_MAX;
 }
 
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+// Lowest decay floor the prefill accepts: a block's decayed keys span a
+// factor of up to exp(-32 g_min) (k / P_r with P_r >= exp(32 g_min)), which
+// must stay inside the fp32 / bf16 normal range (2^126) with margin.
+constexpr float kMinGateFloor = KDA_PREFILL_MIN_G_FLOOR;
+static_assert(kda::kBlockTokens * -KDA_PREFILL_MIN_G_FLOOR * 1.4426950408889634f < 120.f,
+              "decay span of a block");
 
 // Every tensor pointer must be 16-byte aligned (NULL passes).
 bool aligned16(std::initializer_list<const void*> ps) {
@@ -51,8 +59,8 @@ const char* kda_status_string(kda_status status) {
 
 int64_t kda_prefill_num_checkpoints(const int32_t* cu_seqlens_host, int32_t num_seqs,
                                     int32_t ckpt_interval) {
-  int64_t tokens, chunks;
-  if (!scan_lengths(cu_seqlens_host, num_seqs, &tokens, &chunks)) return -1;
+  int64_t tokens, blocks;
+  if (!scan_lengths(cu_seqlens_host, num_seqs, &tokens, &blocks)) return -1;
   if (ckpt_interval <= 0) return 0;
   int64_t total = 0;
   for (int32_t n = 0; n < num_seqs; ++n)
@@ -62,10 +70,10 @@ int64_t kda_prefill_num_checkpoints(const int32_t* cu_seqlens_host, int32_t num_
 
 size_t kda_prefill_workspace_size(const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
                                   int32_t Dk, int32_t Dv) {
-  int64_t tokens, chunks;
-  if (H <= 0 || !supported_dims(Dk, Dv) || !scan_lengths(cu_seqlens_host, num_seqs, &tokens, &chunks))
+  int64_t tokens, blocks;
+  if (H <= 0 || !supported_dims(Dk, Dv) || !scan_lengths(cu_seqlens_host, num_seqs, &tokens, &blocks))
     return 0;
-  return kda::prefill_layout(num_seqs, chunks, H, Dk).total;
+  return kda::prefill_layout(num_seqs, blocks, H, Dk).total;
 }
 
 kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_dtype dtype,
@@ -77,9 +85,10 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
   if (!supported_dims(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
-  int64_t tokens, chunks;
-  if (H <= 0 || num_seqs < 0 || !cu_seqlens || !scan_lengths(cu_seqlens_host, num_seqs, &tokens, &chunks))
+  int64_t tokens, blocks;
+  if (H <= 0 || num_seqs < 0 || !cu_seqlens || !scan_lengths(cu_seqlens_host, num_seqs, &tokens, &blocks))
     return KDA_ERR_INVALID_ARG;
+  if (!(g_min >= kMinGateFloor && g_min <= 0.f)) return KDA_ERR_INVALID_ARG;
   if ((int64_t)num_seqs * H * (Dv / 16) > INT32_MAX || tokens * (int64_t)H > INT32_MAX)
     return KDA_ERR_INVALID_ARG;
   if (tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARG;
@@ -90,14 +99,14 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_
   if (!aligned16({q, k, v, g, beta, cu_seqlens, initial_state, final_state, checkpoints, o}))
     return KDA_ERR_INVALID_ARG;
   if (num_seqs == 0) return KDA_OK;
-  const kda::PrefillLayout L = kda::prefill_layout(num_seqs, chunks, H, Dk);
+  const kda::PrefillLayout L = kda::prefill_layout(num_seqs, blocks, H, Dk);
   if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255)) return KDA_ERR_WORKSPACE;
 
   kda::PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.cu_seqlens = cu_seqlens;
   a.num_seqs = num_seqs; a.H = H; a.D = Dk;
-  a.total_tokens = tokens; a.total_chunks = chunks;
+  a.total_tokens = tokens; a.total_blocks = blocks;
   a.scale = scale; a.g_min = g_min;
   a.initial_state = initial_state; a.final_state = final_state;
   a.ckpt_interval = nck > 0 ? ckpt_interval : 0;

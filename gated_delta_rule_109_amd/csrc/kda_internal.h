@@ -8,6 +8,9 @@
 
 namespace kda {
 
+// Tokens per prefill block: the chain takes one step per two 16-token chunks.
+constexpr int kBlockTokens = 32;
+
 struct DecodeArgs {
   const void *q, *k, *v;
   const float *g, *beta;
@@ -25,7 +28,7 @@ struct PrefillArgs {
   const int32_t* cu_seqlens;  // device
   int32_t num_seqs, H, D;
   int64_t total_tokens;
-  int64_t total_chunks;       // sum_n ceil(L_n / 16), from the host copy
+  int64_t total_blocks;       // sum_n ceil(L_n / kBlockTokens), from the host copy
   float scale, g_min;
   const float* initial_state;
   float* final_state;
@@ -39,15 +42,15 @@ struct PrefillArgs {
 
 // Workspace layout of the prefill (all offsets 256-byte aligned).
 struct PrefillLayout {
-  size_t seq_chunk_off;   // int32 [N + 1]
+  size_t seq_blk_off;     // int32 [N + 1]
   size_t seq_ck_off;      // int32 [N + 1]
-  size_t chunk_info;      // int2  [total_chunks] (first token, valid tokens)
-  size_t records;         // per (chunk, head) operand records
+  size_t blk_info;        // int2  [total_blocks] (first token, valid tokens)
+  size_t records;         // per (block, head) operand records
   size_t record_bytes;    // bytes of one record
   size_t total;
 };
 
-PrefillLayout prefill_layout(int32_t num_seqs, int64_t total_chunks, int32_t H, int32_t D);
+PrefillLayout prefill_layout(int32_t num_seqs, int64_t total_blocks, int32_t H, int32_t D);
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);

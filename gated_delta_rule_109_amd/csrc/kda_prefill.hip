@@ -6,8 +6,8 @@
 // [K3-DD] "MoonshotAI/Kimi-K3 딥다이브", 4-1 KDA, second bullet: 16-token
 // tiles, dense products inside a tile, a recurrence only between tiles.
 //
-// Chunk algebra (one chunk of c <= 16 tokens r = 1..c, entry state S,
-// per-channel in-chunk cumulative decay P_r = prod_{j<=r} alpha_j = e^{G_r},
+// Block algebra (one block of c <= 32 tokens r = 1..c, entry state S,
+// per-channel in-block cumulative decay P_r = prod_{j<=r} alpha_j = e^{G_r},
 // Pc = P_c, B_r = Pc / P_r):
 //   Kp = k (.) P      Qt = q (.) P      Kh = k (.) B      Km = k (.) P^{-1}
 //   A  = strictlower(diag(beta) Kp Km^T),   L = lower_incl(Qt Km^T)
@@ -15,23 +15,28 @@
 //   delta = T (V - Kp S)
 //   O     = scale (Qt S + L delta)
 //   S'    = Diag(Pc) S + Kh^T delta
-// A tail chunk is padded with k = q = 0, alpha = 1, beta = 0, which leaves the
-// state and the valid outputs unchanged.
+// The algebra holds for any block length; the sequential chain takes one step
+// per two 16-token chunks of the pages (a 32-token block), which halves the
+// number of dependent steps while every product keeps the 16 x 16 MFMA tile
+// of a chunk. A tail block is padded with k = q = 0, alpha = 1, beta = 0,
+// which leaves the state and the valid outputs unchanged. The state after the
+// first 16 tokens of a block (a checkpoint position when the interval is an
+// odd multiple of 16) is Diag(P_16) S + Diag(P_16 / Pc) Kh[<16]^T delta[<16].
 //
 // Three kernels, all on the caller's stream:
-//  1. plan_kernel   (1 workgroup): per-sequence chunk / checkpoint offsets and
-//                   a chunk -> (first token, valid tokens) table.
-//  2. prep_kernel   (one workgroup per chunk and head, fully parallel): gates,
+//  1. plan_kernel   (1 workgroup): per-sequence block / checkpoint offsets and
+//                   a block -> (first token, valid tokens) table.
+//  2. prep_kernel   (one workgroup per block and head, fully parallel): gates,
 //                   decayed operands, A and L on MFMA, T by forward
-//                   substitution; writes one "record" per (chunk, head) whose
+//                   substitution; writes one "record" per (block, head) whose
 //                   byte layout is exactly the MFMA operand fragments the chain
 //                   kernel consumes, lane by lane.
 //  3. chain_kernel  (one workgroup per sequence, head and 16-column slice of the
-//                   state): the sequential recurrence over chunks. Columns of S
+//                   state): the sequential recurrence over blocks. Columns of S
 //                   evolve independently, so each slice runs on its own. The
 //                   fp32 state slice lives in the MFMA accumulators of two
 //                   compute waves (half the rows each); loader waves stream
-//                   records into an LDS ring several chunks ahead and an
+//                   records into an LDS ring several blocks ahead and an
 //                   output wave forms and stores the output tiles.
 //
 // Precision: MFMA operands are bf16 with fp32 accumulation. The decayed key of
@@ -43,55 +48,66 @@
 
 namespace kda {
 
+constexpr int kBT = kBlockTokens;   // tokens per block (two chunks)
+
 // ---- record layout ----------------------------------------------------------
-// One record per (chunk, head), stored head-major (record h * total_chunks + c);
-// byte offsets within a record (1 KiB = one 16-byte-per-lane wave load):
-//   Kp  : NP blocks. Block p, lane l (token m = l%16, g = l/16):
-//         Kp[m][32p + 4g + 0..3], Kp[m][32p + 16 + 4g + 0..3]   (bf16 x 8)
-//   Qt  : same for Qt.
-//   Kh  : NT blocks. Block t, lane l (channel 16t + l%16, g = l/16):
-//         Kh_hi[4g + 0..3][ch], Kh_lo[4g + 0..3][ch]            (bf16 x 8)
-//   TL  : 2 blocks. Lane l (row r = l%16, g = l/16), 32 bytes:
-//         T_hi[r][4g + 0..3], T_lo[r][4g + 0..3], L[r][4g + 0..3] (bf16 x 12),
-//         then the chunk decay Pc[2l], Pc[2l + 1] of channels 2l, 2l + 1 (fp32).
-// The 32-wide k index of the Kp/Qt fragments interleaves two 16-row tiles of
-// S (k = 8g + j <-> channel 32p + 4g + j for j < 4, 32p + 16 + 4g + j - 4
-// otherwise), matching the order in which the MFMA accumulator layout holds S,
-// so the state feeds the next product without leaving registers.
+// One record per (block, head), stored head-major (record h * total_blocks + b);
+// it is a sequence of 1 KiB fragments (one 16-byte-per-lane wave load each).
+// Two index orders appear in the fragments:
+//  - a 32-deep contraction over key channels (k block p) uses channel
+//      ch(p, 8g + j) = 32p + 4g + j (j < 4),  32p + 16 + 4g + j - 4 (j >= 4),
+//    the order in which the MFMA accumulator layout holds two 16-row tiles of
+//    S, so the state feeds the next product without leaving registers;
+//  - a 32-deep contraction over the tokens of a block uses
+//      tok(8g + j) = 4g + j (j < 4),  16 + 4g + j - 4 (j >= 4),
+//    the order in which two 16-token accumulator tiles (tokens 0-15, 16-31)
+//    concatenate.
+// Lane l below has mm = l % 16, g = l / 16; "x 8" lists j = 0..7.
+//   Kp  [u][p]  (u = token tile, p < NP):  Kp[16u + mm][ch(p, 8g + j)]  bf16 x 8
+//   Qt  [u][p]:                            Qt[16u + mm][ch(p, 8g + j)]  bf16 x 8
+//   Kh  [rt][hi, lo]  (rt = row tile):     Kh[tok(8g + j)][16rt + mm]   bf16 x 8
+//   T   [u]  (2 KiB, 32 bytes per lane):   T[16u + mm][tok(8g + j)]     hi x 8, lo x 8
+//   L   [u]:                               L[16u + mm][tok(8g + j)]     bf16 x 8
+//   Pc  : Pc[0..D) then P_16[0..D), fp32 (decay over the whole block and over
+//         its first 16 tokens, per channel).
+__device__ __forceinline__ int ch_of(int p, int g, int j) { return j < 4 ? 32 * p + 4 * g + j : 32 * p + 16 + 4 * g + j - 4; }
+
 template <int D>
 struct Rec {
   static constexpr int NT = D / 16;          // 16-row tiles of S
   static constexpr int NP = (NT + 1) / 2;    // 32-deep k blocks over channels
   static constexpr int kKp = 0;
-  static constexpr int kQt = NP * 1024;
-  static constexpr int kKh = 2 * NP * 1024;
-  static constexpr int kTL = (2 * NP + NT) * 1024;
-  static constexpr int kBlocks = 2 * NP + NT + 2;
-  static constexpr int kBytes = kBlocks * 1024;
+  static constexpr int kQt = kKp + 2 * NP * 1024;
+  static constexpr int kKh = kQt + 2 * NP * 1024;
+  static constexpr int kT = kKh + 2 * NT * 1024;
+  static constexpr int kL = kT + 4 * 1024;
+  static constexpr int kPc = kL + 2 * 1024;
+  static constexpr int kFrags = kPc / 1024 + (8 * D + 1023) / 1024;
+  static constexpr int kBytes = kFrags * 1024;
 };
 
 size_t record_bytes(int D) { return D == 128 ? Rec<128>::kBytes : Rec<16>::kBytes; }
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-PrefillLayout prefill_layout(int32_t num_seqs, int64_t total_chunks, int32_t H, int32_t D) {
+PrefillLayout prefill_layout(int32_t num_seqs, int64_t total_blocks, int32_t H, int32_t D) {
   PrefillLayout L;
   size_t off = 0;
-  L.seq_chunk_off = off; off = align256(off + sizeof(int32_t) * (size_t)(num_seqs + 1));
-  L.seq_ck_off = off;    off = align256(off + sizeof(int32_t) * (size_t)(num_seqs + 1));
-  L.chunk_info = off;    off = align256(off + 2 * sizeof(int32_t) * (size_t)total_chunks);
+  L.seq_blk_off = off; off = align256(off + sizeof(int32_t) * (size_t)(num_seqs + 1));
+  L.seq_ck_off = off;  off = align256(off + sizeof(int32_t) * (size_t)(num_seqs + 1));
+  L.blk_info = off;    off = align256(off + 2 * sizeof(int32_t) * (size_t)total_blocks);
   L.records = off;
   L.record_bytes = record_bytes(D);
-  off += L.record_bytes * (size_t)total_chunks * (size_t)H;
+  off += L.record_bytes * (size_t)total_blocks * (size_t)H;
   L.total = off;
   return L;
 }
 
 // ---- 1. plan ----------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu, int N,
-                                                    int ckpt_interval, int32_t* seq_chunk_off,
-                                                    int32_t* seq_ck_off, int2* chunk_info,
-                                                    int total_chunks) {
+                                                    int ckpt_interval, int32_t* seq_blk_off,
+                                                    int32_t* seq_ck_off, int2* blk_info,
+                                                    int total_blocks) {
   __shared__ int s_c[1024], s_k[1024];
   __shared__ int carry_c, carry_k;
   const int tid = threadIdx.x;
@@ -100,7 +116,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   for (int base = 0; base < N; base += 1024) {
     const int n = base + tid;
     const int len = n < N ? cu[n + 1] - cu[n] : 0;
-    const int vc = (len + kChunk - 1) / kChunk;
+    const int vc = (len + kBT - 1) / kBT;
     const int vk = ckpt_interval > 0 ? len / ckpt_interval : 0;
     s_c[tid] = vc;
     s_k[tid] = vk;
@@ -114,7 +130,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       __syncthreads();
     }
     if (n < N) {
-      seq_chunk_off[n] = carry_c + s_c[tid] - vc;
+      seq_blk_off[n] = carry_c + s_c[tid] - vc;
       seq_ck_off[n] = carry_k + s_k[tid] - vk;
     }
     __syncthreads();
@@ -125,228 +141,284 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     __syncthreads();
   }
   if (tid == 0) {
-    seq_chunk_off[N] = carry_c;
+    seq_blk_off[N] = carry_c;
     seq_ck_off[N] = carry_k;
   }
   __syncthreads();
-  for (int c = tid; c < total_chunks; c += 1024) {
-    // last n with seq_chunk_off[n] <= c (skips empty sequences)
+  for (int c = tid; c < total_blocks; c += 1024) {
+    // last n with seq_blk_off[n] <= c (skips empty sequences)
     int lo = 0, hi = N - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (seq_chunk_off[mid] <= c) lo = mid; else hi = mid - 1;
+      if (seq_blk_off[mid] <= c) lo = mid; else hi = mid - 1;
     }
-    const int t0 = cu[lo] + kChunk * (c - seq_chunk_off[lo]);
-    const int cnt = min(kChunk, cu[lo + 1] - t0);
-    chunk_info[c] = make_int2(t0, cnt);
+    const int t0 = cu[lo] + kBT * (c - seq_blk_off[lo]);
+    const int cnt = min(kBT, cu[lo + 1] - t0);
+    blk_info[c] = make_int2(t0, cnt);
   }
 }
 
-// ---- 2. per-chunk preparation ------------------------------------------------------
+// ---- 2. per-block preparation ------------------------------------------------------
+// Two phases per (block, head):
+//  1. one thread per key channel: gates, the in-block cumulative decay P_r
+//     (kept in LDS), Pc and P_16, and the Kh fragments (Kh needs every token
+//     of one channel, which this mapping holds);
+//  2. one lane per (token, 8 channels) in exactly the fragment layout: each
+//     lane loads its q / k pieces, scales them by P (Kp, Qt) and 1 / P (Km),
+//     stores the Kp / Qt fragments and keeps all three in registers for the
+//     A and L products, which need no LDS staging.
+// Then T by blocks from A (LDS), with L written straight from the MFMA.
+template <int D>
+constexpr int prep_threads() { return D >= 128 ? D : 64; }
+
 template <int D, typename TIn>
-__global__ __launch_bounds__(D >= 64 ? D : 64) void prep_kernel(
+__global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ g,
-    const float* __restrict__ beta, const int2* __restrict__ chunk_info, int H, float g_min,
+    const float* __restrict__ beta, const int2* __restrict__ blk_info, int H, float g_min,
     char* __restrict__ records) {
   using R = Rec<D>;
-  constexpr int kThreads = D >= 64 ? D : 64;
-  // Rows padded by 16 bytes so that the 16 token rows of a fragment read fall
-  // on different LDS banks.
-  constexpr int DP = D + 8;
-  // The input staging rows (q, k, g) and the decayed operands (Kp, Qt, Km)
-  // share one LDS buffer; a barrier separates the last staging read from the
-  // first operand write. Keeping LDS small lets more workgroups overlap their
-  // load latency.
-  constexpr int kStageBytes = 2 * kChunk * DP * (int)sizeof(TIn) + kChunk * (D + 4) * 4;
-  constexpr int kOpBytes = 3 * kChunk * DP * 2;
-  __shared__ __attribute__((aligned(16))) char lds_raw[kStageBytes > kOpBytes ? kStageBytes : kOpBytes];
-  __bf16(*sKp)[DP] = (__bf16(*)[DP])lds_raw;
-  __bf16(*sQt)[DP] = (__bf16(*)[DP])(lds_raw + kChunk * DP * 2);
-  __bf16(*sKm)[DP] = (__bf16(*)[DP])(lds_raw + 2 * kChunk * DP * 2);
-  __shared__ __attribute__((aligned(16))) float sA[kChunk][kChunk];
-  __shared__ __attribute__((aligned(16))) float sL[kChunk][kChunk];
-  __shared__ __attribute__((aligned(16))) float sT[kChunk][kChunk];
-  __shared__ float sBeta[kChunk];
+  constexpr int kThreads = prep_threads<D>();
+  constexpr int kWaves = kThreads / kWave;
+  // P[r][ch] (fp32, rows padded by 16 bytes) during phases 1-2, then the
+  // blocks of T.
+  constexpr int kPBytes = kBT * (D + 4) * 4;
+  constexpr int kTBytes = (kBT * (kBT + 4) + 2 * 16 * 20) * 4;
+  __shared__ __attribute__((aligned(16))) char lds_raw[kPBytes > kTBytes ? kPBytes : kTBytes];
+  float(*sP)[D + 4] = (float(*)[D + 4])lds_raw;
+  float(*sT)[kBT + 4] = (float(*)[kBT + 4])lds_raw;
+  float(*sX)[20] = (float(*)[20])(lds_raw + kBT * (kBT + 4) * 4);                  // (I + A_bb)^{-1}
+  float(*sM)[20] = (float(*)[20])(lds_raw + (kBT * (kBT + 4) + 16 * 20) * 4);      // A_ba T_aa
+  __shared__ __attribute__((aligned(16))) float sA[kBT][kBT + 4];
+  __shared__ float sBeta[kBT];
 
   // Heads vary fastest across consecutive workgroups: the H heads of one token
   // row are contiguous in q, k, v and g, so neighbouring workgroups read
   // neighbouring memory.
   const int h = blockIdx.x, c = blockIdx.y;
   const int tid = threadIdx.x;
-  const int2 ci = chunk_info[c];
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int mm = lane % 16, gq = lane / 16;
+  const int2 ci = blk_info[c];
   const int tok0 = ci.x, cnt = ci.y;
-  char* rec = records + ((size_t)h * gridDim.y + c) * R::kBytes;   // head-major: a head's chunks are contiguous
+  char* rec = records + ((size_t)h * gridDim.y + c) * R::kBytes;   // head-major: a head's blocks are contiguous
+  auto row = [&](int t) __attribute__((always_inline)) { return ((size_t)(tok0 + t) * H + h) * D; };
 
-  if (tid < kChunk) sBeta[tid] = tid < cnt ? beta[(size_t)(tok0 + tid) * H + h] : 0.f;
+  if (tid < kBT) sBeta[tid] = tid < cnt ? beta[(size_t)(tok0 + tid) * H + h] : 0.f;
 
-  // Stage the chunk's q, k and g rows in LDS with 16-byte loads (a token row
-  // of one head is contiguous), then read them back one channel per thread.
-  // Rows past the end of the sequence are zero (g = 0 gives alpha = 1).
-  TIn(*sQin)[DP] = (TIn(*)[DP])lds_raw;
-  TIn(*sKin)[DP] = (TIn(*)[DP])(lds_raw + kChunk * DP * sizeof(TIn));
-  float(*sGin)[D + 4] = (float(*)[D + 4])(lds_raw + 2 * kChunk * DP * sizeof(TIn));
-  {
-    constexpr int kVec = 16 / (int)sizeof(TIn);        // elements per 16-byte load
-    constexpr int kQK = kChunk * D / kVec;              // 16-byte pieces of q (and of k)
-    constexpr int kG = kChunk * D / 4;                  // 16-byte pieces of g
-    for (int e = tid; e < 2 * kQK + kG; e += kThreads) {
-      if (e < 2 * kQK) {
-        const int which = e / kQK, r = e % kQK;
-        const int t = r / (D / kVec), c = (r % (D / kVec)) * kVec;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (t < cnt) x = *(const u32x4*)((which ? k : q) + ((size_t)(tok0 + t) * H + h) * D + c);
-        *(u32x4*)&(which ? sKin : sQin)[t][c] = x;
-      } else {
-        const int r = e - 2 * kQK;
-        const int t = r / (D / 4), c = (r % (D / 4)) * 4;
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (t < cnt) x = *(const f32x4*)(g + ((size_t)(tok0 + t) * H + h) * D + c);
-        *(f32x4*)&sGin[t][c] = x;
-      }
-    }
-  }
-  __syncthreads();
-
-  float kf[kChunk], qf[kChunk], a[kChunk];
+  // ---- phase 1: one channel per thread (coalesced rows). Rows past the end
+  // of the sequence give alpha = 1 and k = 0. Every load reads a valid row
+  // (clamped) and the padding is selected afterwards: a load under a
+  // condition becomes a branch that waits for it before the next one.
   if (tid < D) {
     const int ch = tid;
+    float a[kBT], kf[kBT];
 #pragma unroll
-    for (int t = 0; t < kChunk; ++t) {
-      kf[t] = Elem<TIn>::load(&sKin[t][ch]);
-      qf[t] = Elem<TIn>::load(&sQin[t][ch]);
-      a[t] = gate_alpha(sGin[t][ch], g_min);
+    for (int t = 0; t < kBT; ++t) {
+      const int tc = min(t, cnt - 1);
+      a[t] = g[row(tc) + ch];
+      kf[t] = Elem<TIn>::load(k + row(tc) + ch);
     }
-  }
-  __syncthreads();   // staging reads done before the operand rows overwrite them
-  if (tid < D) {
-    const int ch = tid;
-    float P = 1.f;
 #pragma unroll
-    for (int t = 0; t < kChunk; ++t) {
+    for (int t = 0; t < kBT; ++t) {
+      a[t] = t < cnt ? gate_alpha(a[t], g_min) : 1.f;
+      kf[t] = t < cnt ? kf[t] : 0.f;
+    }
+    float P = 1.f, P16 = 1.f;
+#pragma unroll
+    for (int t = 0; t < kBT; ++t) {
       P *= a[t];
-      sKp[t][ch] = (__bf16)(kf[t] * P);
-      sQt[t][ch] = (__bf16)(qf[t] * P);
+      sP[t][ch] = P;
+      if (t == kChunk - 1) P16 = P;
     }
-    const float Pc = P, rPc = 1.f / Pc;
-    float kh[kChunk];
+    // Kh_t = k_t * prod_{s > t} alpha_s (in place of k), token groups
+    // g = 0..3 of this channel
+    float* kh = kf;
     float Bk = 1.f;
 #pragma unroll
-    for (int t = kChunk - 1; t >= 0; --t) {
+    for (int t = kBT - 1; t >= 0; --t) {
       kh[t] = kf[t] * Bk;
-      sKm[t][ch] = (__bf16)(kh[t] * rPc);
       Bk *= a[t];
     }
-    // Kh fragments: this thread's channel, token groups g = 0..3.
-    const int rt = ch / 16, mm = ch % 16;
+    const int rt = ch / 16, cm = ch % 16;
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      f32x4 x = {kh[4 * gq], kh[4 * gq + 1], kh[4 * gq + 2], kh[4 * gq + 3]};
-      bf16x4 hi, lo;
-      split_bf16(x, hi, lo);
-      *(bf16x8*)(rec + R::kKh + rt * 1024 + (16 * gq + mm) * 16) = cat(hi, lo);
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 x0 = {kh[4 * g4], kh[4 * g4 + 1], kh[4 * g4 + 2], kh[4 * g4 + 3]};
+      const f32x4 x1 = {kh[16 + 4 * g4], kh[16 + 4 * g4 + 1], kh[16 + 4 * g4 + 2], kh[16 + 4 * g4 + 3]};
+      bf16x4 hi0, lo0, hi1, lo1;
+      split_bf16(x0, hi0, lo0);
+      split_bf16(x1, hi1, lo1);
+      *(bf16x8*)(rec + R::kKh + (2 * rt) * 1024 + (16 * g4 + cm) * 16) = cat(hi0, hi1);
+      *(bf16x8*)(rec + R::kKh + (2 * rt + 1) * 1024 + (16 * g4 + cm) * 16) = cat(lo0, lo1);
     }
-    ((float*)(rec + R::kTL + (ch / 2) * 32 + 24))[ch % 2] = Pc;
+    ((float*)(rec + R::kPc))[ch] = P;
+    ((float*)(rec + R::kPc))[D + ch] = P16;
   }
   __syncthreads();
 
-  // Kp / Qt fragments in the chain kernel's k order.
-  for (int r = tid; r < 2 * R::NP * kWave; r += kThreads) {
-    const int which = r / (R::NP * kWave), rr = r % (R::NP * kWave);
-    const int p = rr / kWave, l = rr % kWave, mm = l % 16, gq = l / 16;
-    const __bf16(*src)[DP] = which ? sQt : sKp;
-    const int ch0 = 32 * p + 4 * gq, ch1 = 32 * p + 16 + 4 * gq;
-    const bf16x4 zero = {};
-    const bf16x4 a0 = ch0 < D ? *(const bf16x4*)&src[mm][ch0] : zero;
-    const bf16x4 a1 = ch1 < D ? *(const bf16x4*)&src[mm][ch1] : zero;
-    *(bf16x8*)(rec + (which ? R::kQt : R::kKp) + p * 1024 + l * 16) = cat(a0, a1);
-  }
-
-  // A = Kp Km^T (wave 0) and Qt Km^T (wave 1; wave 0 when only one wave).
+  // ---- phase 2: fragments (u, p), lane = (token 16u + mm, channels
+  // ch(p, gq, 0..7)). Wave 0 forms Kp and A = diag(beta) Kp Km^T; wave 1 (or
+  // wave 0 when it is the only one) forms Qt and L = Qt Km^T, the latter
+  // transposed (Km as the A operand) so that each lane holds L[16ut + mm]
+  // [16us + 4gq .. +3]: the (us = 0, us = 1) pair of a token tile is exactly
+  // its L fragment. Every wave forms Km.
   {
-    const int wave = tid / kWave, lane = tid % kWave;
-    const int mm = lane % 16, gq = lane / 16;
-    constexpr int kWaves = kThreads / kWave;
+    // (clamped loads, padding selected after the loads: see phase 1)
+    auto piece = [&](const TIn* base, int t, int ch0) __attribute__((always_inline)) {
+      const TIn* ptr = base + row(min(t, cnt - 1)) + (ch0 < D ? ch0 : 0);
+      f32x4 x;
+      if constexpr (sizeof(TIn) == 2) x = from_bf16x4(*(const bf16x4*)ptr);
+      else x = *(const f32x4*)ptr;
+      return t < cnt && ch0 < D ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto decay = [&](int t, int ch0) __attribute__((always_inline)) {
+      const f32x4 x = *(const f32x4*)&sP[t][ch0 < D ? ch0 : 0];
+      return ch0 < D ? x : f32x4{1.f, 1.f, 1.f, 1.f};
+    };
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       if (!(wave == which || (kWaves == 1 && wave == 0))) continue;
-      const __bf16(*src)[DP] = which ? sQt : sKp;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const TIn* src = which ? q : k;
+      bf16x8 X[2][R::NP], Km[2][R::NP];
 #pragma unroll
-      for (int p = 0; p < R::NP; ++p) {
-        const int chs = 32 * p + 8 * gq;
-        const bf16x8 zero = {};
-        const bf16x8 av = chs + 8 <= D ? *(const bf16x8*)&src[mm][chs] : zero;
-        const bf16x8 bv = chs + 8 <= D ? *(const bf16x8*)&sKm[mm][chs] : zero;
-        acc = mfma32(av, bv, acc);
-      }
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * gq + i;
-        if (which == 0) sA[r][mm] = mm < r ? sBeta[r] * acc[i] : 0.f;
-        else sL[r][mm] = mm <= r ? acc[i] : 0.f;
+        for (int p = 0; p < R::NP; ++p) {
+          const int t = 16 * u + mm, c0 = ch_of(p, gq, 0), c1 = ch_of(p, gq, 4);
+          const f32x4 P0 = decay(t, c0), P1 = decay(t, c1);
+          const f32x4 x0 = piece(src, t, c0), x1 = piece(src, t, c1);
+          X[u][p] = cat(to_bf16x4(x0 * P0), to_bf16x4(x1 * P1));
+          const f32x4 k0 = which ? piece(k, t, c0) : x0, k1 = which ? piece(k, t, c1) : x1;
+          f32x4 r0, r1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { r0[i] = k0[i] / P0[i]; r1[i] = k1[i] / P1[i]; }
+          Km[u][p] = cat(to_bf16x4(r0), to_bf16x4(r1));
+          *(bf16x8*)(rec + (which ? R::kQt : R::kKp) + (u * R::NP + p) * 1024 + lane * 16) = X[u][p];
+        }
+#pragma unroll
+      for (int ut = 0; ut < 2; ++ut) {
+        bf16x4 lfrag[2];
+#pragma unroll
+        for (int us = 0; us < 2; ++us) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          if (us <= ut) {
+#pragma unroll
+            for (int p = 0; p < R::NP; ++p)
+              acc = which ? mfma32(Km[us][p], X[ut][p], acc) : mfma32(X[ut][p], Km[us][p], acc);
+          }
+          if (which == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 16 * ut + 4 * gq + i, s = 16 * us + mm;
+              sA[r][s] = s < r ? sBeta[r] * acc[i] : 0.f;
+            }
+          } else {
+            f32x4 lv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lv[i] = 16 * us + 4 * gq + i <= 16 * ut + mm ? acc[i] : 0.f;
+            lfrag[us] = to_bf16x4(lv);
+          }
+        }
+        if (which == 1) *(bf16x8*)(rec + R::kL + ut * 1024 + lane * 16) = cat(lfrag[0], lfrag[1]);
       }
     }
   }
   __syncthreads();
 
-  // T = (I + A)^{-1} diag(beta): forward substitution, one column per lane.
-  if (tid < kChunk) {
-    const int j = tid;
-    float x[kChunk];
+  // ---- T = (I + A)^{-1} diag(beta) by blocks (a = tokens 0-15, b = 16-31):
+  //   T_aa = X_a diag(beta_a),  T_bb = X_b diag(beta_b),
+  //   T_ba = -X_b (A_ba T_aa),  X = (I + A_diag-block)^{-1},
+  // the diagonal blocks by forward substitution (lane j: column j % 16 of
+  // block j / 16), then two 16 x 16 products. T reuses the P storage.
+  if (tid < kBT) {
+    const int blk = tid / 16, j = tid % 16, off = 16 * blk;
+    float x[16];
 #pragma unroll
-    for (int r = 0; r < kChunk; ++r) {
+    for (int r = 0; r < 16; ++r) {
       float acc = r == j ? 1.f : 0.f;
 #pragma unroll
-      for (int i = 0; i < r; ++i) acc -= sA[r][i] * x[i];
+      for (int i4 = 0; i4 < r; i4 += 4) {
+        const f32x4 arow = *(const f32x4*)&sA[off + r][off + i4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (i4 + e < r) acc -= arow[e] * x[i4 + e];
+      }
       x[r] = acc;
     }
-    const float bj = sBeta[j];
+    const float bj = sBeta[off + j];
 #pragma unroll
-    for (int r = 0; r < kChunk; ++r) sT[r][j] = x[r] * bj;
+    for (int r = 0; r < 16; ++r) {
+      sT[off + r][off + j] = x[r] * bj;
+      sT[r][16 + j] = 0.f;             // upper block (written twice, same value)
+      if (blk == 1) sX[r][j] = x[r];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < 256; e += kThreads) {   // M = A_ba T_aa
+    const int r = e / 16, j = e % 16;
+    float acc = 0.f;
+#pragma unroll
+    for (int s4 = 0; s4 < 16; s4 += 4) {
+      const f32x4 arow = *(const f32x4*)&sA[16 + r][s4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += arow[u] * sT[s4 + u][j];
+    }
+    sM[r][j] = acc;
+  }
+  __syncthreads();
+  for (int e = tid; e < 256; e += kThreads) {   // T_ba = -X_b M
+    const int r = e / 16, j = e % 16;
+    float acc = 0.f;
+#pragma unroll
+    for (int i4 = 0; i4 < 16; i4 += 4) {
+      const f32x4 xrow = *(const f32x4*)&sX[r][i4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += xrow[u] * sM[i4 + u][j];
+    }
+    sT[16 + r][j] = -acc;
   }
   __syncthreads();
 
-  if (tid < kWave) {
-    const int r = tid % 16, gq = tid / 16;
-    const f32x4 t4 = *(const f32x4*)&sT[r][4 * gq];
-    const f32x4 l4 = *(const f32x4*)&sL[r][4 * gq];
-    bf16x4 hi, lo;
-    split_bf16(t4, hi, lo);
-    *(bf16x8*)(rec + R::kTL + tid * 32) = cat(hi, lo);
-    *(bf16x4*)(rec + R::kTL + tid * 32 + 16) = to_bf16x4(l4);
+  // T fragments (hi | lo), the A operand of delta.
+  for (int r = tid; r < 2 * kWave; r += kThreads) {
+    const int u = r / kWave, l = r % kWave, lm = l % 16, lg = l / 16;
+    const int tr = 16 * u + lm;
+    const f32x4 t0 = *(const f32x4*)&sT[tr][4 * lg], t1 = *(const f32x4*)&sT[tr][16 + 4 * lg];
+    bf16x4 h0, lo0, h1, lo1;
+    split_bf16(t0, h0, lo0);
+    split_bf16(t1, h1, lo1);
+    *(bf16x8*)(rec + R::kT + u * 2048 + l * 32) = cat(h0, h1);
+    *(bf16x8*)(rec + R::kT + u * 2048 + l * 32 + 16) = cat(lo0, lo1);
   }
 }
 
-// ---- 3. the recurrence over chunks ------------------------------------------------------
+// ---- 3. the recurrence over blocks ------------------------------------------------------
 // A workgroup owns one 16-column slice of one (sequence, head) state (columns
 // of S evolve independently, so slices never talk to each other).
 //  - kHalves compute waves split the slice's D rows: each holds D / kHalves
 //    rows of the fp32 state in MFMA accumulator layout. They exchange only
-//    their partial K~+ S through LDS, once per chunk.
-//  - kLoaders loader waves stream each chunk's record plus the slice's V
-//    columns from L2/HBM with 16-byte vector loads, keeping kInFlight chunks
-//    in flight in their registers, and publish chunk j + 1 into a small LDS
-//    ring before barrier j. (Global->LDS DMA was measured to move only about
-//    16 B per clock per CU on gfx950, too slow for this stream.)
-//  - one output wave forms each chunk's output tile from the partial Q~ S
-//    products and delta the compute waves leave in LDS, and stores it, so the
-//    output product sits off the compute waves' dependent chain.
-// One barrier per chunk. Barrier B0 ends the prologue; chunk j's compute step
+//    their partial K~+ S through LDS, once per block.
+//  - kLoaders loader waves stream each block's record plus the slice's V
+//    columns from L2/HBM with 16-byte vector loads, keeping kInFlight blocks
+//    in flight in their registers, and publish block j + 1 into a small LDS
+//    ring before barrier B(j + 1). (Global->LDS DMA was measured to move only
+//    about 16 B per clock per CU on gfx950, too slow for this stream.)
+//  - one output wave forms each block's output tiles from the partial (Q~ S)^T
+//    products and delta the compute waves leave in LDS, and stores them, so
+//    the output product sits off the compute waves' dependent chain.
+// One barrier per block. Barrier B0 ends the prologue; block j's compute step
 // runs between barriers B(j+1) and B(j+2); a final barrier follows the last.
 //
-// Buffer lifetimes (kRing = 4 ring slots, 4 partial-product sets, 2 delta
-// sets):
-//  - chunk c is stored to slot c % kRing before B(c) and read by the compute
-//    waves after B(c) (as the next chunk's operands) and by the output wave
-//    after B(c + 2); it is overwritten only after B(c + kRing - 1) = B(c + 3);
-//  - the partials of chunk c (xbuf[c % 4]) are written before B(c + 1), read
-//    by the compute waves after B(c + 1) and by the output wave after B(c + 2),
-//    and overwritten after B(c + 4);
-//  - delta of chunk c (dbuf[c % 2]) is written before B(c + 2), read after it
-//    and overwritten after B(c + 3).
+// Buffer lifetimes (3 ring slots, 2 partial-product sets, 2 delta sets):
+//  - block c is stored to slot c % 3 before B(c); the compute waves read it
+//    (as the next block's operands) and the output wave reads its L between
+//    B(c) and B(c + 2); the loaders overwrite it only after B(c + 2);
+//  - the partials of block c (xbuf[c % 2]) are written before B(c + 1) and
+//    read between B(c + 1) and B(c + 2); they are overwritten after B(c + 2);
+//  - delta of block c (dbuf[c % 2]) is written before B(c + 2), read between
+//    B(c + 2) and B(c + 3), and overwritten after B(c + 3).
 constexpr int kLoaders = 4;            // loader waves per workgroup
-constexpr int kInFlight = 6;           // chunks each loader keeps in flight
-constexpr int kRing = 4;               // LDS slots
+constexpr int kInFlight = 4;           // blocks each loader keeps in flight
+constexpr int kRing = 3;               // LDS slots
 
 template <int D, typename TIn>
 struct ChainCfg {
@@ -356,29 +428,32 @@ struct ChainCfg {
   static constexpr int kBlocksPerWave = (kTilesPerWave + 1) / 2;    // 32-deep k blocks per compute wave
   static constexpr int kWaves = kHalves + kLoaders + 1;             // + the output wave
   static constexpr int kThreads = kWave * kWaves;
-  static constexpr int kVBytes = kChunk * 16 * (int)sizeof(TIn);    // V columns of the slice, one chunk
-  static constexpr int kBlocks = R::kBlocks + 1;                     // 1 KiB wave-loads per chunk (+ V)
-  static constexpr int kPerLoader = (kBlocks + kLoaders - 1) / kLoaders;
-  static constexpr int kSlot = kBlocks * 1024;
-  static_assert(kVBytes <= 1024, "one V block");
-  static_assert(kRing == 4, "buffer lifetimes");
-  static_assert(kRing * kSlot <= 96 * 1024, "LDS");
+  static constexpr int kVBytes = kBT * 16 * (int)sizeof(TIn);       // V columns of the slice, one block
+  static constexpr int kVFrags = kVBytes / 1024;
+  static constexpr int kFrags = R::kFrags + kVFrags;                 // 1 KiB wave-loads per block
+  static constexpr int kPerLoader = (kFrags + kLoaders - 1) / kLoaders;
+  static constexpr int kSlot = kFrags * 1024;
+  static constexpr int kXBytes = 2 * kHalves * 2 * 2 * kWave * 16;   // xbuf
+  static constexpr int kDBytes = 2 * 2 * kWave * 16;                 // dbuf
+  static_assert(kVBytes % 1024 == 0, "whole V fragments");
+  static_assert(kRing == 3, "buffer lifetimes");
+  static_assert(kRing * kSlot + kXBytes + kDBytes <= 160 * 1024, "LDS");
   static_assert(kInFlight * kPerLoader < 64, "vmcnt field");
 };
 
 template <int D, typename TIn>
 __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     const TIn* __restrict__ v, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ seq_chunk_off, const int32_t* __restrict__ seq_ck_off,
+    const int32_t* __restrict__ seq_blk_off, const int32_t* __restrict__ seq_ck_off,
     const char* __restrict__ records, const float* initial_state, float* final_state,
     float* __restrict__ ckpts, TIn* __restrict__ o, int N, int H, int ckpt_interval,
-    float scale, int total_chunks) {
+    float scale, int total_blocks) {
   using Cfg = ChainCfg<D, TIn>;
   using R = Rec<D>;
   constexpr int NCW = Cfg::kHalves;
   __shared__ __attribute__((aligned(1024))) char ring[kRing * Cfg::kSlot];
-  __shared__ f32x4 xbuf[4][NCW][2][kWave];     // partial K~+ S (0) and (Q~ S)^T (1) per chunk
-  __shared__ bf16x8 dbuf[2][kWave];            // delta hi | lo per chunk
+  __shared__ f32x4 xbuf[2][NCW][2][2][kWave];   // [set][wave][K~+ S, (Q~ S)^T][token tile]
+  __shared__ bf16x8 dbuf[2][2][kWave];          // [set][hi, lo]: delta of both token tiles
 
   const int NH = N * H;
   const int b = blockIdx.x;
@@ -388,36 +463,48 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   const int mm = lane % 16, gq = lane / 16;
   const int t_begin = cu[n];
   const int len = cu[n + 1] - t_begin;
-  const int nchunks = (len + kChunk - 1) / kChunk;
-  if (nchunks == 0 && wave >= NCW) return;   // only the initial -> final state copy remains
-  const char* rec0 = records + ((size_t)h * total_chunks + seq_chunk_off[n]) * R::kBytes;
+  const int nblk = (len + kBT - 1) / kBT;
+  if (nblk == 0 && wave >= NCW) return;   // only the initial -> final state copy remains
+  const char* rec0 = records + ((size_t)h * total_blocks + seq_blk_off[n]) * R::kBytes;
   auto slot_of = [&](int c) __attribute__((always_inline)) { return ring + (c % kRing) * Cfg::kSlot; };
 
   if (wave == NCW + kLoaders) {
     // ---------------- output wave ----------------
-    // O^T = (Q~ S)^T + delta^T L^T: with the operands of L delta swapped the
-    // accumulator holds token mm, columns 4gq .. 4gq + 3 in each lane.
-    auto out_tile = [&](int c) __attribute__((always_inline)) {
-      f32x4 P = xbuf[c % 4][0][1][lane];
+    // O^T = (Q~ S)^T + delta^T L^T: with delta as the A operand the
+    // accumulator holds token 16u + mm, columns 4gq .. 4gq + 3 in each lane.
+    f32x4 P[2];
+    bf16x8 Lf[2];
+    auto fetch = [&](int c) __attribute__((always_inline)) {   // between B(c + 1) and B(c + 2)
 #pragma unroll
-      for (int w = 1; w < NCW; ++w) P += xbuf[c % 4][w][1][lane];
-      const bf16x8 dd = dbuf[c % 2][lane];
-      const bf16x4 l4 = *(const bf16x4*)(slot_of(c) + R::kTL + lane * 32 + 16);
-      const f32x4 out = scale * mfma32(dd, cat(l4, l4), P);
-      const int cnt = min(kChunk, len - kChunk * c);
-      if (mm < cnt) {
-        TIn* dst = o + ((size_t)(t_begin + kChunk * c + mm) * H + h) * D + 16 * s + 4 * gq;
-        if constexpr (sizeof(TIn) == 2) *(bf16x4*)dst = to_bf16x4(out);
-        else *(f32x4*)dst = out;
+      for (int u = 0; u < 2; ++u) {
+        P[u] = xbuf[c % 2][0][1][u][lane];
+#pragma unroll
+        for (int w = 1; w < NCW; ++w) P[u] += xbuf[c % 2][w][1][u][lane];
+        Lf[u] = *(const bf16x8*)(slot_of(c) + R::kL + u * 1024 + lane * 16);
+      }
+    };
+    auto emit = [&](int c) __attribute__((always_inline)) {    // between B(c + 2) and B(c + 3)
+      const bf16x8 dh = dbuf[c % 2][0][lane], dl = dbuf[c % 2][1][lane];
+      const int cnt = min(kBT, len - kBT * c);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const f32x4 out = scale * mfma32(dl, Lf[u], mfma32(dh, Lf[u], P[u]));
+        const int tt = 16 * u + mm;
+        if (tt < cnt) {
+          TIn* dst = o + ((size_t)(t_begin + kBT * c + tt) * H + h) * D + 16 * s + 4 * gq;
+          if constexpr (sizeof(TIn) == 2) *(bf16x4*)dst = to_bf16x4(out);
+          else *(f32x4*)dst = out;
+        }
       }
     };
     lds_barrier();
-    for (int j = 0; j < nchunks; ++j) {
+    for (int j = 0; j < nblk; ++j) {
       lds_barrier();
-      if (j >= 1) out_tile(j - 1);
+      if (j >= 1) emit(j - 1);
+      fetch(j);
     }
     lds_barrier();
-    out_tile(nchunks - 1);
+    emit(nblk - 1);
     return;
   }
 
@@ -425,78 +512,79 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     // ---------------- loader waves ----------------
     const int lw = wave - NCW;
     u32x4 buf[kInFlight][Cfg::kPerLoader];
-    // Every loader issues exactly kPerLoader 16-byte loads per chunk (blocks
-    // past the end re-read a valid address and are not stored), so the loads
-    // of one chunk form one contiguous group in the vmcnt order. The V block
-    // holds the slice's 16 columns of the chunk's token rows; lane l reads
-    // bytes 16l .. 16l + 15 of the row-major [token][16] tile (clamped), and
-    // stores them transposed ([column][token]) so that a compute lane finds
-    // its four tokens of one column side by side. Rows past the end of the
-    // sequence are loaded from a valid row and written as zeros, after the
-    // loads have completed (selecting right after the load would force a
-    // wait on it).
+    // Every loader issues exactly kPerLoader 16-byte loads per block
+    // (fragments past the end re-read a valid address and are not stored), so
+    // the loads of one block form one contiguous group in the vmcnt order. The
+    // V fragments hold the slice's 16 columns of the block's token rows; lane
+    // l of V fragment f reads bytes 1024f + 16l .. +15 of the row-major
+    // [token][16] tile, and the loader stores them transposed ([column][token])
+    // so that a compute lane finds its four tokens of one column side by side.
+    // Rows past the end of the sequence are loaded from a valid row and written
+    // as zeros, after the loads have completed (selecting right after the load
+    // would force a wait on it).
     constexpr int kVRow = 16 * (int)sizeof(TIn);
     constexpr int kVec = 16 / (int)sizeof(TIn);
-    const int v_e = min(lane * 16, Cfg::kVBytes - 16);
-    const int v_tt = v_e / kVRow, v_c0 = (v_e % kVRow) / (int)sizeof(TIn);
-    auto load_chunk = [&](u32x4 (&dst)[Cfg::kPerLoader], int j) __attribute__((always_inline)) {
+    auto load_block = [&](u32x4 (&dst)[Cfg::kPerLoader], int j) __attribute__((always_inline)) {
       const char* rec = rec0 + (size_t)j * R::kBytes;
-      const int cnt = min(kChunk, len - kChunk * j);
+      const int cnt = min(kBT, len - kBT * j);
 #pragma unroll
       for (int i = 0; i < Cfg::kPerLoader; ++i) {
-        const int blk = lw + kLoaders * i;
+        const int fr = lw + kLoaders * i;
         const char* src;
-        if (blk < R::kBlocks) {
-          src = rec + blk * 1024 + lane * 16;
+        if (fr < R::kFrags) {
+          src = rec + fr * 1024 + lane * 16;
         } else {
-          const int tt = min(v_tt, cnt - 1);
-          src = (const char*)(v + ((size_t)(t_begin + kChunk * j + tt) * H + h) * D + 16 * s + v_c0);
+          const int e = min(fr - R::kFrags, Cfg::kVFrags - 1) * 1024 + lane * 16;
+          const int tt = min(e / kVRow, cnt - 1), c0 = (e % kVRow) / (int)sizeof(TIn);
+          src = (const char*)(v + ((size_t)(t_begin + kBT * j + tt) * H + h) * D + 16 * s + c0);
         }
         dst[i] = *(const u32x4*)src;
       }
     };
-    auto store_chunk = [&](const u32x4 (&src)[Cfg::kPerLoader], int j) __attribute__((always_inline)) {
+    auto store_block = [&](const u32x4 (&src)[Cfg::kPerLoader], int j) __attribute__((always_inline)) {
       char* slot = slot_of(j);
-      const int cnt = min(kChunk, len - kChunk * j);
+      const int cnt = min(kBT, len - kBT * j);
 #pragma unroll
       for (int i = 0; i < Cfg::kPerLoader; ++i) {
-        const int blk = lw + kLoaders * i;
-        if (blk < R::kBlocks) {
-          *(u32x4*)(slot + blk * 1024 + lane * 16) = src[i];
-        } else if (blk < Cfg::kBlocks && lane * 16 < Cfg::kVBytes) {
+        const int fr = lw + kLoaders * i;
+        if (fr < R::kFrags) {
+          *(u32x4*)(slot + fr * 1024 + lane * 16) = src[i];
+        } else if (fr < Cfg::kFrags) {
+          const int e = (fr - R::kFrags) * 1024 + lane * 16;
+          const int tt = e / kVRow, c0 = (e % kVRow) / (int)sizeof(TIn);
           const u32x4 zero = {0u, 0u, 0u, 0u};
-          const u32x4 x = v_tt < cnt ? src[i] : zero;
+          const u32x4 x = tt < cnt ? src[i] : zero;
+          TIn el[kVec];
+          __builtin_memcpy(el, &x, 16);
           TIn* vt = (TIn*)(slot + R::kBytes);
-          TIn e[kVec];
-          __builtin_memcpy(e, &x, 16);
 #pragma unroll
-          for (int u = 0; u < kVec; ++u) vt[(v_c0 + u) * kChunk + v_tt] = e[u];
+          for (int e2 = 0; e2 < kVec; ++e2) vt[(c0 + e2) * kBT + tt] = el[e2];
         }
       }
     };
-    // The steady-state loop is branch-free (stores past the last chunk land in
-    // a slot nobody reads any more; loads past it re-read the last chunk), so
-    // the compiler's vmcnt bookkeeping keeps all kInFlight chunks in flight.
-    const int last = nchunks - 1;
+    // The steady-state loop is branch-free (stores past the last block land in
+    // a slot nobody reads any more; loads past it re-read the last block), so
+    // the compiler's vmcnt bookkeeping keeps all kInFlight blocks in flight.
+    const int last = nblk - 1;
     static_for<0, kInFlight>([&](auto A) __attribute__((always_inline)) {
-      load_chunk(buf[A.value], min(A.value, last));
+      load_block(buf[A.value], min(A.value, last));
     });
-    store_chunk(buf[0], 0);
-    load_chunk(buf[0], min(kInFlight, last));
+    store_block(buf[0], 0);
+    load_block(buf[0], min(kInFlight, last));
     lds_barrier();
     auto step = [&](auto A, int j) __attribute__((always_inline)) {
-      // publish chunk j + 1 before barrier B(j + 1), then refill its registers
+      // publish block j + 1 before barrier B(j + 1), then refill its registers
       constexpr int set = (decltype(A)::value + 1) % kInFlight;
       const int c = j + 1;
-      store_chunk(buf[set], c);
-      load_chunk(buf[set], min(c + kInFlight, last));
+      store_block(buf[set], c);
+      load_block(buf[set], min(c + kInFlight, last));
       lds_barrier();
     };
     int j0 = 0;
-    for (; j0 + kInFlight <= nchunks; j0 += kInFlight)
+    for (; j0 + kInFlight <= nblk; j0 += kInFlight)
       static_for<0, kInFlight>([&](auto A) __attribute__((always_inline)) { step(A, j0 + A.value); });
     static_for<0, kInFlight>([&](auto A) __attribute__((always_inline)) {
-      if (j0 + A.value < nchunks) step(A, j0 + A.value);
+      if (j0 + A.value < nblk) step(A, j0 + A.value);
     });
     lds_barrier();
     return;
@@ -504,13 +592,13 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
 
   // ---------------- compute waves ----------------
   // Compute wave hf holds rows [hf * D/kHalves, (hf + 1) * D/kHalves) of the
-  // slice. Right after the state update it forms the next chunk's partial
-  // K~+ S over its rows (kept in a register and published to LDS) and partial
+  // slice. Right after the state update it forms the next block's partial
+  // K~+ S over its rows (kept in registers and published to LDS) and partial
   // (Q~ S)^T (for the output wave). After the next barrier each wave adds its
   // partner's K~+ S partial to its own; with two halves that sum is the same
   // bitwise in both waves (fp32 addition commutes), so both derive the same
-  // delta. The next chunk's operands are read from LDS right after the
-  // partner's partial, into the other of two register sets.
+  // delta. Each operand group of the next block is read from LDS right after
+  // the products of this block have consumed the registers it replaces.
   const int hf = wave;
   const int col = 16 * s + mm;
   const size_t state_base = (size_t)nh * D * D;
@@ -527,94 +615,145 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
         acc[t][i] = initial_state[state_base + (size_t)(16 * (t0 + t) + 4 * gq + i) * D + col];
   }
 
-  if (nchunks > 0) {
+  if (nblk > 0) {
     const int ck_base = ckpt_interval > 0 ? seq_ck_off[n] : 0;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    struct ChunkOps {
-      bf16x8 kp[PW], qt[PW];
-      bf16x8 kh[TW];
-      f32x4 pc[TW];
-      bf16x8 tl0;
-      f32x4 vv;
-    };
-    auto read_ops = [&](ChunkOps& f, const char* slot) __attribute__((always_inline)) {
+    bf16x8 kp[2][PW], qt[2][PW];       // next block's K~+ and Q~ fragments
+    bf16x8 th[2], tl[2];               // T hi / lo per token tile
+    f32x4 vv[2];                       // V[16u + 4gq .. +3][mm]
+    bf16x8 khh[TW], khl[TW];           // Kh hi / lo per row tile
+    f32x4 pc[TW];                      // Pc of rows 16rt + 4gq .. +3
+    auto read_kpqt = [&](const char* slot) __attribute__((always_inline)) {
 #pragma unroll
-      for (int q = 0; q < PW; ++q) {
-        const int p = hf * PW + q;        // 32-deep k block (two row tiles)
-        f.kp[q] = *(const bf16x8*)(slot + R::kKp + p * 1024 + lane * 16);
-        f.qt[q] = *(const bf16x8*)(slot + R::kQt + p * 1024 + lane * 16);
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int qq = 0; qq < PW; ++qq) {
+          const int f = u * R::NP + hf * PW + qq;
+          kp[u][qq] = *(const bf16x8*)(slot + R::kKp + f * 1024 + lane * 16);
+          qt[u][qq] = *(const bf16x8*)(slot + R::kQt + f * 1024 + lane * 16);
+        }
+    };
+    auto read_tv = [&](const char* slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        th[u] = *(const bf16x8*)(slot + R::kT + u * 2048 + lane * 32);
+        tl[u] = *(const bf16x8*)(slot + R::kT + u * 2048 + lane * 32 + 16);
+        const TIn* vt = (const TIn*)(slot + R::kBytes) + mm * kBT + 16 * u + 4 * gq;   // V^T[mm][..]
+        if constexpr (sizeof(TIn) == 2) vv[u] = from_bf16x4(*(const bf16x4*)vt);
+        else vv[u] = *(const f32x4*)vt;
       }
+    };
+    auto read_khpc = [&](const char* slot) __attribute__((always_inline)) {
 #pragma unroll
       for (int t = 0; t < TW; ++t) {
         const int rt = t0 + t;
-        f.kh[t] = *(const bf16x8*)(slot + R::kKh + rt * 1024 + lane * 16);
-        // Pc of rows 16rt + 4g .. +3 sits in the TL padding of lanes 8rt + 2g, +1
-        const char* pp = slot + R::kTL + (8 * rt + 2 * gq) * 32 + 24;
-        const f32x2 lo2 = *(const f32x2*)pp, hi2 = *(const f32x2*)(pp + 32);
-        f.pc[t] = f32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+        khh[t] = *(const bf16x8*)(slot + R::kKh + (2 * rt) * 1024 + lane * 16);
+        khl[t] = *(const bf16x8*)(slot + R::kKh + (2 * rt + 1) * 1024 + lane * 16);
+        pc[t] = *(const f32x4*)(slot + R::kPc + (16 * rt + 4 * gq) * 4);
       }
-      f.tl0 = *(const bf16x8*)(slot + R::kTL + lane * 32);
-      const TIn* vt = (const TIn*)(slot + R::kBytes) + mm * kChunk + 4 * gq;   // V^T[mm][4gq ..]
-      if constexpr (sizeof(TIn) == 2) f.vv = from_bf16x4(*(const bf16x4*)vt);
-      else f.vv = *(const f32x4*)vt;
     };
-    // partial products of a chunk over this wave's rows: K~+ S stays in u_own
+    // partial products of a block over this wave's rows: K~+ S stays in u_own
     // and goes to LDS for the partner, (Q~ S)^T goes to LDS for the output wave
-    f32x4 u_own;
-    auto partials = [&](const ChunkOps& f, int c) __attribute__((always_inline)) {
-      f32x4 U = z, P = z;
+    f32x4 u_own[2];
+    auto partials = [&](int c) __attribute__((always_inline)) {
+      f32x4 U[2] = {z, z}, P[2] = {z, z};
 #pragma unroll
-      for (int q = 0; q < PW; ++q) {
+      for (int qq = 0; qq < PW; ++qq) {
         const bf16x4 zero = {};
-        const bf16x8 Bs = cat(to_bf16x4(acc[2 * q]), 2 * q + 1 < TW ? to_bf16x4(acc[2 * q + 1]) : zero);
-        U = mfma32(f.kp[q], Bs, U);
-        P = mfma32(Bs, f.qt[q], P);
-      }
-      u_own = U;
-      if (NCW > 1) xbuf[c % 4][hf][0][lane] = U;
-      xbuf[c % 4][hf][1][lane] = P;
-    };
-    // one chunk step: cur holds chunk j's operands; nxt receives chunk j + 1's
-    auto step = [&](int j, ChunkOps& cur, ChunkOps& nxt) __attribute__((always_inline)) {
-      lds_barrier();
-      f32x4 U = u_own;
-      if (NCW > 1) U += xbuf[j % 4][hf ^ 1][0][lane];
-      // the partner's partial is read before the next chunk's operands, so
-      // the wait for it does not include theirs (LDS returns in order)
-      __builtin_amdgcn_sched_barrier(0);
-      read_ops(nxt, slot_of(j + 1));
-      bf16x4 r_hi, r_lo;
-      split_bf16(cur.vv - U, r_hi, r_lo);
-      const f32x4 dl = mfma32(cur.tl0, cat(r_hi, r_hi), z) + mfma32(cur.tl0, cat(r_lo, r_lo), z);
-      bf16x4 d_hi, d_lo;
-      split_bf16(dl, d_hi, d_lo);
-      if (hf == NCW - 1) dbuf[j % 2][lane] = cat(d_hi, d_lo);
-      const bf16x8 dh2 = cat(d_hi, d_hi), dl2 = cat(d_lo, d_lo);
+        const bf16x8 Bs = cat(to_bf16x4(acc[2 * qq]), 2 * qq + 1 < TW ? to_bf16x4(acc[2 * qq + 1]) : zero);
 #pragma unroll
-      for (int t = 0; t < TW; ++t) acc[t] = mfma32(cur.kh[t], dl2, mfma32(cur.kh[t], dh2, acc[t] * cur.pc[t]));
-      partials(nxt, j + 1);
-      if (ckpt_interval > 0) {
-        const int done = kChunk * (j + 1);
-        if (done <= len && done % ckpt_interval == 0) {
-          float* dst = ckpts + ((size_t)(ck_base + done / ckpt_interval - 1) * H + h) * D * D;
-#pragma unroll
-          for (int t = 0; t < TW; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(size_t)(16 * (t0 + t) + 4 * gq + i) * D + col] = acc[t][i];
+        for (int u = 0; u < 2; ++u) {
+          U[u] = mfma32(kp[u][qq], Bs, U[u]);
+          P[u] = mfma32(Bs, qt[u][qq], P[u]);
         }
       }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        u_own[u] = U[u];
+        if (NCW > 1) xbuf[c % 2][hf][0][u][lane] = U[u];
+        xbuf[c % 2][hf][1][u][lane] = P[u];
+      }
+    };
+    auto store_state = [&](const f32x4* st, int idx) __attribute__((always_inline)) {
+      float* dst = ckpts + ((size_t)(ck_base + idx) * H + h) * D * D;
+#pragma unroll
+      for (int t = 0; t < TW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(size_t)(16 * (t0 + t) + 4 * gq + i) * D + col] = st[t][i];
+    };
+    // one block step: the registers hold block j's T, V, Kh, Pc; block j + 1's
+    // K~+ / Q~ are read first
+    auto step = [&](int j) __attribute__((always_inline)) {
+      lds_barrier();
+      f32x4 U0 = u_own[0], U1 = u_own[1];
+      if (NCW > 1) {
+        U0 += xbuf[j % 2][hf ^ 1][0][0][lane];
+        U1 += xbuf[j % 2][hf ^ 1][0][1][lane];
+      }
+      // the partner's partials are read before the next block's operands, so
+      // the wait for them does not include theirs (LDS returns in order)
+      __builtin_amdgcn_sched_barrier(0);
+      const char* nslot = slot_of(j + 1);
+      read_kpqt(nslot);
+      bf16x4 rh0, rl0, rh1, rl1;
+      split_bf16(vv[0] - U0, rh0, rl0);
+      split_bf16(vv[1] - U1, rh1, rl1);
+      const bf16x8 rh = cat(rh0, rh1), rl = cat(rl0, rl1);
+      // delta = T_hi R_hi + T_hi R_lo + T_lo R_hi, the two token tiles'
+      // dependent chains interleaved (MFMAs issue in order)
+      f32x4 dl[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) dl[u] = mfma32(th[u], rh, z);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) dl[u] = mfma32(th[u], rl, dl[u]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) dl[u] = mfma32(tl[u], rh, dl[u]);
+      // independent work in the shadow of the delta products: the decayed
+      // state for this block's update and the next block's T and V
+      f32x4 accd[TW];
+#pragma unroll
+      for (int t = 0; t < TW; ++t) accd[t] = acc[t] * pc[t];
+      read_tv(nslot);
+      bf16x4 dh0, dlo0, dh1, dlo1;
+      split_bf16(dl[0], dh0, dlo0);
+      split_bf16(dl[1], dh1, dlo1);
+      const bf16x8 dh = cat(dh0, dh1), dlw = cat(dlo0, dlo1);
+      if (hf == NCW - 1) {
+        dbuf[j % 2][0][lane] = dh;
+        dbuf[j % 2][1][lane] = dlw;
+      }
+      const int mid = kBT * j + kChunk;   // checkpoint after the block's first 16 tokens
+      if (ckpt_interval > 0 && mid <= len && mid % ckpt_interval == 0) {
+        const bf16x4 zero = {};
+        const bf16x8 dh_m = cat(dh0, zero), dl_m = cat(dlo0, zero);
+        const char* cslot = slot_of(j);
+        f32x4 sm[TW];
+#pragma unroll
+        for (int t = 0; t < TW; ++t) {
+          const f32x4 upd = mfma32(khl[t], dh_m, mfma32(khh[t], dl_m, mfma32(khh[t], dh_m, z)));
+          const f32x4 p16 = *(const f32x4*)(cslot + R::kPc + (D + 16 * (t0 + t) + 4 * gq) * 4);
+          sm[t] = p16 * acc[t] + (p16 / pc[t]) * upd;
+        }
+        store_state(sm, mid / ckpt_interval - 1);
+      }
+#pragma unroll
+      for (int t = 0; t < TW; ++t)
+        acc[t] = mfma32(khl[t], dh, mfma32(khh[t], dlw, mfma32(khh[t], dh, accd[t])));
+      read_khpc(nslot);
+      partials(j + 1);
+      const int end = kBT * (j + 1);
+      if (ckpt_interval > 0 && end <= len && end % ckpt_interval == 0) store_state(acc, end / ckpt_interval - 1);
     };
 
-    ChunkOps opsA, opsB;
     lds_barrier();
-    read_ops(opsA, slot_of(0));
-    partials(opsA, 0);
-    int j = 0;
-    for (; j + 2 <= nchunks; j += 2) {
-      step(j, opsA, opsB);
-      step(j + 1, opsB, opsA);
+    {
+      const char* slot0 = slot_of(0);
+      read_kpqt(slot0);
+      read_tv(slot0);
+      read_khpc(slot0);
     }
-    if (j < nchunks) step(j, opsA, opsB);
+    partials(0);
+    for (int j = 0; j < nblk; ++j) step(j);
     lds_barrier();
   }
   if (final_state) {
@@ -628,31 +767,30 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
 
 template <int D, typename TIn>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
-  const PrefillLayout L = prefill_layout(a.num_seqs, a.total_chunks, a.H, D);
+  const PrefillLayout L = prefill_layout(a.num_seqs, a.total_blocks, a.H, D);
   char* ws = (char*)a.workspace;
-  int32_t* seq_chunk_off = (int32_t*)(ws + L.seq_chunk_off);
+  int32_t* seq_blk_off = (int32_t*)(ws + L.seq_blk_off);
   int32_t* seq_ck_off = (int32_t*)(ws + L.seq_ck_off);
-  int2* chunk_info = (int2*)(ws + L.chunk_info);
+  int2* blk_info = (int2*)(ws + L.blk_info);
   char* records = ws + L.records;
 
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, a.num_seqs,
-                     a.ckpt_interval, seq_chunk_off, seq_ck_off, chunk_info, (int)a.total_chunks);
+                     a.ckpt_interval, seq_blk_off, seq_ck_off, blk_info, (int)a.total_blocks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.total_chunks > 0) {
-    constexpr int threads = D >= 64 ? D : 64;
-    hipLaunchKernelGGL((prep_kernel<D, TIn>), dim3((unsigned)a.H, (unsigned)a.total_chunks),
-                       dim3(threads), 0, a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g, a.beta,
-                       (const int2*)chunk_info, a.H, a.g_min, records);
+  if (a.total_blocks > 0) {
+    hipLaunchKernelGGL((prep_kernel<D, TIn>), dim3((unsigned)a.H, (unsigned)a.total_blocks),
+                       dim3(prep_threads<D>()), 0, a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g,
+                       a.beta, (const int2*)blk_info, a.H, a.g_min, records);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   using Cfg = ChainCfg<D, TIn>;
   const unsigned blocks = (unsigned)((int64_t)a.num_seqs * a.H * (D / 16));   // one per 16-column slice
   hipLaunchKernelGGL((chain_kernel<D, TIn>), dim3(blocks), dim3(Cfg::kThreads), 0, a.stream, (const TIn*)a.v,
-                     a.cu_seqlens, seq_chunk_off, seq_ck_off, records, a.initial_state,
+                     a.cu_seqlens, seq_blk_off, seq_ck_off, records, a.initial_state,
                      a.final_state, a.checkpoints, (TIn*)a.o, a.num_seqs, a.H, a.ckpt_interval,
-                     a.scale, (int)a.total_chunks);
+                     a.scale, (int)a.total_blocks);
   return hipGetLastError();
 }
 

@@ -60,8 +60,17 @@ typedef enum {
 /* Storage type of q, k, v and o. g, beta and every state are always fp32. */
 typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
 
-/* Chunk length of the prefill ([K3-DD] 4-1 KDA, second bullet: 16-token tiles). */
+/* Chunk length of the prefill ([K3-DD] 4-1 KDA, second bullet: 16-token
+ * tiles): every product of the chunked form works on 16-token tiles, and
+ * checkpoint intervals are multiples of it. (The sequential chain advances
+ * two chunks per step; that is internal and changes no result beyond
+ * rounding.) */
 #define KDA_CHUNK 16
+
+/* Lowest decay floor (g_min) the prefill accepts: inside a 32-token block the
+ * decayed keys span a factor up to exp(-32 g_min), which must stay well inside
+ * the fp32 / bf16 range. ln 0.5 (the configurations here) is far above it. */
+#define KDA_PREFILL_MIN_G_FLOOR (-2.5f)
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* kda_status_string(kda_status status);
@@ -73,9 +82,10 @@ int64_t kda_prefill_num_checkpoints(const int32_t* cu_seqlens_host, int32_t num_
                                     int32_t ckpt_interval);
 
 /* Bytes of device workspace kda_prefill_chunked needs for these lengths and
- * shapes (0 if the arguments are invalid). The workspace holds per-chunk
- * tables and the per-chunk decayed operands of the chunked form; its contents
- * are scratch and need no initialisation. */
+ * shapes (0 if the arguments are invalid). The workspace holds per-block
+ * tables and the per-block decayed operands of the chunked form (about
+ * 1.2 KiB per token and head at D = 128); its contents are scratch and need
+ * no initialisation. */
 size_t kda_prefill_workspace_size(const int32_t* cu_seqlens_host, int32_t num_seqs,
                                   int32_t H, int32_t Dk, int32_t Dv);
 
@@ -93,7 +103,8 @@ size_t kda_prefill_workspace_size(const int32_t* cu_seqlens_host, int32_t num_se
  *                    its initial state, it has no outputs).
  *   scale       readout scale (1.0 reproduces o_t = S_t^T q_t)
  *   g_min       decay floor in log space (ln 0.5 for the configurations here;
- *               [K3-DD] 4-1 KDA, first bullet)
+ *               [K3-DD] 4-1 KDA, first bullet); must lie in
+ *               [KDA_PREFILL_MIN_G_FLOOR, 0]
  *   initial_state  [num_seqs, H, Dk, Dv] fp32, or NULL for zero states
  * Outputs:
  *   o              [T, H, Dv] dtype
@@ -110,7 +121,8 @@ size_t kda_prefill_workspace_size(const int32_t* cu_seqlens_host, int32_t num_se
  *                  256-byte aligned.
  * initial_state may alias final_state (the state is read before it is written).
  * Errors: KDA_ERR_INVALID_ARG (null required pointer, negative sizes,
- * malformed cu_seqlens_host, bad ckpt_interval), KDA_ERR_UNSUPPORTED,
+ * malformed cu_seqlens_host, bad ckpt_interval, g_min outside
+ * [KDA_PREFILL_MIN_G_FLOOR, 0]), KDA_ERR_UNSUPPORTED,
  * KDA_ERR_WORKSPACE, KDA_ERR_HIP (launch failure). */
 kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_dtype dtype,
                                const float* g, const float* beta, const int32_t* cu_seqlens,

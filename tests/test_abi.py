@@ -58,11 +58,14 @@ def test_checkpoint_counts(L):
 
 
 def test_workspace_size(L):
-    # per (chunk, head) record: 18 KiB at D = 128, 5 KiB at D = 16, plus tables
+    # per (32-token block, head) record: 39 KiB at D = 128, 13 KiB at D = 16,
+    # plus tables
     w = kda.workspace_size(cu(8192), 32, 128)
-    assert 512 * 32 * 18 * 1024 <= w < 512 * 32 * 18 * 1024 + 8192
+    assert 256 * 32 * 39 * 1024 <= w < 256 * 32 * 39 * 1024 + 8192
     w16 = kda.workspace_size(cu(64), 2, 16)
-    assert 4 * 2 * 5 * 1024 <= w16 < 4 * 2 * 5 * 1024 + 2048
+    assert 2 * 2 * 13 * 1024 <= w16 < 2 * 2 * 13 * 1024 + 2048
+    # a ragged tail still takes a whole block
+    assert kda.workspace_size(cu(33, 1), 1, 128) >= 3 * 39 * 1024
     assert kda.workspace_size(cu(10), 2, 64) == 0          # unsupported D
     assert kda.workspace_size([0, 5, 2], 2, 128) == 0       # malformed offsets
 
@@ -98,6 +101,9 @@ def test_prefill_argument_errors(L):
     assert _prefill_status(L, ws=None, ws_bytes=1 << 30) == E.KDA_ERR_WORKSPACE
     assert _prefill_status(L, ws=ctypes.c_void_p(0x1010), ws_bytes=1 << 30) == E.KDA_ERR_WORKSPACE
     assert _prefill_status(L, v=ctypes.c_void_p(0x1002)) == E.KDA_ERR_INVALID_ARG   # misaligned
+    assert _prefill_status(L, g_min=-3.0) == E.KDA_ERR_INVALID_ARG     # decay floor below the supported range
+    assert _prefill_status(L, g_min=0.5) == E.KDA_ERR_INVALID_ARG
+    assert _prefill_status(L, g_min=float("nan")) == E.KDA_ERR_INVALID_ARG
     empty = (ctypes.c_int32 * 1)(0)
     assert _prefill_status(L, N=0, cu_host=ctypes.cast(empty, ctypes.POINTER(ctypes.c_int32))) == E.KDA_OK
 

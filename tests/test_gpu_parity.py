@@ -90,6 +90,23 @@ def test_prefill_ragged_varlen_with_checkpoints(D, bf16):
     check_states(ck, ck_ref, "checkpoint")
 
 
+@pytest.mark.parametrize("ckpt", [16, 48])
+def test_prefill_checkpoints_inside_a_block(ckpt):
+    """Checkpoint intervals that are odd multiples of 16 put every other
+    checkpoint after the first half of a 32-token block (and on a tail block
+    whose valid part ends there)."""
+    lengths = [37, 16, 100, 48, 95, 0, 160]
+    H, D = 2, 128
+    print(f"case: checkpoints every {ckpt} lengths={lengths}", flush=True)
+    inp = make_inputs(sum(lengths), H, D, seed=23 + ckpt, lengths=lengths, initial_state=True)
+    o, fin, ck = run_prefill(inp, H, D, ckpt=ckpt)
+    o_ref, f_ref, ck_ref = oracle(inp, ckpt=ckpt)
+    check_outputs(o, o_ref, inp.cu_seqlens, H)
+    check_states(fin, f_ref, "final")
+    assert ck.shape == ck_ref.shape == (sum(L // ckpt for L in lengths), H, D, D)
+    check_states(ck, ck_ref, "checkpoint")
+
+
 def test_prefill_zero_initial_state_and_scale():
     lengths = [80, 33]
     H, D = 2, 128
