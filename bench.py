@@ -25,8 +25,12 @@ import torch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from gated_delta_rule_109_amd import kda  # noqa: E402
+from gated_delta_rule_109_amd import kda, profiling  # noqa: E402
 from gated_delta_rule_109_amd.workloads import make_inputs, make_inputs_device  # noqa: E402
+
+# rocprofv3 byte-counter summary of the prefill (HBM bytes per call); used for
+# roofline.traffic only while it matches the current kernel sources.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "kda_prefill_b1_h32_t8192_hbm_traffic.md")
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
@@ -89,6 +93,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0 = auto)")
+    ap.add_argument("--calibrate", type=int, default=0, metavar="MIB",
+                    help="before timing, run torch.abs over a float32 tensor of MIB MiB (a kernel of known "
+                         "size for calibrating rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -97,6 +104,13 @@ def main():
         sys.exit(2)
 
     dev = torch.device("cuda:0")
+    if args.calibrate > 0:
+        a = torch.ones(args.calibrate * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.abs(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
     T, H, D = 8192, 32, 128
     q, k, v, g, beta, cu, _ = make_inputs_device(T, H, D, seed=2, device=dev)
     plan = kda.make_plan(cu, H, D, dev)
@@ -130,6 +144,7 @@ def main():
     d_gbps = d_bytes / (d_ms * 1e-3) / 1e9
 
     ach_gbps = nbytes / (ev_ms * 1e-3) / 1e9
+    tr = profiling.read_record(TRAFFIC_PROFILE)
     rec = {
         "metric": "KDA prefill tokens/s (B=1, H=32, T=8192, D=128)",
         "value": round(tokens_per_s, 1),
@@ -144,10 +159,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded, device-generated; q,k L2-normalised, g floored at ln 0.5)",
         "config": {"workload": "single-sequence KDA prefill", "batch": 1, "heads": H, "seq_len": T,
-                   "head_dim": D, "chunk": C, "initial_state": False},
+                   "head_dim": D, "chunk": C, "chain_step_tokens": 2 * C, "initial_state": False},
         "roofline": {"kernel": "kda_prefill_chunked (plan + prep + chain kernels, one C-ABI call)",
                      "bound": "hbm", "achieved": round(ach_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(ach_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(ach_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": tr["bytes_per_call"] if tr else None,
                      "algorithmic_bytes_per_launch": nbytes, "launch_ms": round(ev_ms, 4)},
         "prefill_tflops": round(flops / (ev_ms * 1e-3) / 1e12, 2),
         "prefill_mfma_frac_of_peak": round(flops / (ev_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),

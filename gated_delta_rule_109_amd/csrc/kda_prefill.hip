@@ -597,7 +597,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   // (Q~ S)^T (for the output wave). After the next barrier each wave adds its
   // partner's K~+ S partial to its own; with two halves that sum is the same
   // bitwise in both waves (fp32 addition commutes), so both derive the same
-  // delta. Each operand group of the next block is read from LDS right after
+  // delta (with more waves every wave sums all partials in wave order). Each operand group of the next block is read from LDS right after
   // the products of this block have consumed the registers it replaces.
   const int hf = wave;
   const int col = 16 * s + mm;
@@ -686,9 +686,17 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     auto step = [&](int j) __attribute__((always_inline)) {
       lds_barrier();
       f32x4 U0 = u_own[0], U1 = u_own[1];
-      if (NCW > 1) {
+      if constexpr (NCW == 2) {
         U0 += xbuf[j % 2][hf ^ 1][0][0][lane];
         U1 += xbuf[j % 2][hf ^ 1][0][1][lane];
+      } else if constexpr (NCW > 2) {   // every wave sums all partials in the same order
+        U0 = xbuf[j % 2][0][0][0][lane];
+        U1 = xbuf[j % 2][0][0][1][lane];
+#pragma unroll
+        for (int w = 1; w < NCW; ++w) {
+          U0 += xbuf[j % 2][w][0][0][lane];
+          U1 += xbuf[j % 2][w][0][1][lane];
+        }
       }
       // the partner's partials are read before the next block's operands, so
       // the wait for them does not include theirs (LDS returns in order)

@@ -1,0 +1,144 @@
+"""HBM traffic of the prefill from rocprofv3 byte counters.
+
+rocprofv3 reports FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from the L2
+channels. Their scale is calibrated against a plain elementwise kernel of
+known size run in the same process: ``bench.py --calibrate MIB`` runs
+``torch.abs`` (an op nothing else in the run uses) over a float32 tensor of
+MIB MiB, which reads and writes exactly MIB MiB, so each counter is scaled by
+the true size over what it reads for that kernel.
+
+Usage (two counter passes of the same command, then the summary):
+
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dirF> -o kda -- python3 bench.py ... --calibrate 256
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dirW> -o kda -- python3 bench.py ... --calibrate 256
+  python3 -m gated_delta_rule_109_amd.profiling --fetch <dirF> --write <dirW> --calib-mib 256 \
+      --out profiles/<name>.md --command "<the rocprofv3 command>"
+
+The summary ends with one ``traffic-record:`` JSON line that bench.py reads:
+the per-call HBM bytes of kda_prefill_chunked and a digest of the kernel
+sources it was measured on (a changed source makes bench.py report null).
+"""
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+PREFILL_KERNELS = ("plan_kernel", "prep_kernel", "chain_kernel")
+CALIB_KERNEL = "AbsFunctor"
+
+
+def source_digest():
+    """sha256 over the HIP sources and headers the library is built from."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")) + glob.glob(os.path.join(PKG, "csrc", "*.h")))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_csv(d):
+    hits = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not hits:
+        raise FileNotFoundError(f"no counter_collection.csv under {d}")
+    return hits[0]
+
+
+def per_kernel(d, counter):
+    """{short kernel name: (dispatches, mean KiB per dispatch)} for one counter."""
+    acc = {}
+    for r in csv.DictReader(open(_counter_csv(d))):
+        if r["Counter_Name"] != counter:
+            continue
+        name = r["Kernel_Name"]
+        m = re.search(r"kda::(\w+)", name)
+        if m:
+            key = m.group(1)
+        elif CALIB_KERNEL in name:
+            key = CALIB_KERNEL
+        else:
+            continue
+        n, s = acc.get(key, (0, 0.0))
+        acc[key] = (n + 1, s + float(r["Counter_Value"]))
+    return {k: (n, s / n) for k, (n, s) in acc.items()}
+
+
+def summarize(fetch_dir, write_dir, calib_mib):
+    f = per_kernel(fetch_dir, "FETCH_SIZE")
+    w = per_kernel(write_dir, "WRITE_SIZE")
+    calib_kib = calib_mib * 1024.0
+    if CALIB_KERNEL not in f or CALIB_KERNEL not in w:
+        raise RuntimeError("calibration kernel missing from the counter runs (run bench.py with --calibrate)")
+    ff = calib_kib / f[CALIB_KERNEL][1]     # true bytes per counted byte
+    fw = calib_kib / w[CALIB_KERNEL][1]
+    rows = []
+    total = 0.0
+    for k in PREFILL_KERNELS:
+        if k not in f or k not in w:
+            raise RuntimeError(f"{k} missing from the counter runs")
+        fb = f[k][1] * ff * 1024
+        wb = w[k][1] * fw * 1024
+        total += fb + wb
+        rows.append((k, f[k][0], f[k][1], w[k][1], fb, wb))
+    return {"fetch_factor": ff, "write_factor": fw, "rows": rows, "bytes_per_call": total,
+            "calib": (f[CALIB_KERNEL][1], w[CALIB_KERNEL][1])}
+
+
+def render(res, calib_mib, command, algorithmic_bytes):
+    out = ["# KDA prefill HBM traffic (B=1, H=32, T=8192, D=128, bf16 q/k/v)", "",
+           "Commands (run from the repository root on one MI355X; one counter per pass):", "", "```"]
+    out += [c for c in command]
+    out += ["```", "",
+            f"Calibration: `torch.abs` over a {calib_mib} MiB float32 tensor reads and writes exactly "
+            f"{calib_mib} MiB; the counters read {res['calib'][0]:.4g} KiB (FETCH_SIZE) and "
+            f"{res['calib'][1]:.4g} KiB (WRITE_SIZE), so FETCH_SIZE is scaled by {res['fetch_factor']:.3f} "
+            f"and WRITE_SIZE by {res['write_factor']:.3f}.", "",
+            "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB (scaled) |",
+            "|---|---|---|---|---|---|"]
+    for k, n, fk, wk, fb, wb in res["rows"]:
+        out.append(f"| `kda::{k}` | {n} | {fk:.4g} | {wk:.4g} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
+    tot = res["bytes_per_call"]
+    out += ["", f"HBM bytes per `kda_prefill_chunked` call: {tot / 1e6:.1f} MB, against "
+            f"{algorithmic_bytes / 1e6:.1f} MB algorithmic (ratio {tot / algorithmic_bytes:.2f}).", "",
+            "traffic-record: " + json.dumps({"bytes_per_call": round(tot), "source_digest": source_digest(),
+                                              "fetch_factor": round(res["fetch_factor"], 4),
+                                              "write_factor": round(res["write_factor"], 4)})]
+    return "\n".join(out) + "\n"
+
+
+def read_record(path):
+    """The traffic-record of a summary if it matches the current sources, else None."""
+    try:
+        for line in open(path):
+            if line.startswith("traffic-record: "):
+                rec = json.loads(line[len("traffic-record: "):])
+                return rec if rec.get("source_digest") == source_digest() else None
+    except OSError:
+        return None
+    return None
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--calib-mib", type=int, required=True)
+    ap.add_argument("--algorithmic-bytes", type=int, required=True)
+    ap.add_argument("--command", action="append", default=[])
+    ap.add_argument("--out")
+    a = ap.parse_args(argv)
+    text = render(summarize(a.fetch, a.write, a.calib_mib), a.calib_mib, a.command, a.algorithmic_bytes)
+    if a.out:
+        with open(a.out, "w") as fh:
+            fh.write(text)
+    sys.stdout.write(text)
+
+
+if __name__ == "__main__":
+    main()
