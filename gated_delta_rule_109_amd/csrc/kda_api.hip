@@ -130,6 +130,30 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
   kda::DecodeArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
   a.N = N; a.H = H; a.D = Dk;
+  a.T = 1; a.accept = nullptr;
+  a.scale = scale; a.g_min = g_min;
+  a.bf16 = dtype == KDA_BF16;
+  a.stream = stream;
+  return from_hip(kda::launch_decode(a));
+}
+
+kda_status kda_decode_tokens(const void* q, const void* k, const void* v, kda_dtype dtype,
+                             const float* g, const float* beta, float* state,
+                             const int32_t* accept, void* o, int32_t N, int32_t T, int32_t H,
+                             int32_t Dk, int32_t Dv, float scale, float g_min,
+                             hipStream_t stream) {
+  if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
+  if (!supported_dims(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
+  if (T < 1 || T > KDA_DECODE_MAX_TOKENS) return KDA_ERR_INVALID_ARG;
+  if (N < 0 || H <= 0 || (int64_t)N * H > INT32_MAX || (int64_t)N * T * H > INT32_MAX)
+    return KDA_ERR_INVALID_ARG;
+  if (N == 0) return KDA_OK;
+  if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
+  if (!aligned16({q, k, v, g, beta, state, o})) return KDA_ERR_INVALID_ARG;
+  kda::DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
+  a.N = N; a.H = H; a.D = Dk;
+  a.T = T; a.accept = accept;
   a.scale = scale; a.g_min = g_min;
   a.bf16 = dtype == KDA_BF16;
   a.stream = stream;

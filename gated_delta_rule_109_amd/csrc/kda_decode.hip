@@ -11,7 +11,8 @@
 //   S' = Diag(a) S,  u = S'^T k,  d = beta (v - u),  S = S' + k d^T,
 //   o  = scale S^T q = scale (S'^T q + (k.q) d).
 // The last identity lets u, S'^T q and k.q come from the same single pass
-// over S, so S is read once, kept in registers, updated and written once.
+// over S, so S is read once, kept in registers, updated and written once
+// (once per call when several tokens are processed).
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -21,16 +22,31 @@ namespace kda {
 // columns [32w, 32w + 32); lane l owns the 4 columns 32w + 4(l % 8) .. +3 and
 // the 16 rows (l / 8) + 8i, i = 0..15. One float4 load instruction of the wave
 // covers 8 rows x 128 contiguous bytes. The reduction over rows is three
-// cross-lane xor steps (lane bits 3..5), no LDS and no barrier after the gate
-// vectors are staged.
+// cross-lane xor steps (lane bits 3..5): a wave holds whole columns, so the
+// token loop needs no LDS traffic and no barrier after the token vectors are
+// staged.
 //
 // D = 16: one wave per head, lane l owns columns 4(l % 4) .. +3 and row l / 4;
 // reduction over lane bits 2..5.
-template <int D, typename TIn>
+//
+// Several tokens per call (T <= kMaxTokens, e.g. the draft tokens of a
+// speculative step; [K3-SA] Experiments, serving bullets: the day-0 serving
+// recipes use DSpark speculative decoding): the state stays in registers
+// across them and each token's output is written as it is formed. The state
+// written back is the one after `commit` tokens (commit = T unless the caller
+// passes a per-sequence count): commit = 0 leaves the state untouched, so a
+// verify pass can run without committing and a second call commits the
+// accepted prefix.
+//
+// kOne fixes T = 1 at compile time (the plain decode step): the token loop then
+// vanishes and the kernel keeps the register footprint of a single step.
+template <int D, typename TIn, bool kOne>
 __global__ __launch_bounds__(D == 128 ? 256 : 64) void decode_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
-    TIn* __restrict__ o, float scale, float g_min) {
+    TIn* __restrict__ o, int H, int T_arg, const int32_t* __restrict__ accept, float scale,
+    float g_min) {
+  const int T = kOne ? 1 : T_arg;
   constexpr int kThreads = D == 128 ? 256 : 64;
   constexpr int kColGroups = D == 128 ? 8 : 4;         // float4 column groups per wave
   constexpr int kRowGroups = kWave / kColGroups;        // lanes sharing a column group
@@ -38,61 +54,99 @@ __global__ __launch_bounds__(D == 128 ? 256 : 64) void decode_kernel(
   constexpr int kColsPerWave = 4 * kColGroups;
   static_assert(kThreads / kWave * kColsPerWave == D, "layout covers D columns");
 
-  const size_t head = blockIdx.x;
+  const uint32_t head = blockIdx.x;                     // n * H + h
+  const uint32_t n = kOne ? 0 : head / (uint32_t)H, h = kOne ? head : head % (uint32_t)H;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int cg = lane % kColGroups, rg = lane / kColGroups;
   const int col = wave * kColsPerWave + 4 * cg;
+  // row of token t of this (sequence, head) in the [N, T, H, .] inputs
+  auto row = [&](int t) __attribute__((always_inline)) {
+    return kOne ? (size_t)head : ((size_t)n * T + t) * H + h;
+  };
+  const int commit = kOne ? 1 : accept ? min(max(accept[n], 0), T) : T;
 
-  __shared__ float s_k[D], s_q[D], s_a[D];
-  if (tid < D) {
-    s_k[tid] = Elem<TIn>::load(k + head * D + tid);
-    s_q[tid] = Elem<TIn>::load(q + head * D + tid);
-    s_a[tid] = gate_alpha(g[head * D + tid], g_min);
+  // Token vectors in LDS, sized by the launch for T tokens:
+  // k, q, alpha, v as [T][D] fp32 each, then beta [T].
+  extern __shared__ float smem[];
+  float(*s_k)[D] = (float(*)[D])smem;
+  float(*s_q)[D] = s_k + T;
+  float(*s_a)[D] = s_q + T;
+  float(*s_v)[D] = s_a + T;
+  float* s_b = &s_v[T][0];
+  // Loads first (token vectors, then the state), stores to LDS after: the
+  // state loads are in flight while the token values arrive and are staged.
+  // Token element e = t * D + c is handled by thread e % kThreads; indices are
+  // clamped so every load is in bounds, and only e < T * D is stored.
+  constexpr int kIters = kOne ? 1 : (kMaxTokens * D + kThreads - 1) / kThreads;
+  float tk[kIters], tq[kIters], tv[kIters], tg[kIters];
+#pragma unroll
+  for (int j = 0; j < kIters; ++j) {
+    const int e = min(tid + j * kThreads, T * D - 1);
+    const size_t off = row(e / D) * D + e % D;
+    tk[j] = Elem<TIn>::load(k + off);
+    tq[j] = Elem<TIn>::load(q + off);
+    tv[j] = Elem<TIn>::load(v + off);
+    tg[j] = g[off];
   }
-  // Issue the state loads before the barrier so they overlap it.
-  float* S = state + head * (size_t)D * D;
+  const float tb = beta[row(min(tid, T - 1))];
+  // State: plain float4 loads (measured faster here than non-temporal loads),
+  // non-temporal stores at the end (faster than plain stores).
+  float* S = state + (size_t)head * D * D;
   f32x4 s[kRowsPerLane];
 #pragma unroll
   for (int i = 0; i < kRowsPerLane; ++i)
-    s[i] = __builtin_nontemporal_load((const f32x4*)(S + (size_t)(rg + kRowGroups * i) * D + col));
-  __syncthreads();
-
-  f32x4 u = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
-  float kq = 0.f;
+    s[i] = *(const f32x4*)(S + (size_t)(rg + kRowGroups * i) * D + col);
 #pragma unroll
-  for (int i = 0; i < kRowsPerLane; ++i) {
-    const int r = rg + kRowGroups * i;
-    const float a = s_a[r], kr = s_k[r], qr = s_q[r];
-    s[i] *= a;
-    u += s[i] * kr;
-    w += s[i] * qr;
-    kq += kr * qr;
-  }
-#pragma unroll
-  for (int m = kColGroups; m < kWave; m <<= 1) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u[c] += __shfl_xor(u[c], m);
-      w[c] += __shfl_xor(w[c], m);
+  for (int j = 0; j < kIters; ++j) {
+    const int e = tid + j * kThreads;
+    if (e < T * D) {
+      const int t = e / D, c = e % D;
+      s_k[t][c] = tk[j];
+      s_q[t][c] = tq[j];
+      s_v[t][c] = tv[j];
+      s_a[t][c] = gate_alpha(tg[j], g_min);
     }
-    kq += __shfl_xor(kq, m);
   }
-  const float b = beta[head];
-  f32x4 vv;
+  if (tid < T) s_b[tid] = tb;
+  // LDS-only barrier: the state loads stay in flight across it.
+  lds_barrier();
+
+  for (int t = 0; t < T; ++t) {
+    f32x4 u = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
+    float kq = 0.f;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) vv[c] = Elem<TIn>::load(v + head * D + col + c);
-  const f32x4 d = b * (vv - u);
+    for (int i = 0; i < kRowsPerLane; ++i) {
+      const int r = rg + kRowGroups * i;
+      const float a = s_a[t][r], kr = s_k[t][r], qr = s_q[t][r];
+      s[i] *= a;
+      u += s[i] * kr;
+      w += s[i] * qr;
+      kq += kr * qr;
+    }
 #pragma unroll
-  for (int i = 0; i < kRowsPerLane; ++i) {
-    const int r = rg + kRowGroups * i;
-    s[i] += s_k[r] * d;
-    __builtin_nontemporal_store(s[i], (f32x4*)(S + (size_t)r * D + col));
-  }
-  if (rg == 0) {
-    const f32x4 out = scale * (w + kq * d);
+    for (int m = kColGroups; m < kWave; m <<= 1) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) Elem<TIn>::store(o + head * D + col + c, out[c]);
+      for (int c = 0; c < 4; ++c) {
+        u[c] += __shfl_xor(u[c], m);
+        w[c] += __shfl_xor(w[c], m);
+      }
+      kq += __shfl_xor(kq, m);
+    }
+    const f32x4 vv = *(const f32x4*)&s_v[t][col];
+    const f32x4 d = s_b[t] * (vv - u);
+#pragma unroll
+    for (int i = 0; i < kRowsPerLane; ++i) s[i] += s_k[t][rg + kRowGroups * i] * d;
+    if (t + 1 == commit) {
+#pragma unroll
+      for (int i = 0; i < kRowsPerLane; ++i)
+        __builtin_nontemporal_store(s[i], (f32x4*)(S + (size_t)(rg + kRowGroups * i) * D + col));
+    }
+    if (rg == 0) {
+      const f32x4 out = scale * (w + kq * d);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) Elem<TIn>::store(o + row(t) * D + col + c, out[c]);
+    }
   }
 }
 
@@ -100,9 +154,15 @@ template <int D, typename TIn>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
   const int threads = D == 128 ? 256 : 64;
   const unsigned blocks = (unsigned)((int64_t)a.N * a.H);
-  hipLaunchKernelGGL((decode_kernel<D, TIn>), dim3(blocks), dim3(threads), 0, a.stream,
-                     (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta, a.state,
-                     (TIn*)a.o, a.scale, a.g_min);
+  const size_t lds = sizeof(float) * ((size_t)4 * a.T * D + a.T);
+  if (a.T == 1 && !a.accept)
+    hipLaunchKernelGGL((decode_kernel<D, TIn, true>), dim3(blocks), dim3(threads), lds, a.stream,
+                       (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta, a.state,
+                       (TIn*)a.o, a.H, 1, nullptr, a.scale, a.g_min);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, TIn, false>), dim3(blocks), dim3(threads), lds, a.stream,
+                       (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta, a.state,
+                       (TIn*)a.o, a.H, a.T, a.accept, a.scale, a.g_min);
   return hipGetLastError();
 }
 

@@ -6,10 +6,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kda.h"
+
 namespace kda {
 
 // Tokens per prefill block: the chain takes one step per two 16-token chunks.
 constexpr int kBlockTokens = 32;
+// Most tokens one decode call processes per sequence.
+constexpr int kMaxTokens = KDA_DECODE_MAX_TOKENS;
 
 struct DecodeArgs {
   const void *q, *k, *v;
@@ -17,6 +21,8 @@ struct DecodeArgs {
   float* state;
   void* o;
   int32_t N, H, D;
+  int32_t T;                  // tokens per sequence (1 for a plain decode step)
+  const int32_t* accept;      // device [N] tokens to commit, or NULL (= T)
   float scale, g_min;
   bool bf16;
   hipStream_t stream;

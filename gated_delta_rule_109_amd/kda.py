@@ -23,7 +23,8 @@ CHUNK = 16
 LN_HALF = math.log(0.5)
 
 EXPORTED = ("kda_status_string", "kda_prefill_num_checkpoints", "kda_prefill_workspace_size",
-            "kda_prefill_chunked", "kda_decode_step")
+            "kda_prefill_chunked", "kda_decode_step", "kda_decode_tokens")
+DECODE_MAX_TOKENS = 16
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -57,6 +58,9 @@ def lib():
         L.kda_decode_step.restype = ctypes.c_int
         L.kda_decode_step.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _i32, _i32,
                                       _i32, _i32, ctypes.c_float, ctypes.c_float, _vp]
+        L.kda_decode_tokens.restype = ctypes.c_int
+        L.kda_decode_tokens.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _i32,
+                                        _i32, _i32, _i32, _i32, ctypes.c_float, ctypes.c_float, _vp]
         _lib = L
     return _lib
 
@@ -160,4 +164,22 @@ def decode_step(q, k, v, g, beta, state, scale=1.0, g_min=LN_HALF, o=None):
                                float(g_min), _stream(q.device))
     if st != KDA_OK:
         raise KdaError(st, "kda_decode_step")
+    return o
+
+
+def decode_tokens(q, k, v, g, beta, state, accept=None, scale=1.0, g_min=LN_HALF, o=None):
+    """kda_decode_tokens: q,k,g,v [N,T,H,D]; beta [N,T,H]; state [N,H,D,D]
+    updated in place to the state after accept[n] tokens (all T when accept is
+    None); accept is a device int32 [N] tensor. Returns o [N,T,H,D]."""
+    N, T, H, D = q.shape
+    _check_dev(q, k, v, g, beta, state, accept)
+    if accept is not None and accept.dtype != torch.int32:
+        raise TypeError("accept must be int32")
+    if o is None:
+        o = torch.empty_like(v)
+    st = lib().kda_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta),
+                                 _ptr(state), _ptr(accept), _ptr(o), N, T, H, D, v.shape[3],
+                                 float(scale), float(g_min), _stream(q.device))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_decode_tokens")
     return o

@@ -7,6 +7,9 @@ known size run in the same process: ``bench.py --calibrate MIB`` runs
 MIB MiB, which reads and writes exactly MIB MiB, so each counter is scaled by
 the true size over what it reads for that kernel.
 
+It also renders the per-kernel time table of a ``rocprofv3 --kernel-trace
+--stats`` run (``--stats DIR``).
+
 Usage (two counter passes of the same command, then the summary):
 
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dirF> -o kda -- python3 bench.py ... --calibrate 256
@@ -124,16 +127,54 @@ def read_record(path):
     return None
 
 
+def kernel_stats(d):
+    """[(name, calls, avg us, min us, max us, share %)] of the kda kernels in a
+    rocprofv3 --kernel-trace --stats output directory."""
+    hits = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not hits:
+        raise FileNotFoundError(f"no kernel_stats.csv under {d}")
+    rows = []
+    for r in csv.DictReader(open(hits[0])):
+        if "kda::" not in r["Name"]:
+            continue
+        name = re.sub(r"\(.*", "", r["Name"]).replace("void ", "")
+        rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                     float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return rows
+
+
+def render_stats(rows, title, command, bench_line):
+    out = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```"]
+    out += list(command)
+    out += ["```", "", "rocprofv3 kernel statistics of the kda kernels (durations in microseconds; share is "
+            "of all GPU kernel time in the run, input generation included):", "",
+            "| kernel | calls | average | min | max | share |", "|---|---|---|---|---|---|"]
+    for name, n, avg, mn, mx, pct in rows:
+        out.append(f"| `{name}` | {n} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.1f} % |")
+    if bench_line:
+        out += ["", "bench.py line of the same build (no profiler):", "", "```", bench_line.strip(), "```"]
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
-    ap.add_argument("--calib-mib", type=int, required=True)
-    ap.add_argument("--algorithmic-bytes", type=int, required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--calib-mib", type=int)
+    ap.add_argument("--algorithmic-bytes", type=int)
+    ap.add_argument("--stats", help="rocprofv3 --kernel-trace --stats output directory (kernel-time summary)")
+    ap.add_argument("--title", default="KDA kernels")
+    ap.add_argument("--bench-line", help="file whose last line is the bench.py JSON line")
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--out")
     a = ap.parse_args(argv)
-    text = render(summarize(a.fetch, a.write, a.calib_mib), a.calib_mib, a.command, a.algorithmic_bytes)
+    if a.stats:
+        line = open(a.bench_line).read().strip().splitlines()[-1] if a.bench_line else None
+        text = render_stats(kernel_stats(a.stats), a.title, a.command, line)
+    else:
+        if not (a.fetch and a.write and a.calib_mib and a.algorithmic_bytes):
+            ap.error("--fetch, --write, --calib-mib and --algorithmic-bytes are required")
+        text = render(summarize(a.fetch, a.write, a.calib_mib), a.calib_mib, a.command, a.algorithmic_bytes)
     if a.out:
         with open(a.out, "w") as fh:
             fh.write(text)

@@ -145,6 +145,37 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
                            int32_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
                            float g_min, hipStream_t stream);
 
+/* Most tokens per sequence that kda_decode_tokens takes in one call. */
+#define KDA_DECODE_MAX_TOKENS 16
+
+/* T consecutive recurrent steps per sequence in one call (1 <= T <=
+ * KDA_DECODE_MAX_TOKENS): the draft tokens of a speculative-decoding step
+ * ([K3-SA] Experiments, serving bullets: the day-0 serving recipes use DSpark
+ * speculative decoding), or several decode tokens at once. Each step is the
+ * recurrence of kda_decode_step; the fp32 state is read once and written at
+ * most once per call, so the state traffic stays 8 D^2 bytes per head however
+ * many tokens the call holds.
+ *   q, k   [N, T, H, Dk] dtype (token t of sequence n is row n*T + t)
+ *   v      [N, T, H, Dv] dtype
+ *   g      [N, T, H, Dk] fp32 log-decay (clamped to [g_min, 0])
+ *   beta   [N, T, H] fp32
+ *   state  [N, H, Dk, Dv] fp32, read, and updated IN PLACE to the state after
+ *          the first accept[n] tokens of sequence n
+ *   accept device int32 [N] or NULL (NULL commits all T tokens). Values are
+ *          clamped to [0, T]; 0 leaves that sequence's state unchanged. A
+ *          verify pass therefore runs with accept = 0, and once the accepted
+ *          prefix length a_n is known a second call with accept = a_n on the
+ *          same inputs commits exactly that prefix.
+ *   o      [N, T, H, Dv] dtype, output of every token whatever accept holds
+ * Errors: KDA_ERR_INVALID_ARG (null required pointer, T outside
+ * [1, KDA_DECODE_MAX_TOKENS], negative N, H <= 0), KDA_ERR_UNSUPPORTED,
+ * KDA_ERR_HIP. */
+kda_status kda_decode_tokens(const void* q, const void* k, const void* v, kda_dtype dtype,
+                             const float* g, const float* beta, float* state,
+                             const int32_t* accept, void* o, int32_t N, int32_t T, int32_t H,
+                             int32_t Dk, int32_t Dv, float scale, float g_min,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -120,3 +120,26 @@ def test_decode_argument_errors(L):
     assert call(state=None) == kda.KDA_ERR_INVALID_ARG
     assert call(state=ctypes.c_void_p(0x1004)) == kda.KDA_ERR_INVALID_ARG
     assert call(N=0) == kda.KDA_OK                                    # nothing to do
+
+
+def test_decode_tokens_argument_errors(L):
+    fake = ctypes.c_void_p(0x1000)
+    call = lambda **o: L.kda_decode_tokens(*dict(dict(q=fake, k=fake, v=fake, dtype=0, g=fake,
+                                                      beta=fake, state=fake, accept=None, o=fake,
+                                                      N=4, T=3, H=2, Dk=128, Dv=128, scale=1.0,
+                                                      g_min=-0.69, stream=None), **o).values())
+    assert call(Dk=16, Dv=128) == kda.KDA_ERR_UNSUPPORTED
+    assert call(dtype=2) == kda.KDA_ERR_UNSUPPORTED
+    assert call(T=0) == kda.KDA_ERR_INVALID_ARG
+    assert call(T=kda.DECODE_MAX_TOKENS + 1) == kda.KDA_ERR_INVALID_ARG
+    assert call(N=-2) == kda.KDA_ERR_INVALID_ARG
+    assert call(H=-1) == kda.KDA_ERR_INVALID_ARG
+    assert call(N=1 << 20, T=16, H=256) == kda.KDA_ERR_INVALID_ARG   # N*T*H overflows int32
+    assert call(o=None) == kda.KDA_ERR_INVALID_ARG
+    assert call(beta=ctypes.c_void_p(0x1002)) == kda.KDA_ERR_INVALID_ARG
+    assert call(N=0) == kda.KDA_OK
+
+
+def test_decode_max_tokens_matches_header():
+    m = re.search(r"#define\s+KDA_DECODE_MAX_TOKENS\s+(\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == kda.DECODE_MAX_TOKENS

@@ -269,3 +269,126 @@ def test_decode_equals_one_token_prefill():
     torch.cuda.synchronize()
     assert rel_err(o_dec.float().cpu().numpy(), o_pre) <= 1e-2
     assert rel_err(state.cpu().numpy(), fin) <= 1e-3
+
+
+# ------------------------------------------------------- multi-token decode
+def _tokens_case(N, T, H, D, seed, bf16=True):
+    """N sequences of T new tokens each, as [N, T, H, .] host arrays, plus the
+    oracle's per-token outputs and the state after each prefix length
+    (states[t] = state after t tokens; states[0] = the initial state), from T
+    single-token oracle steps."""
+    d = make_inputs(N * T, H, D, seed=seed, lengths=[T] * N, initial_state=True, bf16=bf16)
+    shp = lambda a: np.ascontiguousarray(a.reshape(N, T, *a.shape[1:]))
+    q, k, v, g, beta = map(shp, (d.q, d.k, d.v, d.g, d.beta))
+    states = [d.initial_state.astype(np.float64)]
+    o_ref = np.zeros((N, T, H, D))
+    for t in range(T):
+        o_ref[:, t], s = reference.decode(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], states[-1],
+                                          scale=0.5)
+        states.append(s)
+    return (q, k, v, g, beta, d.initial_state), o_ref, states
+
+
+def _run_tokens(inp, accept, bf16=True):
+    q, k, v, g, beta, s0 = inp
+    dt = torch.bfloat16 if bf16 else torch.float32
+    state = to_dev(s0)
+    acc = None if accept is None else torch.tensor(accept, dtype=torch.int32, device=DEV)
+    o = kda.decode_tokens(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), to_dev(g), to_dev(beta), state,
+                          accept=acc, scale=0.5)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), state.cpu().numpy()
+
+
+@pytest.mark.parametrize("D", [128, 16])
+@pytest.mark.parametrize("T", [1, 3, 8, 16])
+def test_decode_tokens_against_stepwise_oracle(D, T):
+    """Every token's output against T oracle steps, and the committed state
+    against the oracle state after accept[n] tokens (0, T, and values between)."""
+    N, H = 6, 3
+    print(f"case: decode_tokens N={N} T={T} H={H} D={D}", flush=True)
+    inp, o_ref, states = _tokens_case(N, T, H, D, seed=50 + T + D)
+    accept = [0, T, T // 2, 1, max(T - 1, 0), -3][:N]   # -3 is clamped to 0
+    o, S = _run_tokens(inp, accept)
+    for n, h in np.ndindex(N, H):
+        err = rel_err(o[n, :, h], o_ref[n, :, h])
+        assert err <= O_TOL, f"o seq {n} head {h}: rel err {err:.3e}"
+    for n in range(N):
+        a = min(max(accept[n], 0), T)
+        if a == 0:
+            assert np.array_equal(S[n], inp[5][n]), f"seq {n}: state changed with accept 0"
+        else:
+            check_states(S[n:n + 1], states[a][n:n + 1], f"state seq {n} after {a}")
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_decode_tokens_commit_all_fp32_and_bf16(bf16):
+    N, T, H, D = 4, 5, 2, 128
+    print(f"case: decode_tokens commit-all bf16={bf16}", flush=True)
+    inp, o_ref, states = _tokens_case(N, T, H, D, seed=71, bf16=bf16)
+    o, S = _run_tokens(inp, None, bf16=bf16)
+    for n, h in np.ndindex(N, H):
+        assert rel_err(o[n, :, h], o_ref[n, :, h]) <= O_TOL
+    check_states(S, states[T], "state")
+
+
+def test_decode_tokens_verify_then_commit():
+    """A verify call (accept 0) leaves every state bit-identical; a second
+    call with the accepted lengths gives the same outputs and exactly the
+    state a single committing call gives."""
+    N, T, H, D = 8, 6, 4, 128
+    print(f"case: decode_tokens verify-then-commit N={N} T={T}", flush=True)
+    inp, _, states = _tokens_case(N, T, H, D, seed=83)
+    o0, S0 = _run_tokens(inp, [0] * N)
+    assert np.array_equal(S0, inp[5])
+    accept = [3, 0, 6, 1, 2, 5, 4, 6]
+    o1, S1 = _run_tokens(inp, accept)
+    assert np.array_equal(o0, o1)
+    for n in range(N):
+        if accept[n]:
+            check_states(S1[n:n + 1], states[accept[n]][n:n + 1], f"seq {n}")
+
+
+def test_decode_tokens_equals_repeated_decode_steps():
+    """One T-token call and T single-token calls run the same fp32 arithmetic
+    per step (the state is stored as fp32 between the single calls)."""
+    N, T, H, D = 5, 4, 3, 128
+    inp, _, _ = _tokens_case(N, T, H, D, seed=97)
+    q, k, v, g, beta, s0 = inp
+    state = to_dev(s0)
+    outs = []
+    for t in range(T):
+        outs.append(kda.decode_step(to_dev(q[:, t], torch.bfloat16), to_dev(k[:, t], torch.bfloat16),
+                                    to_dev(v[:, t], torch.bfloat16), to_dev(g[:, t]), to_dev(beta[:, t]),
+                                    state, scale=0.5))
+    torch.cuda.synchronize()
+    o_steps = torch.stack(outs, 1).float().cpu().numpy()
+    o, S = _run_tokens(inp, None)
+    assert rel_err(o, o_steps) <= 1e-2          # bf16 outputs: at most an ulp apart
+    assert rel_err(S, state.cpu().numpy()) <= 1e-5
+
+
+def test_decode_tokens_full_size_draft_step():
+    """256 sequences x 32 heads, 4 draft tokens each, D=128, mixed accepted
+    lengths; sampled (sequence, head) pairs against the oracle."""
+    N, T, H, D = 256, 4, 32, 128
+    print(f"case: decode_tokens full size N={N} T={T} H={H}", flush=True)
+    d = make_inputs(N * T, H, D, seed=101, lengths=[T] * N, initial_state=True)
+    shp = lambda a: np.ascontiguousarray(a.reshape(N, T, *a.shape[1:]))
+    q, k, v, g, beta = map(shp, (d.q, d.k, d.v, d.g, d.beta))
+    accept = [(n * 7) % (T + 1) for n in range(N)]
+    o, S = _run_tokens((q, k, v, g, beta, d.initial_state), accept)
+    rng = np.random.default_rng(5)
+    seqs = rng.choice(N, 12, replace=False)
+    for n in seqs:
+        st = d.initial_state[n:n + 1].astype(np.float64)
+        for t in range(T):
+            o_t, st_next = reference.decode(q[n:n + 1, t], k[n:n + 1, t], v[n:n + 1, t], g[n:n + 1, t],
+                                            beta[n:n + 1, t], st, scale=0.5)
+            for h in range(H):
+                assert rel_err(o[n, t, h], o_t[0, h]) <= O_TOL, (n, t, h)
+            st = st_next
+            if t + 1 == accept[n]:
+                check_states(S[n:n + 1], st, f"seq {n}")
+        if accept[n] == 0:
+            assert np.array_equal(S[n], d.initial_state[n])
