@@ -9,4 +9,6 @@ Modules:
   oracle.reference  -- ctypes front end of the C fp64 token-by-token oracle
   oracle.brute      -- exact rational recurrence and dense transition products
   oracle.chunk_spec -- fp64 chunked (matmul) form, used to pin chunk algebra
+  oracle.frontend   -- fp64 front end: q/k L2 normalisation, gate and beta
+                       from raw logits
 """

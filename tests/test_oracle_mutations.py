@@ -85,3 +85,43 @@ def test_a_pin_catches(name, tmp_path, monkeypatch):
         except AssertionError:
             caught.append(getattr(pin, "__name__", "pin"))
     assert caught, f"no pin caught the planted mistake: {name}"
+
+
+# ------------------------------------------------------ front-end oracle
+import importlib.util  # noqa: E402
+
+import test_oracle_frontend as fe_pins  # noqa: E402
+
+FE_SRC = os.path.join(os.path.dirname(SRC), "frontend.py")
+
+FE_MUTATIONS = {
+    "softplus sign": ("return -np.logaddexp(0.0,", "return np.logaddexp(0.0,"),
+    "softplus replaced by the logit": ("return -np.logaddexp(0.0, np.asarray(a, dtype=np.float64))",
+                                       "return -np.asarray(a, dtype=np.float64)"),
+    "norm without the square root": ("x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + float(eps))",
+                                     "x / (np.sum(x * x, axis=-1, keepdims=True) + float(eps))"),
+    "norm over the wrong axis": ("np.sum(x * x, axis=-1, keepdims=True)", "np.sum(x * x, axis=-2, keepdims=True)"),
+    "norm eps dropped": ("keepdims=True) + float(eps))", "keepdims=True))"),
+    "sigmoid sign": ("1.0 / (1.0 + np.exp(-b))", "1.0 / (1.0 + np.exp(b))"),
+    "k left unnormalised": ("q, k = l2_normalize(q, eps), l2_normalize(k, eps)", "q = l2_normalize(q, eps)"),
+    "beta flag applies the gate": ("beta = beta_from_logits(beta)", "beta = gate_from_logits(beta)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FE_MUTATIONS))
+def test_a_front_end_pin_catches(name, tmp_path):
+    old, new = FE_MUTATIONS[name]
+    src = open(FE_SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    path = tmp_path / "frontend_mut.py"
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location("frontend_mut", str(path))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    caught = []
+    for check in fe_pins.CHECKS:
+        try:
+            check(mod)
+        except AssertionError:
+            caught.append(check.__name__)
+    assert caught, f"no front-end pin caught the planted mistake: {name}"
