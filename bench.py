@@ -133,6 +133,17 @@ def main():
     nbytes = prefill_bytes(T, H, D)
     tokens_per_s = T / (ms_step * 1e-3)
 
+    # the same prefill from raw projections, with the fused front end
+    rq, rk, rv, rg, rbeta, _, _ = make_inputs_device(T, H, D, seed=2, device=dev, raw=True)
+    fe = kda.Frontend(kda.FE_ALL, 1e-6)
+
+    def fstep():
+        kda.prefill(rq, rk, rv, rg, rbeta, plan=plan, o=o, final_state=fin, frontend=fe)
+
+    _, fms = time_events(fstep, args.steps, args.warmup)
+    f_ms = float(np.mean(fms))
+    del rq, rk, rv, rg, rbeta
+
     # decode: 256 sequences x 32 heads
     N = 256
     dq, dk, dv, dg, dbeta, _, ds0 = make_inputs_device(N, H, D, seed=3, device=dev, lengths=[1] * N,
@@ -190,6 +201,9 @@ def main():
                      "algorithmic_bytes_per_launch": nbytes, "launch_ms": round(ev_ms, 4)},
         "prefill_tflops": round(flops / (ev_ms * 1e-3) / 1e12, 2),
         "prefill_mfma_frac_of_peak": round(flops / (ev_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        "prefill_front_end": {"workload": "the same prefill from raw q, k and gate/beta logits "
+                                          "(L2 norm, -softplus gate, sigmoid beta fused into the prep kernel)",
+                              "launch_ms": round(f_ms, 4), "tokens_per_s": round(T / (f_ms * 1e-3), 1)},
         "decode": {"workload": "256 sequences x 32 heads, D=128, one token, fp32 states in place",
                    "ms": round(d_ms, 4), "head_tokens_per_s": round(N * H / (d_ms * 1e-3), 1),
                    "GBps": round(d_gbps, 1), "hbm_frac": round(d_gbps / HBM_PEAK_GBPS, 4),

@@ -4,6 +4,7 @@
 #include "kda.h"
 #include "kda_internal.h"
 
+#include <float.h>
 #include <limits.h>
 
 #include <initializer_list>
@@ -36,6 +37,13 @@ static_assert(kda::kBlockTokens * -KDA_PREFILL_MIN_G_FLOOR * 1.4426950408889634f
               "decay span of a block");
 
 // Every tensor pointer must be 16-byte aligned (NULL passes).
+// Front-end descriptor: NULL or known flag bits with a usable epsilon.
+bool frontend_ok(const kda_frontend* fe) {
+  if (!fe) return true;
+  const uint32_t known = KDA_FE_L2NORM_QK | KDA_FE_GATE_LOGITS | KDA_FE_BETA_LOGITS;
+  return (fe->flags & ~known) == 0 && fe->norm_eps >= 0.f && fe->norm_eps <= FLT_MAX;
+}
+
 bool aligned16(std::initializer_list<const void*> ps) {
   for (const void* p : ps)
     if ((uintptr_t)p & 15) return false;
@@ -83,7 +91,21 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_
                                const float* initial_state, float* final_state,
                                int32_t ckpt_interval, float* checkpoints, void* o,
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return kda_prefill_chunked_fe(q, k, v, dtype, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H,
+                                Dk, Dv, scale, g_min, initial_state, final_state, ckpt_interval,
+                                checkpoints, o, workspace, workspace_bytes, nullptr, stream);
+}
+
+kda_status kda_prefill_chunked_fe(const void* q, const void* k, const void* v, kda_dtype dtype,
+                                  const float* g, const float* beta, const int32_t* cu_seqlens,
+                                  const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
+                                  int32_t Dk, int32_t Dv, float scale, float g_min,
+                                  const float* initial_state, float* final_state,
+                                  int32_t ckpt_interval, float* checkpoints, void* o,
+                                  void* workspace, size_t workspace_bytes,
+                                  const kda_frontend* fe, hipStream_t stream) {
   if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
+  if (!frontend_ok(fe)) return KDA_ERR_INVALID_ARG;
   if (!supported_dims(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
   int64_t tokens, blocks;
   if (H <= 0 || num_seqs < 0 || !cu_seqlens || !scan_lengths(cu_seqlens_host, num_seqs, &tokens, &blocks))
@@ -108,6 +130,7 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_
   a.num_seqs = num_seqs; a.H = H; a.D = Dk;
   a.total_tokens = tokens; a.total_blocks = blocks;
   a.scale = scale; a.g_min = g_min;
+  a.fe_flags = fe ? fe->flags : 0u; a.fe_eps = fe ? fe->norm_eps : 0.f;
   a.initial_state = initial_state; a.final_state = final_state;
   a.ckpt_interval = nck > 0 ? ckpt_interval : 0;
   a.checkpoints = checkpoints;
@@ -141,8 +164,9 @@ kda_status kda_decode_tokens(const void* q, const void* k, const void* v, kda_dt
                              const float* g, const float* beta, float* state,
                              const int32_t* accept, void* o, int32_t N, int32_t T, int32_t H,
                              int32_t Dk, int32_t Dv, float scale, float g_min,
-                             hipStream_t stream) {
+                             const kda_frontend* fe, hipStream_t stream) {
   if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
+  if (!frontend_ok(fe)) return KDA_ERR_INVALID_ARG;
   if (!supported_dims(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
   if (T < 1 || T > KDA_DECODE_MAX_TOKENS) return KDA_ERR_INVALID_ARG;
   if (N < 0 || H <= 0 || (int64_t)N * H > INT32_MAX || (int64_t)N * T * H > INT32_MAX)
@@ -155,6 +179,7 @@ kda_status kda_decode_tokens(const void* q, const void* k, const void* v, kda_dt
   a.N = N; a.H = H; a.D = Dk;
   a.T = T; a.accept = accept;
   a.scale = scale; a.g_min = g_min;
+  a.fe_flags = fe ? fe->flags : 0u; a.fe_eps = fe ? fe->norm_eps : 0.f;
   a.bf16 = dtype == KDA_BF16;
   a.stream = stream;
   return from_hip(kda::launch_decode(a));

@@ -48,6 +48,22 @@ __device__ __forceinline__ float gate_alpha(float g, float g_min) {
   return __builtin_amdgcn_exp2f(g * kLog2e);
 }
 
+// Front end (raw inputs; flag values as in kda.h):
+// decay from a gate logit a: e^{-softplus(a)} = 1 / (1 + e^a), floored at
+// alpha_min = e^{g_min}. Equal to exp(clamp(-softplus(a), g_min, 0)), since
+// -softplus(a) < 0 and exp is monotone.
+__device__ __forceinline__ float gate_alpha_logit(float a, float alpha_min) {
+  return fmaxf(__builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a * kLog2e)), alpha_min);
+}
+// write strength from a logit b: sigmoid(b) = 1 / (1 + e^-b)
+__device__ __forceinline__ float beta_logit(float b) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-b * kLog2e));
+}
+// 1 / sqrt(sum of squares + eps)
+__device__ __forceinline__ float inv_norm(float sumsq, float eps) {
+  return __builtin_amdgcn_rsqf(sumsq + eps);
+}
+
 // ---- bf16 operand packing -----------------------------------------------------
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
   bf16x4 r;

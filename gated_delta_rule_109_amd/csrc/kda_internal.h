@@ -24,6 +24,8 @@ struct DecodeArgs {
   int32_t T;                  // tokens per sequence (1 for a plain decode step)
   const int32_t* accept;      // device [N] tokens to commit, or NULL (= T)
   float scale, g_min;
+  uint32_t fe_flags = 0;      // KDA_FE_* (0: inputs used as given)
+  float fe_eps = 0.f;
   bool bf16;
   hipStream_t stream;
 };
@@ -36,6 +38,8 @@ struct PrefillArgs {
   int64_t total_tokens;
   int64_t total_blocks;       // sum_n ceil(L_n / kBlockTokens), from the host copy
   float scale, g_min;
+  uint32_t fe_flags = 0;      // KDA_FE_* (0: inputs used as given)
+  float fe_eps = 0.f;
   const float* initial_state;
   float* final_state;
   int32_t ckpt_interval;

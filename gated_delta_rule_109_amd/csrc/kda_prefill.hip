@@ -171,11 +171,15 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
 template <int D>
 constexpr int prep_threads() { return D >= 128 ? D : 64; }
 
-template <int D, typename TIn>
+//
+// kFE: the optional front end (flags as in kda.h). Raw q and k rows are scaled
+// by their inverse L2 norms (phase 0 computes them per token), and g and beta
+// may be logits: alpha = max(1 / (1 + e^a), e^{g_min}), beta = sigmoid(b).
+template <int D, typename TIn, bool kFE>
 __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const int2* __restrict__ blk_info, int H, float g_min,
-    char* __restrict__ records) {
+    uint32_t fe_flags, float fe_eps, char* __restrict__ records) {
   using R = Rec<D>;
   constexpr int kThreads = prep_threads<D>();
   constexpr int kWaves = kThreads / kWave;
@@ -190,6 +194,7 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
   float(*sM)[20] = (float(*)[20])(lds_raw + (kBT * (kBT + 4) + 16 * 20) * 4);      // A_ba T_aa
   __shared__ __attribute__((aligned(16))) float sA[kBT][kBT + 4];
   __shared__ float sBeta[kBT];
+  __shared__ float sRk[kFE ? kBT : 1], sRq[kFE ? kBT : 1];   // inverse row norms of k and q
 
   // Heads vary fastest across consecutive workgroups: the H heads of one token
   // row are contiguous in q, k, v and g, so neighbouring workgroups read
@@ -203,7 +208,53 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
   char* rec = records + ((size_t)h * gridDim.y + c) * R::kBytes;   // head-major: a head's blocks are contiguous
   auto row = [&](int t) __attribute__((always_inline)) { return ((size_t)(tok0 + t) * H + h) * D; };
 
-  if (tid < kBT) sBeta[tid] = tid < cnt ? beta[(size_t)(tok0 + tid) * H + h] : 0.f;
+  if (tid < kBT) {
+    float b = beta[(size_t)(tok0 + min(tid, cnt - 1)) * H + h];
+    if (kFE && (fe_flags & KDA_FE_BETA_LOGITS)) b = beta_logit(b);
+    sBeta[tid] = tid < cnt ? b : 0.f;
+  }
+  const float alpha_min = kFE ? __builtin_amdgcn_exp2f(g_min * kLog2e) : 0.f;
+  auto alpha_of = [&](float x) __attribute__((always_inline)) {
+    return kFE && (fe_flags & KDA_FE_GATE_LOGITS) ? gate_alpha_logit(x, alpha_min) : gate_alpha(x, g_min);
+  };
+
+  // ---- phase 0 (front end only): inverse L2 norms of the 32 k and q rows.
+  // kThreads / 32 lanes per token, each summing D / (kThreads / 32) channels
+  // of both rows, then a butterfly over those lanes.
+  if constexpr (kFE) {
+    constexpr int kLanesPerTok = kThreads / kBT;
+    constexpr int kChPerLane = D / kLanesPerTok;
+    static_assert(kChPerLane % 4 == 0 && (kLanesPerTok & (kLanesPerTok - 1)) == 0, "phase 0 split");
+    const int t = tid / kLanesPerTok, part = tid % kLanesPerTok;
+    const size_t off = row(min(t, cnt - 1)) + part * kChPerLane;
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int c = 0; c < kChPerLane; c += 4) {
+      f32x4 xk, xq;
+      if constexpr (sizeof(TIn) == 2) {
+        xk = from_bf16x4(*(const bf16x4*)(k + off + c));
+        xq = from_bf16x4(*(const bf16x4*)(q + off + c));
+      } else {
+        xk = *(const f32x4*)(k + off + c);
+        xq = *(const f32x4*)(q + off + c);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { sk += xk[i] * xk[i]; sq += xq[i] * xq[i]; }
+    }
+#pragma unroll
+    for (int m = 1; m < kLanesPerTok; m <<= 1) {
+      sk += __shfl_xor(sk, m);
+      sq += __shfl_xor(sq, m);
+    }
+    if (part == 0) {
+      const bool norm = fe_flags & KDA_FE_L2NORM_QK;
+      sRk[t] = norm ? inv_norm(sk, fe_eps) : 1.f;
+      sRq[t] = norm ? inv_norm(sq, fe_eps) : 1.f;
+    }
+    __syncthreads();
+  }
+  auto rk = [&](int t) __attribute__((always_inline)) { return kFE ? sRk[t] : 1.f; };
+  auto rq = [&](int t) __attribute__((always_inline)) { return kFE ? sRq[t] : 1.f; };
 
   // ---- phase 1: one channel per thread (coalesced rows). Rows past the end
   // of the sequence give alpha = 1 and k = 0. Every load reads a valid row
@@ -220,8 +271,8 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
     }
 #pragma unroll
     for (int t = 0; t < kBT; ++t) {
-      a[t] = t < cnt ? gate_alpha(a[t], g_min) : 1.f;
-      kf[t] = t < cnt ? kf[t] : 0.f;
+      a[t] = t < cnt ? alpha_of(a[t]) : 1.f;
+      kf[t] = t < cnt ? kf[t] * rk(t) : 0.f;
     }
     float P = 1.f, P16 = 1.f;
 #pragma unroll
@@ -285,9 +336,10 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
         for (int p = 0; p < R::NP; ++p) {
           const int t = 16 * u + mm, c0 = ch_of(p, gq, 0), c1 = ch_of(p, gq, 4);
           const f32x4 P0 = decay(t, c0), P1 = decay(t, c1);
-          const f32x4 x0 = piece(src, t, c0), x1 = piece(src, t, c1);
+          const float rs = which ? rq(t) : rk(t);
+          const f32x4 x0 = piece(src, t, c0) * rs, x1 = piece(src, t, c1) * rs;
           X[u][p] = cat(to_bf16x4(x0 * P0), to_bf16x4(x1 * P1));
-          const f32x4 k0 = which ? piece(k, t, c0) : x0, k1 = which ? piece(k, t, c1) : x1;
+          const f32x4 k0 = which ? piece(k, t, c0) * rk(t) : x0, k1 = which ? piece(k, t, c1) * rk(t) : x1;
           f32x4 r0, r1;
 #pragma unroll
           for (int i = 0; i < 4; ++i) { r0[i] = k0[i] / P0[i]; r1[i] = k1[i] / P1[i]; }
@@ -787,9 +839,14 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.total_blocks > 0) {
-    hipLaunchKernelGGL((prep_kernel<D, TIn>), dim3((unsigned)a.H, (unsigned)a.total_blocks),
-                       dim3(prep_threads<D>()), 0, a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g,
-                       a.beta, (const int2*)blk_info, a.H, a.g_min, records);
+    if (a.fe_flags)
+      hipLaunchKernelGGL((prep_kernel<D, TIn, true>), dim3((unsigned)a.H, (unsigned)a.total_blocks),
+                         dim3(prep_threads<D>()), 0, a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g,
+                         a.beta, (const int2*)blk_info, a.H, a.g_min, a.fe_flags, a.fe_eps, records);
+    else
+      hipLaunchKernelGGL((prep_kernel<D, TIn, false>), dim3((unsigned)a.H, (unsigned)a.total_blocks),
+                         dim3(prep_threads<D>()), 0, a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g,
+                         a.beta, (const int2*)blk_info, a.H, a.g_min, 0u, 0.f, records);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

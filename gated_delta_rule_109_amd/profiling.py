@@ -31,7 +31,10 @@ import re
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-PREFILL_KERNELS = ("plan_kernel", "prep_kernel", "chain_kernel")
+# the kernels of one plain kda_prefill_chunked call on the benchmarked shape
+# (D = 128, bf16 q/k/v, no front end)
+PREFILL_KERNELS = ("kda::plan_kernel", "kda::prep_kernel<128, unsigned short, false>",
+                   "kda::chain_kernel<128, unsigned short>")
 CALIB_KERNEL = "AbsFunctor"
 
 
@@ -53,16 +56,21 @@ def _counter_csv(d):
     return hits[0]
 
 
+def kernel_key(name):
+    """A kernel's name with its template arguments, without the parameter list."""
+    return re.sub(r"\(.*", "", name).replace("void ", "").strip()
+
+
 def per_kernel(d, counter):
-    """{short kernel name: (dispatches, mean KiB per dispatch)} for one counter."""
+    """{kernel name with template arguments: (dispatches, mean KiB per
+    dispatch)} for one counter."""
     acc = {}
     for r in csv.DictReader(open(_counter_csv(d))):
         if r["Counter_Name"] != counter:
             continue
         name = r["Kernel_Name"]
-        m = re.search(r"kda::(\w+)", name)
-        if m:
-            key = m.group(1)
+        if "kda::" in name:
+            key = kernel_key(name)
         elif CALIB_KERNEL in name:
             key = CALIB_KERNEL
         else:
@@ -89,8 +97,10 @@ def summarize(fetch_dir, write_dir, calib_mib):
         wb = w[k][1] * fw * 1024
         total += fb + wb
         rows.append((k, f[k][0], f[k][1], w[k][1], fb, wb))
-    return {"fetch_factor": ff, "write_factor": fw, "rows": rows, "bytes_per_call": total,
-            "calib": (f[CALIB_KERNEL][1], w[CALIB_KERNEL][1])}
+    others = [(k, f[k][0], f[k][1], w[k][1], f[k][1] * ff * 1024, w[k][1] * fw * 1024)
+              for k in sorted(f) if k in w and k not in PREFILL_KERNELS and k != CALIB_KERNEL]
+    return {"fetch_factor": ff, "write_factor": fw, "rows": rows, "others": others,
+            "bytes_per_call": total, "calib": (f[CALIB_KERNEL][1], w[CALIB_KERNEL][1])}
 
 
 def render(res, calib_mib, command, algorithmic_bytes):
@@ -105,8 +115,14 @@ def render(res, calib_mib, command, algorithmic_bytes):
             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB (scaled) |",
             "|---|---|---|---|---|---|"]
     for k, n, fk, wk, fb, wb in res["rows"]:
-        out.append(f"| `kda::{k}` | {n} | {fk:.4g} | {wk:.4g} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
+        out.append(f"| `{k}` | {n} | {fk:.4g} | {wk:.4g} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
     tot = res["bytes_per_call"]
+    if res.get("others"):
+        out += ["", "Other kda kernels in the same run (not part of the call above; per dispatch):", "",
+                "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB (scaled) |",
+                "|---|---|---|---|---|---|"]
+        for k, n, fk, wk, fb, wb in res["others"]:
+            out.append(f"| `{k}` | {n} | {fk:.4g} | {wk:.4g} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
     out += ["", f"HBM bytes per `kda_prefill_chunked` call: {tot / 1e6:.1f} MB, against "
             f"{algorithmic_bytes / 1e6:.1f} MB algorithmic (ratio {tot / algorithmic_bytes:.2f}).", "",
             "traffic-record: " + json.dumps({"bytes_per_call": round(tot), "source_digest": source_digest(),
@@ -137,7 +153,7 @@ def kernel_stats(d):
     for r in csv.DictReader(open(hits[0])):
         if "kda::" not in r["Name"]:
             continue
-        name = re.sub(r"\(.*", "", r["Name"]).replace("void ", "")
+        name = kernel_key(r["Name"])
         rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                      float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
     return rows

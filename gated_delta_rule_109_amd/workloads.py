@@ -96,22 +96,29 @@ class Inputs:
 
 
 def make_inputs(T, H, Dk, Dv=None, seed=0, bf16=True, num_seqs=None, lengths=None,
-                initial_state=False, g_scale=1.0) -> Inputs:
-    """Packed inputs [T, H, D]; ``lengths`` (or one sequence) sets cu_seqlens."""
+                initial_state=False, g_scale=1.0, raw=False) -> Inputs:
+    """Packed inputs [T, H, D]; ``lengths`` (or one sequence) sets cu_seqlens.
+
+    raw=True returns the same draws before the front-end step: q and k as
+    drawn (not normalised), g and beta as the N(0, 1) logits."""
     Dv = Dk if Dv is None else Dv
     rng = np.random.default_rng(seed)
     if lengths is None:
         lengths = [T] if num_seqs is None else None
     assert lengths is not None and sum(lengths) == T
-    q = _l2n(rng.standard_normal((T, H, Dk), dtype=np.float32))
-    k = _l2n(rng.standard_normal((T, H, Dk), dtype=np.float32))
+    norm = (lambda x: x) if raw else _l2n
+    q = norm(rng.standard_normal((T, H, Dk), dtype=np.float32))
+    k = norm(rng.standard_normal((T, H, Dk), dtype=np.float32))
     v = rng.standard_normal((T, H, Dv), dtype=np.float32)
     if bf16:
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     bl = rng.standard_normal((T, H), dtype=np.float32)
-    beta = (1.0 / (1.0 + np.exp(-bl))).astype(np.float32)
+    beta = bl if raw else (1.0 / (1.0 + np.exp(-bl))).astype(np.float32)
     gl = rng.standard_normal((T, H, Dk), dtype=np.float32)
-    g = np.clip(-np.logaddexp(np.float32(0), gl), np.float32(LN_HALF), np.float32(0)).astype(np.float32)
+    if raw:
+        g = gl
+    else:
+        g = np.clip(-np.logaddexp(np.float32(0), gl), np.float32(LN_HALF), np.float32(0)).astype(np.float32)
     if g_scale != 1.0:
         g = (g * np.float32(g_scale)).astype(np.float32)
     s0 = None
@@ -127,11 +134,11 @@ def workload_inputs(w: Workload) -> Inputs:
                        initial_state=w.initial_state)
 
 
-def make_inputs_device(T, H, D, seed, device, lengths=None, initial_state=False, bf16=True):
+def make_inputs_device(T, H, D, seed, device, lengths=None, initial_state=False, bf16=True, raw=False):
     """Same recipe as make_inputs, drawn with a seeded torch generator on the
     device (for the large workloads, where host generation would dominate).
     Returns torch tensors: q, k, v (bf16 or fp32), g, beta (fp32), cu (int32,
-    host), s0 (fp32 or None)."""
+    host), s0 (fp32 or None). raw=True as in make_inputs."""
     import torch
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
@@ -142,14 +149,18 @@ def make_inputs_device(T, H, D, seed, device, lengths=None, initial_state=False,
         return torch.randn(*shape, generator=gen, device=device, dtype=torch.float32)
 
     q = normal(T, H, D)
-    q = q / q.norm(dim=-1, keepdim=True)
     k = normal(T, H, D)
-    k = k / k.norm(dim=-1, keepdim=True)
+    if not raw:
+        q = q / q.norm(dim=-1, keepdim=True)
+        k = k / k.norm(dim=-1, keepdim=True)
     v = normal(T, H, D)
     dt = torch.bfloat16 if bf16 else torch.float32
     q, k, v = q.to(dt), k.to(dt), v.to(dt)
-    beta = torch.sigmoid(normal(T, H))
-    g = (-torch.nn.functional.softplus(normal(T, H, D))).clamp_(min=LN_HALF, max=0.0)
+    beta = normal(T, H)
+    g = normal(T, H, D)
+    if not raw:
+        beta = torch.sigmoid(beta)
+        g = (-torch.nn.functional.softplus(g)).clamp_(min=LN_HALF, max=0.0)
     s0 = 0.02 * normal(len(lengths), H, D, D) if initial_state else None
     cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
     cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)

@@ -72,6 +72,29 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
  * the fp32 / bf16 range. ln 0.5 (the configurations here) is far above it. */
 #define KDA_PREFILL_MIN_G_FLOOR (-2.5f)
 
+/* Optional front end: the step just before the recurrence, fused into the
+ * kernels that first read q, k, g and beta, so that no separate pass over
+ * them is needed. Each flag replaces one input convention:
+ *   KDA_FE_L2NORM_QK   q and k are raw; each (token, head) row x is used as
+ *                      x / sqrt(sum_i x_i^2 + norm_eps), computed in fp32
+ *                      (the operator's inputs are unit-norm keys and queries;
+ *                      [K3-SA] Background: the delta rule as a step on the L2
+ *                      value-retrieval loss)
+ *   KDA_FE_GATE_LOGITS g holds raw gate logits a; the log-decay is
+ *                      g = -softplus(a) = -ln(1 + e^a), then floored at g_min
+ *                      as always ([K3-DD] 4-1 KDA, first bullet: a lower
+ *                      bound on each key channel's decay)
+ *   KDA_FE_BETA_LOGITS beta holds raw logits b; the write strength is
+ *                      sigmoid(b) = 1 / (1 + e^-b)
+ * A NULL descriptor, or flags = 0, means the inputs are used as given. */
+#define KDA_FE_L2NORM_QK 1u
+#define KDA_FE_GATE_LOGITS 2u
+#define KDA_FE_BETA_LOGITS 4u
+typedef struct {
+  uint32_t flags;   /* OR of KDA_FE_* ; other bits are invalid */
+  float norm_eps;   /* >= 0 and finite; used only with KDA_FE_L2NORM_QK */
+} kda_frontend;
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* kda_status_string(kda_status status);
 
@@ -132,6 +155,20 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_
                                int32_t ckpt_interval, float* checkpoints, void* o,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* kda_prefill_chunked with the optional front end `fe` (see kda_frontend):
+ * q, k, g and beta may be raw (unnormalised keys and queries, gate and write
+ * logits). Same arguments, layouts, outputs and errors otherwise, plus
+ * KDA_ERR_INVALID_ARG for unknown flag bits or a negative or non-finite
+ * norm_eps. fe = NULL is exactly kda_prefill_chunked. */
+kda_status kda_prefill_chunked_fe(const void* q, const void* k, const void* v, kda_dtype dtype,
+                                  const float* g, const float* beta, const int32_t* cu_seqlens,
+                                  const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
+                                  int32_t Dk, int32_t Dv, float scale, float g_min,
+                                  const float* initial_state, float* final_state,
+                                  int32_t ckpt_interval, float* checkpoints, void* o,
+                                  void* workspace, size_t workspace_bytes,
+                                  const kda_frontend* fe, hipStream_t stream);
+
 /* One recurrent decode step for N independent sequences ([K3-SA] Methods 1)
  * FlashKDA, first bullet: decode runs the state update directly; about 7 D^2
  * FLOPs and 8 D^2 bytes of fp32 state traffic per head-token).
@@ -167,14 +204,15 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
  *          prefix length a_n is known a second call with accept = a_n on the
  *          same inputs commits exactly that prefix.
  *   o      [N, T, H, Dv] dtype, output of every token whatever accept holds
+ *   fe     optional front end (see kda_frontend), or NULL
  * Errors: KDA_ERR_INVALID_ARG (null required pointer, T outside
- * [1, KDA_DECODE_MAX_TOKENS], negative N, H <= 0), KDA_ERR_UNSUPPORTED,
- * KDA_ERR_HIP. */
+ * [1, KDA_DECODE_MAX_TOKENS], negative N, H <= 0, bad front-end flags or
+ * norm_eps), KDA_ERR_UNSUPPORTED, KDA_ERR_HIP. */
 kda_status kda_decode_tokens(const void* q, const void* k, const void* v, kda_dtype dtype,
                              const float* g, const float* beta, float* state,
                              const int32_t* accept, void* o, int32_t N, int32_t T, int32_t H,
                              int32_t Dk, int32_t Dv, float scale, float g_min,
-                             hipStream_t stream);
+                             const kda_frontend* fe, hipStream_t stream);
 
 #ifdef __cplusplus
 }

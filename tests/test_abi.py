@@ -127,7 +127,7 @@ def test_decode_tokens_argument_errors(L):
     call = lambda **o: L.kda_decode_tokens(*dict(dict(q=fake, k=fake, v=fake, dtype=0, g=fake,
                                                       beta=fake, state=fake, accept=None, o=fake,
                                                       N=4, T=3, H=2, Dk=128, Dv=128, scale=1.0,
-                                                      g_min=-0.69, stream=None), **o).values())
+                                                      g_min=-0.69, fe=None, stream=None), **o).values())
     assert call(Dk=16, Dv=128) == kda.KDA_ERR_UNSUPPORTED
     assert call(dtype=2) == kda.KDA_ERR_UNSUPPORTED
     assert call(T=0) == kda.KDA_ERR_INVALID_ARG
@@ -138,8 +138,34 @@ def test_decode_tokens_argument_errors(L):
     assert call(o=None) == kda.KDA_ERR_INVALID_ARG
     assert call(beta=ctypes.c_void_p(0x1002)) == kda.KDA_ERR_INVALID_ARG
     assert call(N=0) == kda.KDA_OK
+    for bad in (kda.Frontend(8), kda.Frontend(kda.FE_ALL, -1.0), kda.Frontend(1, float("nan")),
+                kda.Frontend(1, float("inf"))):
+        assert call(fe=ctypes.byref(bad)) == kda.KDA_ERR_INVALID_ARG
+    assert call(fe=ctypes.byref(kda.Frontend(kda.FE_ALL, 0.0)), N=0) == kda.KDA_OK
 
 
 def test_decode_max_tokens_matches_header():
     m = re.search(r"#define\s+KDA_DECODE_MAX_TOKENS\s+(\d+)", open(HEADER).read())
     assert m and int(m.group(1)) == kda.DECODE_MAX_TOKENS
+
+
+def test_prefill_front_end_argument_errors(L):
+    """kda_prefill_chunked_fe validates the descriptor first; with fe = NULL
+    it returns what kda_prefill_chunked returns."""
+    fake = ctypes.c_void_p(0x1000)
+    cu = (ctypes.c_int32 * 2)(0, 64)
+    ws = ctypes.c_void_p(0x100000)
+
+    def call(fe, **over):
+        a = dict(q=fake, k=fake, v=fake, dtype=0, g=fake, beta=fake, cu=fake,
+                 cu_host=ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)), N=1, H=2, Dk=128, Dv=128,
+                 scale=1.0, g_min=-0.69, s0=None, fin=None, ck_int=0, ck=None, o=fake, ws=ws,
+                 ws_bytes=0, fe=fe, stream=None)
+        a.update(over)
+        return L.kda_prefill_chunked_fe(*a.values())
+    for bad in (kda.Frontend(16), kda.Frontend(kda.FE_L2NORM_QK, -0.5), kda.Frontend(2, float("nan"))):
+        assert call(ctypes.byref(bad)) == kda.KDA_ERR_INVALID_ARG
+    # valid descriptor: the next check that fails is the workspace size
+    assert call(ctypes.byref(kda.Frontend(kda.FE_ALL, 1e-6))) == kda.KDA_ERR_WORKSPACE
+    assert call(None) == kda.KDA_ERR_WORKSPACE
+    assert call(None, Dk=64, Dv=64) == kda.KDA_ERR_UNSUPPORTED

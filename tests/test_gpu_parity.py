@@ -392,3 +392,122 @@ def test_decode_tokens_full_size_draft_step():
                 check_states(S[n:n + 1], st, f"seq {n}")
         if accept[n] == 0:
             assert np.array_equal(S[n], d.initial_state[n])
+
+
+# ------------------------------------------------------------- front end
+from oracle import frontend as fe_oracle  # noqa: E402
+
+FE_EPS = 1e-6
+
+
+def _fe_oracle_prefill(q, k, v, g, beta, cu, s0, flags, ckpt=0):
+    q2, k2, g2, b2 = fe_oracle.apply(q, k, g, beta, flags, eps=FE_EPS)
+    return reference.prefill(q2, k2, v, g2, b2, cu_seqlens=cu, initial_state=s0, ckpt_interval=ckpt)
+
+
+@pytest.mark.parametrize("D", [128, 16])
+@pytest.mark.parametrize("bf16", [True, False])
+def test_prefill_front_end_all_flags(D, bf16):
+    """Raw q, k (not normalised), gate and write logits, ragged varlen with
+    initial states and checkpoints; against the fp64 front end + oracle."""
+    lengths = [37, 0, 16, 1, 100, 64, 15, 17]
+    H = 3
+    print(f"case: prefill front end D={D} bf16={bf16}", flush=True)
+    raw = make_inputs(sum(lengths), H, D, seed=61 + D, lengths=lengths, initial_state=True, bf16=bf16,
+                      raw=True)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    o, fin, ck = kda.prefill(to_dev(raw.q, dt), to_dev(raw.k, dt), to_dev(raw.v, dt), to_dev(raw.g),
+                             to_dev(raw.beta), cu_seqlens=raw.cu_seqlens,
+                             initial_state=to_dev(raw.initial_state), ckpt_interval=32,
+                             frontend=kda.Frontend(kda.FE_ALL, FE_EPS))
+    torch.cuda.synchronize()
+    o_ref, f_ref, ck_ref = _fe_oracle_prefill(raw.q, raw.k, raw.v, raw.g, raw.beta, raw.cu_seqlens,
+                                              raw.initial_state, fe_oracle.L2NORM_QK | fe_oracle.GATE_LOGITS
+                                              | fe_oracle.BETA_LOGITS, ckpt=32)
+    check_outputs(o.float().cpu().numpy(), o_ref, raw.cu_seqlens, H)
+    check_states(fin.cpu().numpy(), f_ref, "final")
+    check_states(ck.cpu().numpy(), ck_ref, "checkpoint")
+
+
+@pytest.mark.parametrize("flag", [1, 2, 4])
+def test_prefill_front_end_one_flag(flag):
+    """One raw input kind at a time; the others are the prepared inputs drawn
+    from the same seed."""
+    lengths = [70, 33]
+    H, D = 2, 128
+    print(f"case: prefill front end flag {flag}", flush=True)
+    raw = make_inputs(sum(lengths), H, D, seed=73, lengths=lengths, raw=True)
+    prep = make_inputs(sum(lengths), H, D, seed=73, lengths=lengths)
+    q, k = (raw.q, raw.k) if flag == 1 else (prep.q, prep.k)
+    g = raw.g if flag == 2 else prep.g
+    beta = raw.beta if flag == 4 else prep.beta
+    o, fin, _ = kda.prefill(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16), to_dev(prep.v, torch.bfloat16),
+                            to_dev(g), to_dev(beta), cu_seqlens=prep.cu_seqlens,
+                            frontend=kda.Frontend(flag, FE_EPS))
+    torch.cuda.synchronize()
+    o_ref, f_ref, _ = _fe_oracle_prefill(q, k, prep.v, g, beta, prep.cu_seqlens, None, flag)
+    check_outputs(o.float().cpu().numpy(), o_ref, prep.cu_seqlens, H)
+    check_states(fin.cpu().numpy(), f_ref, "final")
+
+
+def test_prefill_front_end_no_flags_is_plain_prefill():
+    """A descriptor with no flags gives bit-for-bit the plain call."""
+    lengths = [50, 31]
+    H, D = 2, 128
+    inp = make_inputs(sum(lengths), H, D, seed=79, lengths=lengths, initial_state=True)
+    o1, f1, _ = run_prefill(inp, H, D)
+    o2, f2, _ = kda.prefill(to_dev(inp.q, torch.bfloat16), to_dev(inp.k, torch.bfloat16),
+                            to_dev(inp.v, torch.bfloat16), to_dev(inp.g), to_dev(inp.beta),
+                            cu_seqlens=inp.cu_seqlens, initial_state=to_dev(inp.initial_state),
+                            frontend=kda.Frontend(0, 0.0))
+    torch.cuda.synchronize()
+    assert np.array_equal(o1, o2.float().cpu().numpy()) and np.array_equal(f1, f2.cpu().numpy())
+
+
+def test_prefill_front_end_full_size_sampled_heads():
+    """B=1, H=32, T=8192, D=128 from raw projections; oracle on 2 heads."""
+    T, H, D = 8192, 32, 128
+    print("case: front end full size", flush=True)
+    q, k, v, g, beta, cu, _ = make_inputs_device(T, H, D, seed=12, device=DEV, raw=True)
+    o, fin, _ = kda.prefill(q, k, v, g, beta, cu_seqlens=cu, frontend=kda.Frontend(kda.FE_ALL, FE_EPS))
+    torch.cuda.synchronize()
+    heads = [0, 31]
+    sel = lambda t: t[:, heads].float().cpu().numpy()
+    o_ref, f_ref, _ = _fe_oracle_prefill(sel(q), sel(k), sel(v), sel(g), sel(beta), cu.numpy(), None,
+                                         fe_oracle.L2NORM_QK | fe_oracle.GATE_LOGITS | fe_oracle.BETA_LOGITS)
+    check_outputs(o[:, heads].float().cpu().numpy(), o_ref, cu.numpy(), len(heads))
+    check_states(fin[:, heads].cpu().numpy(), f_ref, "final")
+
+
+@pytest.mark.parametrize("D", [128, 16])
+@pytest.mark.parametrize("T", [1, 5])
+def test_decode_tokens_front_end(D, T):
+    """Multi-token decode from raw inputs with mixed accepted lengths, against
+    the fp64 front end + T single-token oracle steps."""
+    N, H = 4, 3
+    print(f"case: decode_tokens front end D={D} T={T}", flush=True)
+    raw = make_inputs(N * T, H, D, seed=89 + D + T, lengths=[T] * N, initial_state=True, raw=True)
+    shp = lambda a: np.ascontiguousarray(a.reshape(N, T, *a.shape[1:]))
+    q, k, v, g, beta = map(shp, (raw.q, raw.k, raw.v, raw.g, raw.beta))
+    accept = [T, 0, 1, T // 2 + 1][:N]
+    state = to_dev(raw.initial_state)
+    acc = torch.tensor(accept, dtype=torch.int32, device=DEV)
+    o = kda.decode_tokens(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16), to_dev(v, torch.bfloat16),
+                          to_dev(g), to_dev(beta), state, accept=acc, scale=0.5,
+                          frontend=kda.Frontend(kda.FE_ALL, FE_EPS))
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    S = state.cpu().numpy()
+    q2, k2, g2, b2 = fe_oracle.apply(q, k, g, beta, fe_oracle.L2NORM_QK | fe_oracle.GATE_LOGITS
+                                     | fe_oracle.BETA_LOGITS, eps=FE_EPS)
+    st = raw.initial_state.astype(np.float64)
+    for t in range(T):
+        o_t, st = reference.decode(q2[:, t], k2[:, t], v[:, t], g2[:, t], b2[:, t], st, scale=0.5)
+        for n, h in np.ndindex(N, H):
+            assert rel_err(o[n, t, h], o_t[n, h]) <= O_TOL, (n, t, h)
+        for n in range(N):
+            if min(accept[n], T) == t + 1:
+                check_states(S[n:n + 1], st[n:n + 1], f"seq {n}")
+    for n in range(N):
+        if accept[n] == 0:
+            assert np.array_equal(S[n], raw.initial_state[n])
