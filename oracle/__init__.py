@@ -11,4 +11,6 @@ Modules:
   oracle.chunk_spec -- fp64 chunked (matmul) form, used to pin chunk algebra
   oracle.frontend   -- fp64 front end: q/k L2 normalisation, gate and beta
                        from raw logits
+  oracle.variants   -- GDN (one decay per head) and DeltaNet (no decay) gates
+                       as per-channel KDA gates
 """

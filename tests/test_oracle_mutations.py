@@ -125,3 +125,40 @@ def test_a_front_end_pin_catches(name, tmp_path):
         except AssertionError:
             caught.append(check.__name__)
     assert caught, f"no front-end pin caught the planted mistake: {name}"
+
+
+# ------------------------------------------------------ gate variants
+import test_oracle_variants as var_pins  # noqa: E402
+
+VAR_SRC = os.path.join(os.path.dirname(SRC), "variants.py")
+
+VAR_MUTATIONS = {
+    "head gate ignored": ("return np.broadcast_to(np.asarray(g, dtype=np.float64)[..., None], shape).copy()",
+                          "return np.zeros(shape)"),
+    "head gate taken from the first head": (
+        "return np.broadcast_to(np.asarray(g, dtype=np.float64)[..., None], shape).copy()",
+        "return np.broadcast_to(np.asarray(g, dtype=np.float64)[..., :1, None], shape).copy()"),
+    "no gate decays at the floor": ("        return np.zeros(shape)\n    raise",
+                                    "        return np.full(shape, -0.6931471805599453)\n    raise"),
+    "head gate negated": ("return np.broadcast_to(np.asarray(g, dtype=np.float64)[..., None], shape).copy()",
+                          "return np.broadcast_to(-np.asarray(g, dtype=np.float64)[..., None], shape).copy()"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(VAR_MUTATIONS))
+def test_a_variant_pin_catches(name, tmp_path):
+    old, new = VAR_MUTATIONS[name]
+    src = open(VAR_SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    path = tmp_path / "variants_mut.py"
+    path.write_text(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location("variants_mut", str(path))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    caught = []
+    for check in var_pins.CHECKS:
+        try:
+            check(mod)
+        except AssertionError:
+            caught.append(check.__name__)
+    assert caught, f"no variant pin caught the planted mistake: {name}"
