@@ -95,7 +95,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first (the clocks take a few dozen calls to settle)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0 = auto)")
     ap.add_argument("--calibrate", type=int, default=0, metavar="MIB",
@@ -135,14 +136,24 @@ def main():
 
     # the same prefill from raw projections, with the fused front end
     rq, rk, rv, rg, rbeta, _, _ = make_inputs_device(T, H, D, seed=2, device=dev, raw=True)
-    fe = kda.Frontend(kda.FE_ALL, 1e-6)
+    fe = kda.Options(kda.FE_ALL, 1e-6)
 
     def fstep():
-        kda.prefill(rq, rk, rv, rg, rbeta, plan=plan, o=o, final_state=fin, frontend=fe)
+        kda.prefill(rq, rk, rv, rg, rbeta, plan=plan, o=o, final_state=fin, options=fe)
 
     _, fms = time_events(fstep, args.steps, args.warmup)
     f_ms = float(np.mean(fms))
     del rq, rk, rv, rg, rbeta
+
+    # the same prefill for Gated DeltaNet (one decay per token and head) and DeltaNet (no decay)
+    g_head = g[..., 0].contiguous()
+    vms = {}
+    for name, gate, gv in (("gdn", kda.GATE_HEAD, g_head), ("deltanet", kda.GATE_NONE, None)):
+        opt = kda.Options(gate=gate)
+        _, ts = time_events(lambda: kda.prefill(q, k, v, gv, beta, plan=plan, o=o, final_state=fin,
+                                                options=opt), args.steps, args.warmup)
+        vms[name] = float(np.mean(ts))
+    del g_head
 
     # decode: 256 sequences x 32 heads
     N = 256
@@ -204,6 +215,8 @@ def main():
         "prefill_front_end": {"workload": "the same prefill from raw q, k and gate/beta logits "
                                           "(L2 norm, -softplus gate, sigmoid beta fused into the prep kernel)",
                               "launch_ms": round(f_ms, 4), "tokens_per_s": round(T / (f_ms * 1e-3), 1)},
+        "prefill_variants": {"workload": "the same prefill for Gated DeltaNet (g [T, H]) and DeltaNet (no g)",
+                             "gdn_launch_ms": round(vms["gdn"], 4), "deltanet_launch_ms": round(vms["deltanet"], 4)},
         "decode": {"workload": "256 sequences x 32 heads, D=128, one token, fp32 states in place",
                    "ms": round(d_ms, 4), "head_tokens_per_s": round(N * H / (d_ms * 1e-3), 1),
                    "GBps": round(d_gbps, 1), "hbm_frac": round(d_gbps / HBM_PEAK_GBPS, 4),

@@ -37,12 +37,16 @@ static_assert(kda::kBlockTokens * -KDA_PREFILL_MIN_G_FLOOR * 1.4426950408889634f
               "decay span of a block");
 
 // Every tensor pointer must be 16-byte aligned (NULL passes).
-// Front-end descriptor: NULL or known flag bits with a usable epsilon.
-bool frontend_ok(const kda_frontend* fe) {
-  if (!fe) return true;
+// Options: NULL, or known flag bits, a known gate layout and a usable epsilon.
+bool options_ok(const kda_options* opt) {
+  if (!opt) return true;
   const uint32_t known = KDA_FE_L2NORM_QK | KDA_FE_GATE_LOGITS | KDA_FE_BETA_LOGITS;
-  return (fe->flags & ~known) == 0 && fe->norm_eps >= 0.f && fe->norm_eps <= FLT_MAX;
+  if (opt->flags & ~known) return false;
+  if (opt->gate != KDA_GATE_CHANNEL && opt->gate != KDA_GATE_HEAD && opt->gate != KDA_GATE_NONE) return false;
+  if (opt->gate == KDA_GATE_NONE && (opt->flags & KDA_FE_GATE_LOGITS)) return false;
+  return opt->norm_eps >= 0.f && opt->norm_eps <= FLT_MAX;
 }
+int32_t gate_of(const kda_options* opt) { return opt ? opt->gate : KDA_GATE_CHANNEL; }
 
 bool aligned16(std::initializer_list<const void*> ps) {
   for (const void* p : ps)
@@ -91,21 +95,22 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_
                                const float* initial_state, float* final_state,
                                int32_t ckpt_interval, float* checkpoints, void* o,
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return kda_prefill_chunked_fe(q, k, v, dtype, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H,
+  return kda_prefill_chunked_ex(q, k, v, dtype, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H,
                                 Dk, Dv, scale, g_min, initial_state, final_state, ckpt_interval,
                                 checkpoints, o, workspace, workspace_bytes, nullptr, stream);
 }
 
-kda_status kda_prefill_chunked_fe(const void* q, const void* k, const void* v, kda_dtype dtype,
+kda_status kda_prefill_chunked_ex(const void* q, const void* k, const void* v, kda_dtype dtype,
                                   const float* g, const float* beta, const int32_t* cu_seqlens,
                                   const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
                                   int32_t Dk, int32_t Dv, float scale, float g_min,
                                   const float* initial_state, float* final_state,
                                   int32_t ckpt_interval, float* checkpoints, void* o,
                                   void* workspace, size_t workspace_bytes,
-                                  const kda_frontend* fe, hipStream_t stream) {
+                                  const kda_options* opt, hipStream_t stream) {
   if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
-  if (!frontend_ok(fe)) return KDA_ERR_INVALID_ARG;
+  if (!options_ok(opt)) return KDA_ERR_INVALID_ARG;
+  const bool need_g = gate_of(opt) != KDA_GATE_NONE;
   if (!supported_dims(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
   int64_t tokens, blocks;
   if (H <= 0 || num_seqs < 0 || !cu_seqlens || !scan_lengths(cu_seqlens_host, num_seqs, &tokens, &blocks))
@@ -113,7 +118,7 @@ kda_status kda_prefill_chunked_fe(const void* q, const void* k, const void* v, k
   if (!(g_min >= kMinGateFloor && g_min <= 0.f)) return KDA_ERR_INVALID_ARG;
   if ((int64_t)num_seqs * H * (Dv / 16) > INT32_MAX || tokens * (int64_t)H > INT32_MAX)
     return KDA_ERR_INVALID_ARG;
-  if (tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARG;
+  if (tokens > 0 && (!q || !k || !v || (need_g && !g) || !beta || !o)) return KDA_ERR_INVALID_ARG;
   if (ckpt_interval < 0 || (ckpt_interval > 0 && ckpt_interval % KDA_CHUNK != 0))
     return KDA_ERR_INVALID_ARG;
   const int64_t nck = kda_prefill_num_checkpoints(cu_seqlens_host, num_seqs, ckpt_interval);
@@ -130,7 +135,8 @@ kda_status kda_prefill_chunked_fe(const void* q, const void* k, const void* v, k
   a.num_seqs = num_seqs; a.H = H; a.D = Dk;
   a.total_tokens = tokens; a.total_blocks = blocks;
   a.scale = scale; a.g_min = g_min;
-  a.fe_flags = fe ? fe->flags : 0u; a.fe_eps = fe ? fe->norm_eps : 0.f;
+  a.fe_flags = opt ? opt->flags : 0u; a.fe_eps = opt ? opt->norm_eps : 0.f;
+  a.gate = gate_of(opt);
   a.initial_state = initial_state; a.final_state = final_state;
   a.ckpt_interval = nck > 0 ? ckpt_interval : 0;
   a.checkpoints = checkpoints;
@@ -164,22 +170,24 @@ kda_status kda_decode_tokens(const void* q, const void* k, const void* v, kda_dt
                              const float* g, const float* beta, float* state,
                              const int32_t* accept, void* o, int32_t N, int32_t T, int32_t H,
                              int32_t Dk, int32_t Dv, float scale, float g_min,
-                             const kda_frontend* fe, hipStream_t stream) {
+                             const kda_options* opt, hipStream_t stream) {
   if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
-  if (!frontend_ok(fe)) return KDA_ERR_INVALID_ARG;
+  if (!options_ok(opt)) return KDA_ERR_INVALID_ARG;
+  const bool need_g = gate_of(opt) != KDA_GATE_NONE;
   if (!supported_dims(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
   if (T < 1 || T > KDA_DECODE_MAX_TOKENS) return KDA_ERR_INVALID_ARG;
   if (N < 0 || H <= 0 || (int64_t)N * H > INT32_MAX || (int64_t)N * T * H > INT32_MAX)
     return KDA_ERR_INVALID_ARG;
   if (N == 0) return KDA_OK;
-  if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
+  if (!q || !k || !v || (need_g && !g) || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
   if (!aligned16({q, k, v, g, beta, state, o})) return KDA_ERR_INVALID_ARG;
   kda::DecodeArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
   a.N = N; a.H = H; a.D = Dk;
   a.T = T; a.accept = accept;
   a.scale = scale; a.g_min = g_min;
-  a.fe_flags = fe ? fe->flags : 0u; a.fe_eps = fe ? fe->norm_eps : 0.f;
+  a.fe_flags = opt ? opt->flags : 0u; a.fe_eps = opt ? opt->norm_eps : 0.f;
+  a.gate = gate_of(opt);
   a.bf16 = dtype == KDA_BF16;
   a.stream = stream;
   return from_hip(kda::launch_decode(a));

@@ -41,18 +41,19 @@ namespace kda {
 // kOne fixes T = 1 at compile time (the plain decode step): the token loop then
 // vanishes and the kernel keeps the register footprint of a single step.
 //
-// kFE: the optional front end (flags as in kda.h). Gate and write logits are
-// turned into alpha and beta when staged. Raw q and k are not rescaled in
-// LDS: the same row pass also sums k.k and q.q, and the inverse norms rk, rq
-// scale the reduced results instead (u and the state update by rk, S'^T q by
-// rq, k.q by rk rq).
-template <int D, typename TIn, bool kOne, bool kFE>
+// kGeneral: the instantiation that takes the options of kda.h at run time.
+// The gate layout (per channel, per head, none) decides how alpha is staged.
+// With the front end, gate and write logits become alpha and beta when
+// staged. Raw q and k are not rescaled in LDS: the same row pass also sums
+// k.k and q.q, and the inverse norms rk, rq scale the reduced results instead
+// (u and the state update by rk, S'^T q by rq, k.q by rk rq).
+template <int D, typename TIn, bool kOne, bool kGeneral>
 __global__ __launch_bounds__(D == 128 ? 256 : 64) void decode_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
     TIn* __restrict__ o, int H, int T_arg, const int32_t* __restrict__ accept, float scale,
-    float g_min, uint32_t fe_flags, float fe_eps) {
-  static_assert(!(kOne && kFE), "the front end runs in the general kernel");
+    float g_min, uint32_t fe_flags, float fe_eps, int gate) {
+  static_assert(!(kOne && kGeneral), "options run in the general kernel");
   const int T = kOne ? 1 : T_arg;
   constexpr int kThreads = D == 128 ? 256 : 64;
   constexpr int kColGroups = D == 128 ? 8 : 4;         // float4 column groups per wave
@@ -94,10 +95,13 @@ __global__ __launch_bounds__(D == 128 ? 256 : 64) void decode_kernel(
     tk[j] = Elem<TIn>::load(k + off);
     tq[j] = Elem<TIn>::load(q + off);
     tv[j] = Elem<TIn>::load(v + off);
-    tg[j] = g[off];
+    // gate by layout: one unconditional load from a selected base and index
+    // (without a gate it reads beta, which always exists; the value is unused)
+    if (!kGeneral) tg[j] = g[off];
+    else tg[j] = (gate == KDA_GATE_NONE ? beta : g)[gate == KDA_GATE_CHANNEL ? off : row(e / D)];
   }
   const float tb = beta[row(min(tid, T - 1))];
-  const float alpha_min = kFE ? __builtin_amdgcn_exp2f(g_min * kLog2e) : 0.f;
+  const float alpha_min = kGeneral ? __builtin_amdgcn_exp2f(g_min * kLog2e) : 0.f;
   // State: plain float4 loads (measured faster here than non-temporal loads),
   // non-temporal stores at the end (faster than plain stores).
   float* S = state + (size_t)head * D * D;
@@ -113,15 +117,16 @@ __global__ __launch_bounds__(D == 128 ? 256 : 64) void decode_kernel(
       s_k[t][c] = tk[j];
       s_q[t][c] = tq[j];
       s_v[t][c] = tv[j];
-      s_a[t][c] = kFE && (fe_flags & KDA_FE_GATE_LOGITS) ? gate_alpha_logit(tg[j], alpha_min)
-                                                         : gate_alpha(tg[j], g_min);
+      s_a[t][c] = kGeneral && gate == KDA_GATE_NONE          ? 1.f
+                  : kGeneral && (fe_flags & KDA_FE_GATE_LOGITS) ? gate_alpha_logit(tg[j], alpha_min)
+                                                           : gate_alpha(tg[j], g_min);
     }
   }
-  if (tid < T) s_b[tid] = kFE && (fe_flags & KDA_FE_BETA_LOGITS) ? beta_logit(tb) : tb;
+  if (tid < T) s_b[tid] = kGeneral && (fe_flags & KDA_FE_BETA_LOGITS) ? beta_logit(tb) : tb;
   // LDS-only barrier: the state loads stay in flight across it.
   lds_barrier();
 
-  const bool norm = kFE && (fe_flags & KDA_FE_L2NORM_QK);
+  const bool norm = kGeneral && (fe_flags & KDA_FE_L2NORM_QK);
   for (int t = 0; t < T; ++t) {
     f32x4 u = {0.f, 0.f, 0.f, 0.f}, w = {0.f, 0.f, 0.f, 0.f};
     float kq = 0.f, kk = 0.f, qq = 0.f;
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(D == 128 ? 256 : 64) void decode_kernel(
       u += s[i] * kr;
       w += s[i] * qr;
       kq += kr * qr;
-      if constexpr (kFE) {
+      if constexpr (kGeneral) {
         kk += kr * kr;
         qq += qr * qr;
       }
@@ -146,21 +151,21 @@ __global__ __launch_bounds__(D == 128 ? 256 : 64) void decode_kernel(
         w[c] += __shfl_xor(w[c], m);
       }
       kq += __shfl_xor(kq, m);
-      if constexpr (kFE) {
+      if constexpr (kGeneral) {
         kk += __shfl_xor(kk, m);
         qq += __shfl_xor(qq, m);
       }
     }
     // inverse norms of this token's k and q rows (1 without the front end)
     const float rk = norm ? inv_norm(kk, fe_eps) : 1.f, rq = norm ? inv_norm(qq, fe_eps) : 1.f;
-    if constexpr (kFE) {
+    if constexpr (kGeneral) {
       u *= rk;
       w *= rq;
       kq *= rk * rq;
     }
     const f32x4 vv = *(const f32x4*)&s_v[t][col];
     const f32x4 d = s_b[t] * (vv - u);
-    const f32x4 dk = kFE ? d * rk : d;       // k_hat d^T = k (rk d)^T
+    const f32x4 dk = kGeneral ? d * rk : d;       // k_hat d^T = k (rk d)^T
 #pragma unroll
     for (int i = 0; i < kRowsPerLane; ++i) s[i] += s_k[t][rg + kRowGroups * i] * dk;
     if (t + 1 == commit) {
@@ -181,18 +186,19 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   const int threads = D == 128 ? 256 : 64;
   const unsigned blocks = (unsigned)((int64_t)a.N * a.H);
   const size_t lds = sizeof(float) * ((size_t)4 * a.T * D + a.T);
-  if (a.fe_flags)
+  if (a.fe_flags || a.gate != KDA_GATE_CHANNEL)
     hipLaunchKernelGGL((decode_kernel<D, TIn, false, true>), dim3(blocks), dim3(threads), lds, a.stream,
                        (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta, a.state,
-                       (TIn*)a.o, a.H, a.T, a.accept, a.scale, a.g_min, a.fe_flags, a.fe_eps);
+                       (TIn*)a.o, a.H, a.T, a.accept, a.scale, a.g_min, a.fe_flags, a.fe_eps,
+                       (int)a.gate);
   else if (a.T == 1 && !a.accept)
     hipLaunchKernelGGL((decode_kernel<D, TIn, true, false>), dim3(blocks), dim3(threads), lds, a.stream,
                        (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta, a.state,
-                       (TIn*)a.o, a.H, 1, nullptr, a.scale, a.g_min, 0u, 0.f);
+                       (TIn*)a.o, a.H, 1, nullptr, a.scale, a.g_min, 0u, 0.f, (int)KDA_GATE_CHANNEL);
   else
     hipLaunchKernelGGL((decode_kernel<D, TIn, false, false>), dim3(blocks), dim3(threads), lds, a.stream,
                        (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, a.g, a.beta, a.state,
-                       (TIn*)a.o, a.H, a.T, a.accept, a.scale, a.g_min, 0u, 0.f);
+                       (TIn*)a.o, a.H, a.T, a.accept, a.scale, a.g_min, 0u, 0.f, (int)KDA_GATE_CHANNEL);
   return hipGetLastError();
 }
 

@@ -26,6 +26,7 @@ struct DecodeArgs {
   float scale, g_min;
   uint32_t fe_flags = 0;      // KDA_FE_* (0: inputs used as given)
   float fe_eps = 0.f;
+  int32_t gate = KDA_GATE_CHANNEL;  // layout of g (kda_gate)
   bool bf16;
   hipStream_t stream;
 };
@@ -40,6 +41,7 @@ struct PrefillArgs {
   float scale, g_min;
   uint32_t fe_flags = 0;      // KDA_FE_* (0: inputs used as given)
   float fe_eps = 0.f;
+  int32_t gate = KDA_GATE_CHANNEL;  // layout of g (kda_gate)
   const float* initial_state;
   float* final_state;
   int32_t ckpt_interval;

@@ -172,14 +172,17 @@ template <int D>
 constexpr int prep_threads() { return D >= 128 ? D : 64; }
 
 //
-// kFE: the optional front end (flags as in kda.h). Raw q and k rows are scaled
-// by their inverse L2 norms (phase 0 computes them per token), and g and beta
+// kGeneral: the instantiation that takes the options of kda.h at run time.
+// The gate layout: per channel (KDA), one per token and head (Gated DeltaNet)
+// or none (DeltaNet). The optional front end: raw q and k rows are scaled by
+// their inverse L2 norms (phase 0 computes them per token), and g and beta
 // may be logits: alpha = max(1 / (1 + e^a), e^{g_min}), beta = sigmoid(b).
-template <int D, typename TIn, bool kFE>
+// The plain KDA call uses kGeneral = false, which has none of this code.
+template <int D, typename TIn, bool kGeneral>
 __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const int2* __restrict__ blk_info, int H, float g_min,
-    uint32_t fe_flags, float fe_eps, char* __restrict__ records) {
+    uint32_t fe_flags, float fe_eps, int gate, char* __restrict__ records) {
   using R = Rec<D>;
   constexpr int kThreads = prep_threads<D>();
   constexpr int kWaves = kThreads / kWave;
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
   float(*sM)[20] = (float(*)[20])(lds_raw + (kBT * (kBT + 4) + 16 * 20) * 4);      // A_ba T_aa
   __shared__ __attribute__((aligned(16))) float sA[kBT][kBT + 4];
   __shared__ float sBeta[kBT];
-  __shared__ float sRk[kFE ? kBT : 1], sRq[kFE ? kBT : 1];   // inverse row norms of k and q
+  __shared__ float sRk[kGeneral ? kBT : 1], sRq[kGeneral ? kBT : 1];   // inverse row norms of k and q
 
   // Heads vary fastest across consecutive workgroups: the H heads of one token
   // row are contiguous in q, k, v and g, so neighbouring workgroups read
@@ -210,51 +213,66 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
 
   if (tid < kBT) {
     float b = beta[(size_t)(tok0 + min(tid, cnt - 1)) * H + h];
-    if (kFE && (fe_flags & KDA_FE_BETA_LOGITS)) b = beta_logit(b);
+    if (kGeneral && (fe_flags & KDA_FE_BETA_LOGITS)) b = beta_logit(b);
     sBeta[tid] = tid < cnt ? b : 0.f;
   }
-  const float alpha_min = kFE ? __builtin_amdgcn_exp2f(g_min * kLog2e) : 0.f;
+  const float alpha_min = kGeneral ? __builtin_amdgcn_exp2f(g_min * kLog2e) : 0.f;
   auto alpha_of = [&](float x) __attribute__((always_inline)) {
-    return kFE && (fe_flags & KDA_FE_GATE_LOGITS) ? gate_alpha_logit(x, alpha_min) : gate_alpha(x, g_min);
+    if (kGeneral && gate == KDA_GATE_NONE) return 1.f;
+    return kGeneral && (fe_flags & KDA_FE_GATE_LOGITS) ? gate_alpha_logit(x, alpha_min) : gate_alpha(x, g_min);
+  };
+  // g of token tc (< cnt) and channel ch, by the gate layout. One
+  // unconditional load from a selected base and index (a load under a branch
+  // would wait for each load in turn); without a gate it reads beta, which
+  // always exists, and the value is not used.
+  const float* gsrc = !kGeneral || gate != KDA_GATE_NONE ? g : beta;
+  auto g_at = [&](int tc, int ch) __attribute__((always_inline)) {
+    if (!kGeneral) return g[row(tc) + ch];
+    const size_t i = gate == KDA_GATE_CHANNEL ? row(tc) + ch : (size_t)(tok0 + tc) * H + h;
+    return gsrc[i];
   };
 
   // ---- phase 0 (front end only): inverse L2 norms of the 32 k and q rows.
   // kThreads / 32 lanes per token, each summing D / (kThreads / 32) channels
   // of both rows, then a butterfly over those lanes.
-  if constexpr (kFE) {
+  if constexpr (kGeneral) {
     constexpr int kLanesPerTok = kThreads / kBT;
     constexpr int kChPerLane = D / kLanesPerTok;
     static_assert(kChPerLane % 4 == 0 && (kLanesPerTok & (kLanesPerTok - 1)) == 0, "phase 0 split");
     const int t = tid / kLanesPerTok, part = tid % kLanesPerTok;
-    const size_t off = row(min(t, cnt - 1)) + part * kChPerLane;
-    float sk = 0.f, sq = 0.f;
+    float rk_t = 1.f, rq_t = 1.f;
+    if (fe_flags & KDA_FE_L2NORM_QK) {
+      const size_t off = row(min(t, cnt - 1)) + part * kChPerLane;
+      float sk = 0.f, sq = 0.f;
 #pragma unroll
-    for (int c = 0; c < kChPerLane; c += 4) {
-      f32x4 xk, xq;
-      if constexpr (sizeof(TIn) == 2) {
-        xk = from_bf16x4(*(const bf16x4*)(k + off + c));
-        xq = from_bf16x4(*(const bf16x4*)(q + off + c));
-      } else {
-        xk = *(const f32x4*)(k + off + c);
-        xq = *(const f32x4*)(q + off + c);
+      for (int c = 0; c < kChPerLane; c += 4) {
+        f32x4 xk, xq;
+        if constexpr (sizeof(TIn) == 2) {
+          xk = from_bf16x4(*(const bf16x4*)(k + off + c));
+          xq = from_bf16x4(*(const bf16x4*)(q + off + c));
+        } else {
+          xk = *(const f32x4*)(k + off + c);
+          xq = *(const f32x4*)(q + off + c);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { sk += xk[i] * xk[i]; sq += xq[i] * xq[i]; }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { sk += xk[i] * xk[i]; sq += xq[i] * xq[i]; }
-    }
-#pragma unroll
-    for (int m = 1; m < kLanesPerTok; m <<= 1) {
-      sk += __shfl_xor(sk, m);
-      sq += __shfl_xor(sq, m);
+      for (int m = 1; m < kLanesPerTok; m <<= 1) {
+        sk += __shfl_xor(sk, m);
+        sq += __shfl_xor(sq, m);
+      }
+      rk_t = inv_norm(sk, fe_eps);
+      rq_t = inv_norm(sq, fe_eps);
     }
     if (part == 0) {
-      const bool norm = fe_flags & KDA_FE_L2NORM_QK;
-      sRk[t] = norm ? inv_norm(sk, fe_eps) : 1.f;
-      sRq[t] = norm ? inv_norm(sq, fe_eps) : 1.f;
+      sRk[t] = rk_t;
+      sRq[t] = rq_t;
     }
     __syncthreads();
   }
-  auto rk = [&](int t) __attribute__((always_inline)) { return kFE ? sRk[t] : 1.f; };
-  auto rq = [&](int t) __attribute__((always_inline)) { return kFE ? sRq[t] : 1.f; };
+  auto rk = [&](int t) __attribute__((always_inline)) { return kGeneral ? sRk[t] : 1.f; };
+  auto rq = [&](int t) __attribute__((always_inline)) { return kGeneral ? sRq[t] : 1.f; };
 
   // ---- phase 1: one channel per thread (coalesced rows). Rows past the end
   // of the sequence give alpha = 1 and k = 0. Every load reads a valid row
@@ -266,7 +284,7 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
 #pragma unroll
     for (int t = 0; t < kBT; ++t) {
       const int tc = min(t, cnt - 1);
-      a[t] = g[row(tc) + ch];
+      a[t] = g_at(tc, ch);
       kf[t] = Elem<TIn>::load(k + row(tc) + ch);
     }
 #pragma unroll
@@ -493,7 +511,12 @@ struct ChainCfg {
   static_assert(kInFlight * kPerLoader < 64, "vmcnt field");
 };
 
-template <int D, typename TIn>
+// kSplitS: K~+ S takes the state as a bf16 hi/lo pair (two MFMAs per tile)
+// instead of one bf16 value. Used without a decay (DeltaNet): K~+ is then
+// exactly the bf16 key, nothing forgets the state, and K~+ S nearly cancels V,
+// so the state's bf16 rounding dominates the error of V - K~+ S (measured: final
+// states about 1.5e-3 relative with one bf16 term, at every length).
+template <int D, typename TIn, bool kSplitS>
 __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     const TIn* __restrict__ v, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ seq_blk_off, const int32_t* __restrict__ seq_ck_off,
@@ -708,19 +731,25 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     // and goes to LDS for the partner, (Q~ S)^T goes to LDS for the output wave
     f32x4 u_own[2];
     auto partials = [&](int c) __attribute__((always_inline)) {
-      f32x4 U[2] = {z, z}, P[2] = {z, z};
+      f32x4 U[2] = {z, z}, P[2] = {z, z}, UL[2] = {z, z};
 #pragma unroll
       for (int qq = 0; qq < PW; ++qq) {
         const bf16x4 zero = {};
-        const bf16x8 Bs = cat(to_bf16x4(acc[2 * qq]), 2 * qq + 1 < TW ? to_bf16x4(acc[2 * qq + 1]) : zero);
+        const bool two = 2 * qq + 1 < TW;
+        bf16x4 h0, l0, h1 = zero, l1 = zero;
+        split_bf16(acc[2 * qq], h0, l0);
+        if (two) split_bf16(acc[2 * qq + 1], h1, l1);
+        const bf16x8 Bs = cat(h0, h1);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           U[u] = mfma32(kp[u][qq], Bs, U[u]);
           P[u] = mfma32(Bs, qt[u][qq], P[u]);
+          if constexpr (kSplitS) UL[u] = mfma32(kp[u][qq], cat(l0, l1), UL[u]);
         }
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
+        if constexpr (kSplitS) U[u] += UL[u];
         u_own[u] = U[u];
         if (NCW > 1) xbuf[c % 2][hf][0][u][lane] = U[u];
         xbuf[c % 2][hf][1][u][lane] = P[u];
@@ -839,20 +868,23 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.total_blocks > 0) {
-    if (a.fe_flags)
+    if (a.fe_flags || a.gate != KDA_GATE_CHANNEL)
       hipLaunchKernelGGL((prep_kernel<D, TIn, true>), dim3((unsigned)a.H, (unsigned)a.total_blocks),
                          dim3(prep_threads<D>()), 0, a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g,
-                         a.beta, (const int2*)blk_info, a.H, a.g_min, a.fe_flags, a.fe_eps, records);
+                         a.beta, (const int2*)blk_info, a.H, a.g_min, a.fe_flags, a.fe_eps, (int)a.gate,
+                         records);
     else
       hipLaunchKernelGGL((prep_kernel<D, TIn, false>), dim3((unsigned)a.H, (unsigned)a.total_blocks),
                          dim3(prep_threads<D>()), 0, a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g,
-                         a.beta, (const int2*)blk_info, a.H, a.g_min, 0u, 0.f, records);
+                         a.beta, (const int2*)blk_info, a.H, a.g_min, 0u, 0.f, (int)KDA_GATE_CHANNEL,
+                         records);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   using Cfg = ChainCfg<D, TIn>;
   const unsigned blocks = (unsigned)((int64_t)a.num_seqs * a.H * (D / 16));   // one per 16-column slice
-  hipLaunchKernelGGL((chain_kernel<D, TIn>), dim3(blocks), dim3(Cfg::kThreads), 0, a.stream, (const TIn*)a.v,
+  auto chain = a.gate == KDA_GATE_NONE ? chain_kernel<D, TIn, true> : chain_kernel<D, TIn, false>;
+  hipLaunchKernelGGL(chain, dim3(blocks), dim3(Cfg::kThreads), 0, a.stream, (const TIn*)a.v,
                      a.cu_seqlens, seq_blk_off, seq_ck_off, records, a.initial_state,
                      a.final_state, a.checkpoints, (TIn*)a.o, a.num_seqs, a.H, a.ckpt_interval,
                      a.scale, (int)a.total_blocks);

@@ -23,18 +23,21 @@ CHUNK = 16
 LN_HALF = math.log(0.5)
 
 EXPORTED = ("kda_status_string", "kda_prefill_num_checkpoints", "kda_prefill_workspace_size",
-            "kda_prefill_chunked", "kda_prefill_chunked_fe", "kda_decode_step", "kda_decode_tokens")
+            "kda_prefill_chunked", "kda_prefill_chunked_ex", "kda_decode_step", "kda_decode_tokens")
 DECODE_MAX_TOKENS = 16
 FE_L2NORM_QK, FE_GATE_LOGITS, FE_BETA_LOGITS = 1, 2, 4
 FE_ALL = FE_L2NORM_QK | FE_GATE_LOGITS | FE_BETA_LOGITS
+GATE_CHANNEL, GATE_HEAD, GATE_NONE = 0, 1, 2     # KDA, Gated DeltaNet, DeltaNet
 
 
-class Frontend(ctypes.Structure):
-    """kda_frontend: which inputs are raw (FE_* flags) and the norm epsilon."""
-    _fields_ = [("flags", ctypes.c_uint32), ("norm_eps", ctypes.c_float)]
+class Options(ctypes.Structure):
+    """kda_options: which inputs are raw (FE_* flags), the norm epsilon, and
+    the gate layout (GATE_CHANNEL: g [.., H, D]; GATE_HEAD: g [.., H];
+    GATE_NONE: no g)."""
+    _fields_ = [("flags", ctypes.c_uint32), ("norm_eps", ctypes.c_float), ("gate", ctypes.c_int32)]
 
-    def __init__(self, flags=FE_ALL, norm_eps=1e-6):
-        super().__init__(int(flags), float(norm_eps))
+    def __init__(self, flags=0, norm_eps=1e-6, gate=GATE_CHANNEL):
+        super().__init__(int(flags), float(norm_eps), int(gate))
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -71,10 +74,10 @@ def lib():
         L.kda_decode_tokens.restype = ctypes.c_int
         L.kda_decode_tokens.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _i32,
                                         _i32, _i32, _i32, _i32, ctypes.c_float, ctypes.c_float,
-                                        ctypes.POINTER(Frontend), _vp]
-        L.kda_prefill_chunked_fe.restype = ctypes.c_int
-        L.kda_prefill_chunked_fe.argtypes = L.kda_prefill_chunked.argtypes[:-1] + [
-            ctypes.POINTER(Frontend), _vp]
+                                        ctypes.POINTER(Options), _vp]
+        L.kda_prefill_chunked_ex.restype = ctypes.c_int
+        L.kda_prefill_chunked_ex.argtypes = L.kda_prefill_chunked.argtypes[:-1] + [
+            ctypes.POINTER(Options), _vp]
         _lib = L
     return _lib
 
@@ -138,15 +141,16 @@ def make_plan(cu_seqlens, H: int, D: int, device, ckpt_interval: int = 0) -> Pre
                        int(ckpt_interval))
 
 
-def _fe_ptr(frontend: Optional[Frontend]):
-    return None if frontend is None else ctypes.byref(frontend)
+def _opt_ptr(options: Optional[Options]):
+    return None if options is None else ctypes.byref(options)
 
 
 def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, scale=1.0, g_min=LN_HALF,
             ckpt_interval=0, out_final_state=True, plan: Optional[PrefillPlan] = None,
-            o=None, final_state=None, checkpoints=None, frontend: Optional[Frontend] = None):
-    """kda_prefill_chunked on packed [T, H, D] tensors (kda_prefill_chunked_fe
-    when a Frontend is given: q, k, g and beta are then raw as its flags say).
+            o=None, final_state=None, checkpoints=None, options: Optional[Options] = None):
+    """kda_prefill_chunked on packed [T, H, D] tensors (kda_prefill_chunked_ex
+    when Options are given: gate layout, and q, k, g, beta raw as the flags
+    say).
 
     Returns (o, final_state or None, checkpoints or None)."""
     T, H, D = q.shape
@@ -164,10 +168,10 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, scale=1.0, g_
             plan.cu_host.numpy().ctypes.data_as(_i32p), N, H, D, v.shape[2], float(scale),
             float(g_min), _ptr(initial_state), _ptr(final_state), plan.ckpt_interval,
             _ptr(checkpoints), _ptr(o), _ptr(plan.workspace), plan.workspace.numel())
-    if frontend is None:
+    if options is None:
         st = lib().kda_prefill_chunked(*args, _stream(q.device))
     else:
-        st = lib().kda_prefill_chunked_fe(*args, _fe_ptr(frontend), _stream(q.device))
+        st = lib().kda_prefill_chunked_ex(*args, _opt_ptr(options), _stream(q.device))
     if st != KDA_OK:
         raise KdaError(st, "kda_prefill_chunked")
     return o, final_state, checkpoints
@@ -189,10 +193,10 @@ def decode_step(q, k, v, g, beta, state, scale=1.0, g_min=LN_HALF, o=None):
 
 
 def decode_tokens(q, k, v, g, beta, state, accept=None, scale=1.0, g_min=LN_HALF, o=None,
-                  frontend: Optional[Frontend] = None):
+                  options: Optional[Options] = None):
     """kda_decode_tokens: q,k,g,v [N,T,H,D]; beta [N,T,H]; state [N,H,D,D]
     updated in place to the state after accept[n] tokens (all T when accept is
-    None); accept is a device int32 [N] tensor; frontend as in prefill.
+    None); accept is a device int32 [N] tensor; options as in prefill.
     Returns o [N,T,H,D]."""
     N, T, H, D = q.shape
     _check_dev(q, k, v, g, beta, state, accept)
@@ -202,7 +206,7 @@ def decode_tokens(q, k, v, g, beta, state, accept=None, scale=1.0, g_min=LN_HALF
         o = torch.empty_like(v)
     st = lib().kda_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta),
                                  _ptr(state), _ptr(accept), _ptr(o), N, T, H, D, v.shape[3],
-                                 float(scale), float(g_min), _fe_ptr(frontend), _stream(q.device))
+                                 float(scale), float(g_min), _opt_ptr(options), _stream(q.device))
     if st != KDA_OK:
         raise KdaError(st, "kda_decode_tokens")
     return o

@@ -34,7 +34,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # the kernels of one plain kda_prefill_chunked call on the benchmarked shape
 # (D = 128, bf16 q/k/v, no front end)
 PREFILL_KERNELS = ("kda::plan_kernel", "kda::prep_kernel<128, unsigned short, false>",
-                   "kda::chain_kernel<128, unsigned short>")
+                   "kda::chain_kernel<128, unsigned short, false>")
 CALIB_KERNEL = "AbsFunctor"
 
 

@@ -72,9 +72,24 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
  * the fp32 / bf16 range. ln 0.5 (the configurations here) is far above it. */
 #define KDA_PREFILL_MIN_G_FLOOR (-2.5f)
 
-/* Optional front end: the step just before the recurrence, fused into the
- * kernels that first read q, k, g and beta, so that no separate pass over
- * them is needed. Each flag replaces one input convention:
+/* Options of the extended entry points (kda_prefill_chunked_ex,
+ * kda_decode_tokens). A NULL pointer means all defaults: the KDA gate and no
+ * front end.
+ *
+ * gate: layout of g, i.e. which member of the delta-rule family runs
+ * ([K3-SA] Background: DeltaNet is the delta rule; Gated DeltaNet adds one
+ * LSTM-style forget gate; KDA turns that gate into a diagonal, one decay per
+ * key channel):
+ *   KDA_GATE_CHANNEL  g [.., H, Dk]: one log-decay per key channel (KDA)
+ *   KDA_GATE_HEAD     g [.., H]: one log-decay per token and head (Gated
+ *                     DeltaNet); S' = alpha S. The floor applies as for KDA.
+ *   KDA_GATE_NONE     no decay (DeltaNet); g is not read and may be NULL.
+ * A scalar decay commutes with the erase step, so GDN is exactly KDA with
+ * every channel given the same log-decay, and DeltaNet is KDA with g = 0.
+ *
+ * flags: the optional front end, the step just before the recurrence, fused
+ * into the kernels that first read q, k, g and beta (no separate pass over
+ * them). Each flag replaces one input convention:
  *   KDA_FE_L2NORM_QK   q and k are raw; each (token, head) row x is used as
  *                      x / sqrt(sum_i x_i^2 + norm_eps), computed in fp32
  *                      (the operator's inputs are unit-norm keys and queries;
@@ -83,17 +98,20 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
  *   KDA_FE_GATE_LOGITS g holds raw gate logits a; the log-decay is
  *                      g = -softplus(a) = -ln(1 + e^a), then floored at g_min
  *                      as always ([K3-DD] 4-1 KDA, first bullet: a lower
- *                      bound on each key channel's decay)
+ *                      bound on each key channel's decay). Invalid with
+ *                      KDA_GATE_NONE.
  *   KDA_FE_BETA_LOGITS beta holds raw logits b; the write strength is
  *                      sigmoid(b) = 1 / (1 + e^-b)
- * A NULL descriptor, or flags = 0, means the inputs are used as given. */
+ */
 #define KDA_FE_L2NORM_QK 1u
 #define KDA_FE_GATE_LOGITS 2u
 #define KDA_FE_BETA_LOGITS 4u
+typedef enum { KDA_GATE_CHANNEL = 0, KDA_GATE_HEAD = 1, KDA_GATE_NONE = 2 } kda_gate;
 typedef struct {
-  uint32_t flags;   /* OR of KDA_FE_* ; other bits are invalid */
+  uint32_t flags;   /* OR of KDA_FE_*; other bits are invalid */
   float norm_eps;   /* >= 0 and finite; used only with KDA_FE_L2NORM_QK */
-} kda_frontend;
+  int32_t gate;     /* a kda_gate value */
+} kda_options;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* kda_status_string(kda_status status);
@@ -155,19 +173,22 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_
                                int32_t ckpt_interval, float* checkpoints, void* o,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* kda_prefill_chunked with the optional front end `fe` (see kda_frontend):
- * q, k, g and beta may be raw (unnormalised keys and queries, gate and write
- * logits). Same arguments, layouts, outputs and errors otherwise, plus
- * KDA_ERR_INVALID_ARG for unknown flag bits or a negative or non-finite
- * norm_eps. fe = NULL is exactly kda_prefill_chunked. */
-kda_status kda_prefill_chunked_fe(const void* q, const void* k, const void* v, kda_dtype dtype,
+/* kda_prefill_chunked with options `opt` (see kda_options): the gate layout
+ * (KDA, Gated DeltaNet or DeltaNet) and the optional front end (q, k, g and
+ * beta may be raw: unnormalised keys and queries, gate and write logits).
+ * g is [T, H, Dk], [T, H] or unused (may be NULL) by opt->gate. Same
+ * arguments, layouts, outputs and errors otherwise, plus KDA_ERR_INVALID_ARG
+ * for unknown flag bits, an unknown gate, KDA_FE_GATE_LOGITS with
+ * KDA_GATE_NONE, or a negative or non-finite norm_eps. opt = NULL is exactly
+ * kda_prefill_chunked. */
+kda_status kda_prefill_chunked_ex(const void* q, const void* k, const void* v, kda_dtype dtype,
                                   const float* g, const float* beta, const int32_t* cu_seqlens,
                                   const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
                                   int32_t Dk, int32_t Dv, float scale, float g_min,
                                   const float* initial_state, float* final_state,
                                   int32_t ckpt_interval, float* checkpoints, void* o,
                                   void* workspace, size_t workspace_bytes,
-                                  const kda_frontend* fe, hipStream_t stream);
+                                  const kda_options* opt, hipStream_t stream);
 
 /* One recurrent decode step for N independent sequences ([K3-SA] Methods 1)
  * FlashKDA, first bullet: decode runs the state update directly; about 7 D^2
@@ -194,7 +215,8 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
  * many tokens the call holds.
  *   q, k   [N, T, H, Dk] dtype (token t of sequence n is row n*T + t)
  *   v      [N, T, H, Dv] dtype
- *   g      [N, T, H, Dk] fp32 log-decay (clamped to [g_min, 0])
+ *   g      [N, T, H, Dk] fp32 log-decay (clamped to [g_min, 0]); [N, T, H]
+ *          with KDA_GATE_HEAD; unused (may be NULL) with KDA_GATE_NONE
  *   beta   [N, T, H] fp32
  *   state  [N, H, Dk, Dv] fp32, read, and updated IN PLACE to the state after
  *          the first accept[n] tokens of sequence n
@@ -204,15 +226,16 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
  *          prefix length a_n is known a second call with accept = a_n on the
  *          same inputs commits exactly that prefix.
  *   o      [N, T, H, Dv] dtype, output of every token whatever accept holds
- *   fe     optional front end (see kda_frontend), or NULL
+ *   opt    gate layout and front end (see kda_options), or NULL for the
+ *          KDA gate with inputs used as given
  * Errors: KDA_ERR_INVALID_ARG (null required pointer, T outside
- * [1, KDA_DECODE_MAX_TOKENS], negative N, H <= 0, bad front-end flags or
- * norm_eps), KDA_ERR_UNSUPPORTED, KDA_ERR_HIP. */
+ * [1, KDA_DECODE_MAX_TOKENS], negative N, H <= 0, bad options),
+ * KDA_ERR_UNSUPPORTED, KDA_ERR_HIP. */
 kda_status kda_decode_tokens(const void* q, const void* k, const void* v, kda_dtype dtype,
                              const float* g, const float* beta, float* state,
                              const int32_t* accept, void* o, int32_t N, int32_t T, int32_t H,
                              int32_t Dk, int32_t Dv, float scale, float g_min,
-                             const kda_frontend* fe, hipStream_t stream);
+                             const kda_options* opt, hipStream_t stream);
 
 #ifdef __cplusplus
 }

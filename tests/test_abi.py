@@ -138,10 +138,17 @@ def test_decode_tokens_argument_errors(L):
     assert call(o=None) == kda.KDA_ERR_INVALID_ARG
     assert call(beta=ctypes.c_void_p(0x1002)) == kda.KDA_ERR_INVALID_ARG
     assert call(N=0) == kda.KDA_OK
-    for bad in (kda.Frontend(8), kda.Frontend(kda.FE_ALL, -1.0), kda.Frontend(1, float("nan")),
-                kda.Frontend(1, float("inf"))):
+    for bad in (kda.Options(8), kda.Options(kda.FE_ALL, -1.0), kda.Options(1, float("nan")),
+                kda.Options(1, float("inf"))):
         assert call(fe=ctypes.byref(bad)) == kda.KDA_ERR_INVALID_ARG
-    assert call(fe=ctypes.byref(kda.Frontend(kda.FE_ALL, 0.0)), N=0) == kda.KDA_OK
+    assert call(fe=ctypes.byref(kda.Options(kda.FE_ALL, 0.0)), N=0) == kda.KDA_OK
+    # gate layouts: unknown values and gate logits without a gate are rejected;
+    # g may be NULL only without a gate
+    assert call(fe=ctypes.byref(kda.Options(gate=3))) == kda.KDA_ERR_INVALID_ARG
+    assert call(fe=ctypes.byref(kda.Options(kda.FE_GATE_LOGITS, gate=kda.GATE_NONE))) == kda.KDA_ERR_INVALID_ARG
+    assert call(g=None) == kda.KDA_ERR_INVALID_ARG
+    assert call(g=None, fe=ctypes.byref(kda.Options(gate=kda.GATE_HEAD))) == kda.KDA_ERR_INVALID_ARG
+    assert call(g=None, fe=ctypes.byref(kda.Options(gate=kda.GATE_NONE)), N=0) == kda.KDA_OK
 
 
 def test_decode_max_tokens_matches_header():
@@ -149,8 +156,8 @@ def test_decode_max_tokens_matches_header():
     assert m and int(m.group(1)) == kda.DECODE_MAX_TOKENS
 
 
-def test_prefill_front_end_argument_errors(L):
-    """kda_prefill_chunked_fe validates the descriptor first; with fe = NULL
+def test_prefill_options_argument_errors(L):
+    """kda_prefill_chunked_ex validates the options first; with opt = NULL
     it returns what kda_prefill_chunked returns."""
     fake = ctypes.c_void_p(0x1000)
     cu = (ctypes.c_int32 * 2)(0, 64)
@@ -162,10 +169,14 @@ def test_prefill_front_end_argument_errors(L):
                  scale=1.0, g_min=-0.69, s0=None, fin=None, ck_int=0, ck=None, o=fake, ws=ws,
                  ws_bytes=0, fe=fe, stream=None)
         a.update(over)
-        return L.kda_prefill_chunked_fe(*a.values())
-    for bad in (kda.Frontend(16), kda.Frontend(kda.FE_L2NORM_QK, -0.5), kda.Frontend(2, float("nan"))):
+        return L.kda_prefill_chunked_ex(*a.values())
+    for bad in (kda.Options(16), kda.Options(kda.FE_L2NORM_QK, -0.5), kda.Options(2, float("nan")),
+                kda.Options(gate=-1), kda.Options(kda.FE_GATE_LOGITS, gate=kda.GATE_NONE)):
         assert call(ctypes.byref(bad)) == kda.KDA_ERR_INVALID_ARG
+    assert call(None, g=None) == kda.KDA_ERR_INVALID_ARG
+    # no gate: g may be NULL (the next failing check is the workspace)
+    assert call(ctypes.byref(kda.Options(gate=kda.GATE_NONE)), g=None) == kda.KDA_ERR_WORKSPACE
     # valid descriptor: the next check that fails is the workspace size
-    assert call(ctypes.byref(kda.Frontend(kda.FE_ALL, 1e-6))) == kda.KDA_ERR_WORKSPACE
+    assert call(ctypes.byref(kda.Options(kda.FE_ALL, 1e-6))) == kda.KDA_ERR_WORKSPACE
     assert call(None) == kda.KDA_ERR_WORKSPACE
     assert call(None, Dk=64, Dv=64) == kda.KDA_ERR_UNSUPPORTED

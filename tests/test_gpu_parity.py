@@ -419,7 +419,7 @@ def test_prefill_front_end_all_flags(D, bf16):
     o, fin, ck = kda.prefill(to_dev(raw.q, dt), to_dev(raw.k, dt), to_dev(raw.v, dt), to_dev(raw.g),
                              to_dev(raw.beta), cu_seqlens=raw.cu_seqlens,
                              initial_state=to_dev(raw.initial_state), ckpt_interval=32,
-                             frontend=kda.Frontend(kda.FE_ALL, FE_EPS))
+                             options=kda.Options(kda.FE_ALL, FE_EPS))
     torch.cuda.synchronize()
     o_ref, f_ref, ck_ref = _fe_oracle_prefill(raw.q, raw.k, raw.v, raw.g, raw.beta, raw.cu_seqlens,
                                               raw.initial_state, fe_oracle.L2NORM_QK | fe_oracle.GATE_LOGITS
@@ -443,7 +443,7 @@ def test_prefill_front_end_one_flag(flag):
     beta = raw.beta if flag == 4 else prep.beta
     o, fin, _ = kda.prefill(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16), to_dev(prep.v, torch.bfloat16),
                             to_dev(g), to_dev(beta), cu_seqlens=prep.cu_seqlens,
-                            frontend=kda.Frontend(flag, FE_EPS))
+                            options=kda.Options(flag, FE_EPS))
     torch.cuda.synchronize()
     o_ref, f_ref, _ = _fe_oracle_prefill(q, k, prep.v, g, beta, prep.cu_seqlens, None, flag)
     check_outputs(o.float().cpu().numpy(), o_ref, prep.cu_seqlens, H)
@@ -459,7 +459,7 @@ def test_prefill_front_end_no_flags_is_plain_prefill():
     o2, f2, _ = kda.prefill(to_dev(inp.q, torch.bfloat16), to_dev(inp.k, torch.bfloat16),
                             to_dev(inp.v, torch.bfloat16), to_dev(inp.g), to_dev(inp.beta),
                             cu_seqlens=inp.cu_seqlens, initial_state=to_dev(inp.initial_state),
-                            frontend=kda.Frontend(0, 0.0))
+                            options=kda.Options(0, 0.0))
     torch.cuda.synchronize()
     assert np.array_equal(o1, o2.float().cpu().numpy()) and np.array_equal(f1, f2.cpu().numpy())
 
@@ -469,7 +469,7 @@ def test_prefill_front_end_full_size_sampled_heads():
     T, H, D = 8192, 32, 128
     print("case: front end full size", flush=True)
     q, k, v, g, beta, cu, _ = make_inputs_device(T, H, D, seed=12, device=DEV, raw=True)
-    o, fin, _ = kda.prefill(q, k, v, g, beta, cu_seqlens=cu, frontend=kda.Frontend(kda.FE_ALL, FE_EPS))
+    o, fin, _ = kda.prefill(q, k, v, g, beta, cu_seqlens=cu, options=kda.Options(kda.FE_ALL, FE_EPS))
     torch.cuda.synchronize()
     heads = [0, 31]
     sel = lambda t: t[:, heads].float().cpu().numpy()
@@ -494,7 +494,7 @@ def test_decode_tokens_front_end(D, T):
     acc = torch.tensor(accept, dtype=torch.int32, device=DEV)
     o = kda.decode_tokens(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16), to_dev(v, torch.bfloat16),
                           to_dev(g), to_dev(beta), state, accept=acc, scale=0.5,
-                          frontend=kda.Frontend(kda.FE_ALL, FE_EPS))
+                          options=kda.Options(kda.FE_ALL, FE_EPS))
     torch.cuda.synchronize()
     o = o.float().cpu().numpy()
     S = state.cpu().numpy()
@@ -511,3 +511,108 @@ def test_decode_tokens_front_end(D, T):
     for n in range(N):
         if accept[n] == 0:
             assert np.array_equal(S[n], raw.initial_state[n])
+
+
+# ------------------------------------------- gate variants: GDN, DeltaNet
+from oracle import variants as var_oracle  # noqa: E402
+
+
+def _variant_gate(inp, gate):
+    """A scalar per-(token, head) log-decay for GDN (channel 0 of the drawn
+    per-channel gate, so it has the workload's distribution), None for
+    DeltaNet."""
+    return np.ascontiguousarray(inp.g[..., 0]) if gate == kda.GATE_HEAD else None
+
+
+@pytest.mark.parametrize("gate", [kda.GATE_HEAD, kda.GATE_NONE])
+@pytest.mark.parametrize("D", [128, 16])
+def test_prefill_gate_variants(gate, D):
+    """Gated DeltaNet (one decay per token and head) and DeltaNet (no decay):
+    ragged varlen with initial states and checkpoints, against the oracle with
+    the variant's gate spread over the key channels."""
+    lengths = [37, 0, 16, 1, 100, 64, 15, 17]
+    H = 3
+    print(f"case: prefill gate {gate} D={D}", flush=True)
+    inp = make_inputs(sum(lengths), H, D, seed=131 + gate + D, lengths=lengths, initial_state=True)
+    gv = _variant_gate(inp, gate)
+    o, fin, ck = kda.prefill(to_dev(inp.q, torch.bfloat16), to_dev(inp.k, torch.bfloat16),
+                             to_dev(inp.v, torch.bfloat16), None if gv is None else to_dev(gv),
+                             to_dev(inp.beta), cu_seqlens=inp.cu_seqlens,
+                             initial_state=to_dev(inp.initial_state), ckpt_interval=32,
+                             options=kda.Options(gate=gate))
+    torch.cuda.synchronize()
+    gc = var_oracle.gate_per_channel(gv, gate, inp.q.shape)
+    o_ref, f_ref, ck_ref = reference.prefill(inp.q, inp.k, inp.v, gc, inp.beta, cu_seqlens=inp.cu_seqlens,
+                                             initial_state=inp.initial_state, ckpt_interval=32)
+    check_outputs(o.float().cpu().numpy(), o_ref, inp.cu_seqlens, H)
+    check_states(fin.cpu().numpy(), f_ref, "final")
+    check_states(ck.cpu().numpy(), ck_ref, "checkpoint")
+
+
+def test_prefill_gdn_with_front_end():
+    """Gated DeltaNet from raw projections: raw q, k, one gate logit per token
+    and head, beta logits."""
+    lengths = [90, 41]
+    H, D = 2, 128
+    print("case: prefill GDN + front end", flush=True)
+    raw = make_inputs(sum(lengths), H, D, seed=141, lengths=lengths, raw=True)
+    ga = np.ascontiguousarray(raw.g[..., 0])
+    o, fin, _ = kda.prefill(to_dev(raw.q, torch.bfloat16), to_dev(raw.k, torch.bfloat16),
+                            to_dev(raw.v, torch.bfloat16), to_dev(ga), to_dev(raw.beta),
+                            cu_seqlens=raw.cu_seqlens,
+                            options=kda.Options(kda.FE_ALL, FE_EPS, gate=kda.GATE_HEAD))
+    torch.cuda.synchronize()
+    q2, k2, g2, b2 = fe_oracle.apply(raw.q, raw.k, ga, raw.beta, fe_oracle.L2NORM_QK | fe_oracle.GATE_LOGITS
+                                     | fe_oracle.BETA_LOGITS, eps=FE_EPS)
+    gc = var_oracle.gate_per_channel(g2, var_oracle.GATE_HEAD, raw.q.shape)
+    o_ref, f_ref, _ = reference.prefill(q2, k2, raw.v, gc, b2, cu_seqlens=raw.cu_seqlens)
+    check_outputs(o.float().cpu().numpy(), o_ref, raw.cu_seqlens, H)
+    check_states(fin.cpu().numpy(), f_ref, "final")
+
+
+@pytest.mark.parametrize("gate", [kda.GATE_HEAD, kda.GATE_NONE])
+def test_prefill_gate_variants_full_size_sampled_heads(gate):
+    """B=1, H=32, T=8192, D=128 for GDN and DeltaNet; oracle on 2 heads."""
+    T, H, D = 8192, 32, 128
+    print(f"case: gate {gate} full size", flush=True)
+    q, k, v, g, beta, cu, _ = make_inputs_device(T, H, D, seed=151 + gate, device=DEV)
+    gv = g[..., 0].contiguous() if gate == kda.GATE_HEAD else None
+    o, fin, _ = kda.prefill(q, k, v, gv, beta, cu_seqlens=cu, options=kda.Options(gate=gate))
+    torch.cuda.synchronize()
+    heads = [0, 31]
+    sel = lambda t: t[:, heads].float().cpu().numpy()
+    gc = var_oracle.gate_per_channel(None if gv is None else sel(gv), gate, (T, len(heads), D))
+    o_ref, f_ref, _ = reference.prefill(sel(q), sel(k), sel(v), gc, sel(beta), cu_seqlens=cu.numpy())
+    check_outputs(o[:, heads].float().cpu().numpy(), o_ref, cu.numpy(), len(heads))
+    check_states(fin[:, heads].cpu().numpy(), f_ref, "final")
+
+
+@pytest.mark.parametrize("gate", [kda.GATE_HEAD, kda.GATE_NONE])
+@pytest.mark.parametrize("D", [128, 16])
+def test_decode_tokens_gate_variants(gate, D):
+    """Multi-token decode for GDN and DeltaNet, mixed accepted lengths."""
+    N, T, H = 4, 3, 2
+    print(f"case: decode_tokens gate {gate} D={D}", flush=True)
+    inp = make_inputs(N * T, H, D, seed=161 + gate + D, lengths=[T] * N, initial_state=True)
+    shp = lambda a: np.ascontiguousarray(a.reshape(N, T, *a.shape[1:]))
+    q, k, v, g, beta = map(shp, (inp.q, inp.k, inp.v, inp.g, inp.beta))
+    gv = np.ascontiguousarray(g[..., 0]) if gate == kda.GATE_HEAD else None
+    accept = [T, 0, 2, 1]
+    state = to_dev(inp.initial_state)
+    o = kda.decode_tokens(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16), to_dev(v, torch.bfloat16),
+                          None if gv is None else to_dev(gv), to_dev(beta), state,
+                          accept=torch.tensor(accept, dtype=torch.int32, device=DEV), scale=0.5,
+                          options=kda.Options(gate=gate))
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    S = state.cpu().numpy()
+    gc = var_oracle.gate_per_channel(gv, gate, q.shape)
+    st = inp.initial_state.astype(np.float64)
+    for t in range(T):
+        o_t, st = reference.decode(q[:, t], k[:, t], v[:, t], gc[:, t], beta[:, t], st, scale=0.5)
+        for n, h in np.ndindex(N, H):
+            assert rel_err(o[n, t, h], o_t[n, h]) <= O_TOL, (n, t, h)
+        for n in range(N):
+            if accept[n] == t + 1:
+                check_states(S[n:n + 1], st[n:n + 1], f"seq {n}")
+    assert np.array_equal(S[1], inp.initial_state[1])
