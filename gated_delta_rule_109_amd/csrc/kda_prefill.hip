@@ -189,9 +189,14 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
   // P[r][ch] (fp32, rows padded by 16 bytes) during phases 1-2, then the
   // blocks of T.
   constexpr int kPBytes = kBT * (D + 4) * 4;
+  constexpr int kKPad = 16 / (int)sizeof(TIn);                   // 16-byte row padding
+  constexpr int kKBytes = kBT * (D + kKPad) * (int)sizeof(TIn);
   constexpr int kTBytes = (kBT * (kBT + 4) + 2 * 16 * 20) * 4;
-  __shared__ __attribute__((aligned(16))) char lds_raw[kPBytes > kTBytes ? kPBytes : kTBytes];
+  __shared__ __attribute__((aligned(16))) char lds_raw[kPBytes + kKBytes > kTBytes ? kPBytes + kKBytes : kTBytes];
   float(*sP)[D + 4] = (float(*)[D + 4])lds_raw;
+  // the block's k rows as loaded (phase 1 reads them once from memory; phase 2
+  // takes them from here in fragment order instead of reading memory again)
+  TIn(*sK)[D + kKPad] = (TIn(*)[D + kKPad])(lds_raw + kPBytes);
   float(*sT)[kBT + 4] = (float(*)[kBT + 4])lds_raw;
   float(*sX)[20] = (float(*)[20])(lds_raw + kBT * (kBT + 4) * 4);                  // (I + A_bb)^{-1}
   float(*sM)[20] = (float(*)[20])(lds_raw + (kBT * (kBT + 4) + 16 * 20) * 4);      // A_ba T_aa
@@ -285,7 +290,10 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
     for (int t = 0; t < kBT; ++t) {
       const int tc = min(t, cnt - 1);
       a[t] = g_at(tc, ch);
-      kf[t] = Elem<TIn>::load(k + row(tc) + ch);
+      const TIn kraw = k[row(tc) + ch];
+      sK[t][ch] = kraw;
+      if constexpr (sizeof(TIn) == 2) kf[t] = bf16_to_f32(kraw);
+      else kf[t] = kraw;
     }
 #pragma unroll
     for (int t = 0; t < kBT; ++t) {
@@ -339,6 +347,14 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
       else x = *(const f32x4*)ptr;
       return t < cnt && ch0 < D ? x : f32x4{0.f, 0.f, 0.f, 0.f};
     };
+    // k from the LDS copy (rows past the end hold row cnt - 1: selected away)
+    auto kpiece = [&](int t, int ch0) __attribute__((always_inline)) {
+      const TIn* ptr = &sK[t][ch0 < D ? ch0 : 0];
+      f32x4 x;
+      if constexpr (sizeof(TIn) == 2) x = from_bf16x4(*(const bf16x4*)ptr);
+      else x = *(const f32x4*)ptr;
+      return t < cnt && ch0 < D ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+    };
     auto decay = [&](int t, int ch0) __attribute__((always_inline)) {
       const f32x4 x = *(const f32x4*)&sP[t][ch0 < D ? ch0 : 0];
       return ch0 < D ? x : f32x4{1.f, 1.f, 1.f, 1.f};
@@ -346,7 +362,6 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       if (!(wave == which || (kWaves == 1 && wave == 0))) continue;
-      const TIn* src = which ? q : k;
       bf16x8 X[2][R::NP], Km[2][R::NP];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -355,9 +370,10 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
           const int t = 16 * u + mm, c0 = ch_of(p, gq, 0), c1 = ch_of(p, gq, 4);
           const f32x4 P0 = decay(t, c0), P1 = decay(t, c1);
           const float rs = which ? rq(t) : rk(t);
-          const f32x4 x0 = piece(src, t, c0) * rs, x1 = piece(src, t, c1) * rs;
+          const f32x4 x0 = (which ? piece(q, t, c0) : kpiece(t, c0)) * rs;
+          const f32x4 x1 = (which ? piece(q, t, c1) : kpiece(t, c1)) * rs;
           X[u][p] = cat(to_bf16x4(x0 * P0), to_bf16x4(x1 * P1));
-          const f32x4 k0 = which ? piece(k, t, c0) * rk(t) : x0, k1 = which ? piece(k, t, c1) * rk(t) : x1;
+          const f32x4 k0 = which ? kpiece(t, c0) * rk(t) : x0, k1 = which ? kpiece(t, c1) * rk(t) : x1;
           f32x4 r0, r1;
 #pragma unroll
           for (int i = 0; i < 4; ++i) { r0[i] = k0[i] / P0[i]; r1[i] = k1[i] / P1[i]; }
