@@ -1,4 +1,6 @@
-"""Build libkda.so (the HIP library behind include/kda.h) in-tree for gfx950.
+"""Build libkda.so (the HIP library behind include/kda.h) in-tree for gfx950,
+and libkda_peak.so, a measurement helper (a bf16 MFMA loop that bench.py times
+as the measured matrix rate; not part of the KDA library).
 
 Each .hip source is compiled with hipcc for gfx950 only, then linked into
 gated_delta_rule_109_amd/libkda.so. Packed-fp32 VALU instructions are turned
@@ -16,6 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkda.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip"]
+PEAK_SOURCE = os.path.join(CSRC, "measure", "peak_mfma.hip")
+PEAK_LIB = os.path.join(HERE, "libkda_peak.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -45,6 +49,9 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
+    tmp = PEAK_LIB + ".tmp"
+    _run([HIPCC, *CFLAGS, "-shared", PEAK_SOURCE, "-o", tmp], verbose)
+    os.replace(tmp, PEAK_LIB)
     return LIB
 
 

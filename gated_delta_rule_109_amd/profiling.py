@@ -8,7 +8,9 @@ MIB MiB, which reads and writes exactly MIB MiB, so each counter is scaled by
 the true size over what it reads for that kernel.
 
 It also renders the per-kernel time table of a ``rocprofv3 --kernel-trace
---stats`` run (``--stats DIR``).
+--stats`` run (``--stats DIR``), and the MFMA utilisation of a counter pass
+with SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16 and
+GRBM_GUI_ACTIVE (``--mfma DIR``).
 
 Usage (two counter passes of the same command, then the summary):
 
@@ -29,6 +31,8 @@ import json
 import os
 import re
 import sys
+
+import numpy as np
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 # the kernels of one plain kda_prefill_chunked call on the benchmarked shape
@@ -159,6 +163,58 @@ def kernel_stats(d):
     return rows
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE")
+SIMD_NUM = 256 * 4          # MI355X: 256 CUs x 4 SIMDs
+XCD_NUM = 8                 # GRBM_GUI_ACTIVE comes summed over the 8 XCDs
+PEAK_KERNEL = "mfma_loop"   # the reference loop of libkda_peak.so
+
+
+def mfma_summary(d):
+    """[(kernel, dispatches, MFMA busy %, bf16 MFMA GFLOP per dispatch)]: busy
+    cycles over all SIMDs / (GPU-active cycles of one XCD x SIMD_NUM); FLOPs =
+    MOPS x 512. The CSV holds GRBM_GUI_ACTIVE summed over the XCDs, so it is
+    divided by XCD_NUM (the vendor's MfmaUtil takes its maximum over them)."""
+    acc = {}
+    for r in csv.DictReader(open(_counter_csv(d))):
+        name = r["Kernel_Name"]
+        if "kda::" in name:
+            key = kernel_key(name)
+        elif PEAK_KERNEL in name:
+            key = kernel_key(name.replace("(anonymous namespace)::", "")) + " (reference loop)"
+        else:
+            continue
+        c = r["Counter_Name"]
+        if c not in MFMA_COUNTERS:
+            continue
+        per = acc.setdefault(key, {}).setdefault(c, [])
+        per.append(float(r["Counter_Value"]))
+    rows = []
+    for key, per in sorted(acc.items()):
+        if not all(c in per for c in MFMA_COUNTERS):
+            continue
+        n = len(per["GRBM_GUI_ACTIVE"])
+        busy = np.mean(per["SQ_VALU_MFMA_BUSY_CYCLES"])
+        active = np.mean(per["GRBM_GUI_ACTIVE"]) / XCD_NUM
+        flops = np.mean(per["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) * 512
+        rows.append((key, n, 100.0 * busy / (active * SIMD_NUM), flops / 1e9))
+    return rows
+
+
+def render_mfma(rows, title, command):
+    out = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```"]
+    out += list(command)
+    out += ["```", "",
+            "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES summed over the SIMDs / (GRBM_GUI_ACTIVE of one XCD x "
+            "1024 SIMDs) (the CSV sums GRBM_GUI_ACTIVE over the 8 XCDs); "
+            "bf16 MFMA FLOPs = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512. This counts every MFMA the kernels issue "
+            "(hi/lo split terms and padding included), not the model FLOPs. The reference loop "
+            "(independent MFMA chains, libkda_peak.so; <0> = 16x16x32, <1> = 32x32x16) shows what the counter reads for a matrix-bound kernel.",
+            "", "| kernel | dispatches | MFMA busy % | bf16 MFMA GFLOP per dispatch |", "|---|---|---|---|"]
+    for key, n, util, gf in rows:
+        out.append(f"| `{key}` | {n} | {util:.2f} | {gf:.2f} |")
+    return "\n".join(out) + "\n"
+
+
 def render_stats(rows, title, command, bench_line):
     out = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```"]
     out += list(command)
@@ -179,6 +235,7 @@ def main(argv=None):
     ap.add_argument("--calib-mib", type=int)
     ap.add_argument("--algorithmic-bytes", type=int)
     ap.add_argument("--stats", help="rocprofv3 --kernel-trace --stats output directory (kernel-time summary)")
+    ap.add_argument("--mfma", help="rocprofv3 --pmc output directory with the MFMA counters")
     ap.add_argument("--title", default="KDA kernels")
     ap.add_argument("--bench-line", help="file whose last line is the bench.py JSON line")
     ap.add_argument("--command", action="append", default=[])
@@ -187,6 +244,8 @@ def main(argv=None):
     if a.stats:
         line = open(a.bench_line).read().strip().splitlines()[-1] if a.bench_line else None
         text = render_stats(kernel_stats(a.stats), a.title, a.command, line)
+    elif a.mfma:
+        text = render_mfma(mfma_summary(a.mfma), a.title, a.command)
     else:
         if not (a.fetch and a.write and a.calib_mib and a.algorithmic_bytes):
             ap.error("--fetch, --write, --calib-mib and --algorithmic-bytes are required")
