@@ -109,6 +109,41 @@ def _check_dev(*ts):
             raise ValueError("tensors must be contiguous device tensors")
 
 
+def _expect(t, name, shape, dtype):
+    """The C ABI takes raw pointers and cannot see sizes: a wrong shape would
+    make a kernel read or write out of bounds, so every tensor is checked here
+    before any call."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+
+
+def _gate_shape(lead, H, D, options):
+    """Shape of g for the gate layout of `options` (None: no g is read)."""
+    gate = GATE_CHANNEL if options is None else options.gate
+    if gate == GATE_NONE:
+        return None
+    return (*lead, H, D) if gate == GATE_CHANNEL else (*lead, H)
+
+
+def _check_inputs(q, k, v, g, beta, lead, H, D, options, beta_shape):
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"q/k/v must be bfloat16 or float32, got {q.dtype}")
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _expect(t, name, (*lead, H, D), q.dtype)
+    gshape = _gate_shape(lead, H, D, options)
+    if gshape is None:
+        g = None
+    elif g is None:
+        raise ValueError("g is required by this gate layout")
+    _expect(g, "g", gshape if gshape else (), torch.float32)
+    _expect(beta, "beta", beta_shape, torch.float32)
+    return g
+
+
 def num_checkpoints(cu_seqlens, ckpt_interval: int) -> int:
     cu, p = _host_cu(cu_seqlens)
     r = lib().kda_prefill_num_checkpoints(p, len(cu) - 1, int(ckpt_interval))
@@ -157,7 +192,14 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, scale=1.0, g_
     if plan is None:
         plan = make_plan([0, T] if cu_seqlens is None else cu_seqlens, H, D, q.device, ckpt_interval)
     N = len(plan.cu_host) - 1
-    _check_dev(q, k, v, g, beta, initial_state)
+    if int(plan.cu_host[-1]) != T:
+        raise ValueError(f"cu_seqlens ends at {int(plan.cu_host[-1])}, but q holds {T} tokens")
+    g = _check_inputs(q, k, v, g, beta, (T,), H, D, options, (T, H))
+    _expect(initial_state, "initial_state", (N, H, D, D), torch.float32)
+    _expect(o, "o", (T, H, D), q.dtype)
+    _expect(final_state, "final_state", (N, H, D, D), torch.float32)
+    _expect(checkpoints, "checkpoints", (plan.num_ckpt, H, D, D), torch.float32)
+    _check_dev(q, k, v, g, beta, initial_state, o, final_state, checkpoints)
     if o is None:
         o = torch.empty_like(v)
     if final_state is None and out_final_state:
@@ -181,7 +223,10 @@ def decode_step(q, k, v, g, beta, state, scale=1.0, g_min=LN_HALF, o=None):
     """kda_decode_step: q,k,g [N,H,D]; v [N,H,D]; beta [N,H]; state [N,H,D,D]
     updated in place. Returns o [N,H,D]."""
     N, H, D = q.shape
-    _check_dev(q, k, v, g, beta, state)
+    _check_inputs(q, k, v, g, beta, (N,), H, D, None, (N, H))
+    _expect(state, "state", (N, H, D, D), torch.float32)
+    _expect(o, "o", (N, H, D), q.dtype)
+    _check_dev(q, k, v, g, beta, state, o)
     if o is None:
         o = torch.empty_like(v)
     st = lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta),
@@ -199,9 +244,11 @@ def decode_tokens(q, k, v, g, beta, state, accept=None, scale=1.0, g_min=LN_HALF
     None); accept is a device int32 [N] tensor; options as in prefill.
     Returns o [N,T,H,D]."""
     N, T, H, D = q.shape
-    _check_dev(q, k, v, g, beta, state, accept)
-    if accept is not None and accept.dtype != torch.int32:
-        raise TypeError("accept must be int32")
+    g = _check_inputs(q, k, v, g, beta, (N, T), H, D, options, (N, T, H))
+    _expect(state, "state", (N, H, D, D), torch.float32)
+    _expect(accept, "accept", (N,), torch.int32)
+    _expect(o, "o", (N, T, H, D), q.dtype)
+    _check_dev(q, k, v, g, beta, state, accept, o)
     if o is None:
         o = torch.empty_like(v)
     st = lib().kda_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta),

@@ -1,0 +1,83 @@
+"""The rocprofv3 summaries behind roofline.traffic and the MFMA figures,
+checked on small synthetic counter files (CPU only)."""
+import csv
+import json
+import os
+
+import pytest
+
+from gated_delta_rule_109_amd import profiling as P
+
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def write_counters(d, rows):
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "kda_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.DictWriter(fh, FIELDS)
+        w.writeheader()
+        for i, (k, c, v) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+
+
+PLAN = "kda::plan_kernel(int const*, int)"
+PREP = "void kda::prep_kernel<128, unsigned short, false>(unsigned short const*)"
+PREP_GEN = "void kda::prep_kernel<128, unsigned short, true>(unsigned short const*)"
+CHAIN = "void kda::chain_kernel<128, unsigned short, false>(unsigned short const*)"
+ABS = "void at::native::vectorized_elementwise_kernel<4, at::native::AbsFunctor<float>>(int)"
+
+
+def test_traffic_summary_scales_by_the_calibration_kernel(tmp_path):
+    f, w = str(tmp_path / "f"), str(tmp_path / "w")
+    # the calibration kernel reads and writes 256 MiB; the counters read half
+    # of that for FETCH_SIZE and all of it for WRITE_SIZE
+    write_counters(f, [(ABS, "FETCH_SIZE", 128 * 1024), (PLAN, "FETCH_SIZE", 1), (PREP, "FETCH_SIZE", 1000),
+                       (PREP_GEN, "FETCH_SIZE", 5000), (CHAIN, "FETCH_SIZE", 2000), (CHAIN, "FETCH_SIZE", 4000)])
+    write_counters(w, [(ABS, "WRITE_SIZE", 256 * 1024), (PLAN, "WRITE_SIZE", 1), (PREP, "WRITE_SIZE", 300),
+                       (PREP_GEN, "WRITE_SIZE", 9), (CHAIN, "WRITE_SIZE", 100)])
+    res = P.summarize(f, w, 256)
+    assert res["fetch_factor"] == pytest.approx(2.0) and res["write_factor"] == pytest.approx(1.0)
+    # plain call only (the front-end prep is listed apart): fetch x2, write x1,
+    # chain fetch averaged over its two dispatches
+    want = (2 * (1 + 1000 + 3000) + (1 + 300 + 100)) * 1024
+    assert res["bytes_per_call"] == pytest.approx(want)
+    assert [r[0] for r in res["others"]] == ["kda::prep_kernel<128, unsigned short, true>"]
+
+
+def test_traffic_record_follows_the_sources(tmp_path):
+    f, w = str(tmp_path / "f"), str(tmp_path / "w")
+    write_counters(f, [(ABS, "FETCH_SIZE", 1024), (PLAN, "FETCH_SIZE", 1), (PREP, "FETCH_SIZE", 1),
+                       (CHAIN, "FETCH_SIZE", 1)])
+    write_counters(w, [(ABS, "WRITE_SIZE", 1024), (PLAN, "WRITE_SIZE", 1), (PREP, "WRITE_SIZE", 1),
+                       (CHAIN, "WRITE_SIZE", 1)])
+    text = P.render(P.summarize(f, w, 1), 1, ["cmd"], 1000)
+    out = tmp_path / "t.md"
+    out.write_text(text)
+    rec = P.read_record(str(out))
+    assert rec is not None and rec["source_digest"] == P.source_digest()
+    stale = text.replace(P.source_digest(), "0" * 16)
+    out.write_text(stale)
+    assert P.read_record(str(out)) is None
+    assert P.read_record(str(tmp_path / "missing.md")) is None
+
+
+def test_mfma_busy_uses_one_xcd_of_active_cycles(tmp_path):
+    d = str(tmp_path / "m")
+    # 16 busy cycles per MFMA summed over the SIMDs; GRBM_GUI_ACTIVE summed
+    # over 8 XCDs: 1000 cycles each
+    busy = 0.5 * 1000 * P.SIMD_NUM
+    write_counters(d, [(CHAIN, "SQ_VALU_MFMA_BUSY_CYCLES", busy), (CHAIN, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 2e6),
+                       (CHAIN, "GRBM_GUI_ACTIVE", 8 * 1000),
+                       ("void (anonymous namespace)::mfma_loop<1>(float*, int)", "SQ_VALU_MFMA_BUSY_CYCLES",
+                        1000 * P.SIMD_NUM),
+                       ("void (anonymous namespace)::mfma_loop<1>(float*, int)", "SQ_INSTS_VALU_MFMA_MOPS_BF16", 0),
+                       ("void (anonymous namespace)::mfma_loop<1>(float*, int)", "GRBM_GUI_ACTIVE", 8000)])
+    rows = {r[0]: r for r in P.mfma_summary(d)}
+    assert rows["kda::chain_kernel<128, unsigned short, false>"][2] == pytest.approx(50.0)
+    assert rows["kda::chain_kernel<128, unsigned short, false>"][3] == pytest.approx(2e6 * 512 / 1e9)
+    assert rows["mfma_loop<1> (reference loop)"][2] == pytest.approx(100.0)
+
+
+def test_kernel_key_keeps_template_arguments():
+    assert P.kernel_key(CHAIN) == "kda::chain_kernel<128, unsigned short, false>"
+    assert P.kernel_key(PLAN) == "kda::plan_kernel"
