@@ -616,3 +616,43 @@ def test_decode_tokens_gate_variants(gate, D):
             if accept[n] == t + 1:
                 check_states(S[n:n + 1], st[n:n + 1], f"seq {n}")
     assert np.array_equal(S[1], inp.initial_state[1])
+
+
+# ------------------------------------------------------------ edge sizes
+def test_prefill_all_sequences_empty():
+    """Every sequence has length 0: no outputs; each final state equals its
+    initial state, bit for bit (and zero without initial states)."""
+    H, D = 3, 128
+    cu = np.array([0, 0, 0, 0])
+    print("case: all sequences empty", flush=True)
+    s0 = np.random.default_rng(3).standard_normal((3, H, D, D)).astype(np.float32)
+    z = lambda *s: torch.zeros(*s, device=DEV)
+    q = torch.zeros(0, H, D, dtype=torch.bfloat16, device=DEV)
+    o, fin, _ = kda.prefill(q, q, q, z(0, H, D), z(0, H), cu_seqlens=cu, initial_state=to_dev(s0))
+    torch.cuda.synchronize()
+    assert o.shape == (0, H, D)
+    assert np.array_equal(fin.cpu().numpy(), s0)
+    _, fin0, _ = kda.prefill(q, q, q, z(0, H, D), z(0, H), cu_seqlens=cu)
+    torch.cuda.synchronize()
+    assert not fin0.abs().any()
+
+
+def test_decode_large_batch_sampled():
+    """2048 sequences x 32 heads (65536 head-states, 4 GiB of fp32 state) in
+    one step; sampled (sequence, head) pairs against the oracle and every
+    state finite."""
+    N, H, D = 2048, 32, 128
+    print(f"case: decode N={N} H={H}", flush=True)
+    q, k, v, g, beta, _, s0 = make_inputs_device(N, H, D, seed=171, device=DEV, lengths=[1] * N,
+                                                 initial_state=True)
+    s_in = s0.clone()
+    o = kda.decode_step(q, k, v, g, beta, s0)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    for n in rng.choice(N, 6, replace=False):
+        sel = lambda t: t[n:n + 1].float().cpu().numpy()
+        o_ref, s_ref = reference.decode(sel(q), sel(k), sel(v), sel(g), sel(beta), s_in[n:n + 1].cpu().numpy())
+        for h in range(H):
+            assert rel_err(o[n, h].float().cpu().numpy(), o_ref[0, h]) <= O_TOL, (n, h)
+        check_states(s0[n:n + 1].cpu().numpy(), s_ref, f"seq {n}")
+    assert torch.isfinite(s0).all()
