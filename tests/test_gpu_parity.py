@@ -656,3 +656,67 @@ def test_decode_large_batch_sampled():
             assert rel_err(o[n, h].float().cpu().numpy(), o_ref[0, h]) <= O_TOL, (n, h)
         check_states(s0[n:n + 1].cpu().numpy(), s_ref, f"seq {n}")
     assert torch.isfinite(s0).all()
+
+
+# -------------------------------------------------------- graph capture
+def test_calls_replay_from_a_captured_graph():
+    """A prefill (with a prepared plan) and a decode step captured in one graph
+    replay correctly: after each replay (new inputs copied into the captured
+    buffers, eager work in between), outputs and states equal eager calls on
+    the same inputs bit for bit. The library launches only kernels on the
+    caller's stream: no allocation, no memset."""
+    H, D = 2, 128
+    lengths = [70, 33]
+    T = sum(lengths)
+    print("case: graph capture", flush=True)
+    plan = kda.make_plan([0, 70, 103], H, D, DEV)
+    bufs = {n: torch.empty(T, H, D, dtype=torch.bfloat16, device=DEV) for n in ("q", "k", "v")}
+    g = torch.empty(T, H, D, device=DEV)
+    beta = torch.empty(T, H, device=DEV)
+    o = torch.empty(T, H, D, dtype=torch.bfloat16, device=DEV)
+    fin = torch.empty(2, H, D, D, device=DEV)
+    N = 8
+    dq, dk, dv = (torch.empty(N, H, D, dtype=torch.bfloat16, device=DEV) for _ in range(3))
+    dg, dbeta = torch.empty(N, H, D, device=DEV), torch.empty(N, H, device=DEV)
+    state = torch.empty(N, H, D, D, device=DEV)
+    dout = torch.empty(N, H, D, dtype=torch.bfloat16, device=DEV)
+
+    def load(seed):
+        inp = make_inputs(T, H, D, seed=seed, lengths=lengths)
+        for n, x in (("q", inp.q), ("k", inp.k), ("v", inp.v)):
+            bufs[n].copy_(to_dev(x, torch.bfloat16))
+        g.copy_(to_dev(inp.g))
+        beta.copy_(to_dev(inp.beta))
+        d = make_inputs(N, H, D, seed=seed + 1, lengths=[1] * N, initial_state=True)
+        for dst, x in ((dq, d.q), (dk, d.k), (dv, d.v)):
+            dst.copy_(to_dev(x, torch.bfloat16))
+        dg.copy_(to_dev(d.g))
+        dbeta.copy_(to_dev(d.beta))
+        state.copy_(to_dev(d.initial_state))
+
+    def calls():
+        kda.prefill(bufs["q"], bufs["k"], bufs["v"], g, beta, plan=plan, o=o, final_state=fin)
+        kda.decode_step(dq, dk, dv, dg, dbeta, state, o=dout)
+
+    load(200)                            # warm-up on a side stream, as graph capture requires
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for seed in (300, 400, 500):
+        load(seed)
+        s0 = state.clone()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (o.clone(), fin.clone(), dout.clone(), state.clone())
+        _ = torch.randn(1 << 20, device=DEV).sum()          # unrelated eager work
+        state.copy_(s0)
+        calls()
+        torch.cuda.synchronize()
+        for a, b in zip(got, (o, fin, dout, state)):
+            assert torch.equal(a, b), f"replay with inputs {seed} differs from the eager call"
