@@ -215,6 +215,21 @@ def main():
         vms[name] = float(np.mean(ts))
     del g_head
 
+    # the per-GPU share of 32 heads over 8 GPUs: 4 heads, the same sequence length.
+    # The chain then fills 32 of 256 compute units; the library splits the
+    # sequence into segments that run side by side (against one segment).
+    H4 = 4
+    q4, k4, v4, g4, b4, cu4, _ = make_inputs_device(T, H4, D, seed=5, device=dev)
+    plan4 = kda.make_plan(cu4, H4, D, dev)
+    o4 = torch.empty_like(v4)
+    fin4 = torch.empty(1, H4, D, D, dtype=torch.float32, device=dev)
+    seg_ms = {}
+    for name, opt in (("one_segment", kda.Options(segments=1)), ("library_choice", None)):
+        _, ts = time_events(lambda: kda.prefill(q4, k4, v4, g4, b4, plan=plan4, o=o4, final_state=fin4,
+                                                options=opt), args.steps, args.warmup, flush)
+        seg_ms[name] = float(np.mean(ts))
+    del q4, k4, v4, g4, b4
+
     # decode: 256 sequences x 32 heads
     N = 256
     dq, dk, dv, dg, dbeta, _, ds0 = make_inputs_device(N, H, D, seed=3, device=dev, lengths=[1] * N,
@@ -282,6 +297,10 @@ def main():
                               "launch_ms": round(f_ms, 4), "tokens_per_s": round(T / (f_ms * 1e-3), 1)},
         "prefill_variants": {"workload": "the same prefill for Gated DeltaNet (g [T, H]) and DeltaNet (no g)",
                              "gdn_launch_ms": round(vms["gdn"], 4), "deltanet_launch_ms": round(vms["deltanet"], 4)},
+        "prefill_4_heads": {"workload": "B=1, H=4, T=8192, D=128 (32 heads over 8 GPUs, one GPU's share)",
+                            "one_segment_ms": round(seg_ms["one_segment"], 4),
+                            "library_choice_ms": round(seg_ms["library_choice"], 4),
+                            "segments_speedup": round(seg_ms["one_segment"] / seg_ms["library_choice"], 3)},
         "decode": {"workload": "256 sequences x 32 heads, D=128, one token, fp32 states in place",
                    "ms": round(d_ms, 4), "back_to_back_ms": round(d_bb_ms, 4), "head_tokens_per_s": round(N * H / (d_ms * 1e-3), 1),
                    "GBps": round(d_gbps, 1), "hbm_frac": round(d_gbps / HBM_PEAK_GBPS, 4),

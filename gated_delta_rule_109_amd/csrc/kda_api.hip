@@ -44,6 +44,7 @@ bool options_ok(const kda_options* opt) {
   if (opt->flags & ~known) return false;
   if (opt->gate != KDA_GATE_CHANNEL && opt->gate != KDA_GATE_HEAD && opt->gate != KDA_GATE_NONE) return false;
   if (opt->gate == KDA_GATE_NONE && (opt->flags & KDA_FE_GATE_LOGITS)) return false;
+  if (opt->segments < 0 || opt->segments > KDA_MAX_SEGMENTS) return false;
   return opt->norm_eps >= 0.f && opt->norm_eps <= FLT_MAX;
 }
 int32_t gate_of(const kda_options* opt) { return opt ? opt->gate : KDA_GATE_CHANNEL; }
@@ -126,6 +127,21 @@ kda_status kda_prefill_chunked_ex(const void* q, const void* k, const void* v, k
   if (!aligned16({q, k, v, g, beta, cu_seqlens, initial_state, final_state, checkpoints, o}))
     return KDA_ERR_INVALID_ARG;
   if (num_seqs == 0) return KDA_OK;
+  // segments per sequence: the library's choice, off, or forced (where the
+  // workspace holds the segment states)
+  int32_t P = 1;
+  const int32_t req = opt ? opt->segments : 0;
+  if (req >= 2) {
+    if (!kda::segments_allowed(num_seqs, H, Dk)) return KDA_ERR_INVALID_ARG;
+    P = req;
+  } else if (req == 0) {
+    int64_t max_blocks = 0;
+    for (int32_t n = 0; n < num_seqs; ++n) {
+      const int64_t b = (cu_seqlens_host[n + 1] - cu_seqlens_host[n] + kda::kBlockTokens - 1) / kda::kBlockTokens;
+      max_blocks = b > max_blocks ? b : max_blocks;
+    }
+    P = kda::auto_segments(num_seqs, H, Dk, max_blocks);
+  }
   const kda::PrefillLayout L = kda::prefill_layout(num_seqs, blocks, H, Dk);
   if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255)) return KDA_ERR_WORKSPACE;
 
@@ -137,6 +153,7 @@ kda_status kda_prefill_chunked_ex(const void* q, const void* k, const void* v, k
   a.scale = scale; a.g_min = g_min;
   a.fe_flags = opt ? opt->flags : 0u; a.fe_eps = opt ? opt->norm_eps : 0.f;
   a.gate = gate_of(opt);
+  a.segments = P;
   a.initial_state = initial_state; a.final_state = final_state;
   a.ckpt_interval = nck > 0 ? ckpt_interval : 0;
   a.checkpoints = checkpoints;

@@ -42,6 +42,7 @@ struct PrefillArgs {
   uint32_t fe_flags = 0;      // KDA_FE_* (0: inputs used as given)
   float fe_eps = 0.f;
   int32_t gate = KDA_GATE_CHANNEL;  // layout of g (kda_gate)
+  int32_t segments = 1;       // segments per sequence (1: none), already resolved
   const float* initial_state;
   float* final_state;
   int32_t ckpt_interval;
@@ -59,10 +60,21 @@ struct PrefillLayout {
   size_t blk_info;        // int2  [total_blocks] (first token, valid tokens)
   size_t records;         // per (block, head) operand records
   size_t record_bytes;    // bytes of one record
+  size_t segs;            // fp32 [N][KDA_MAX_SEGMENTS][H][3][D][D] segment states, or 0
   size_t total;
 };
 
 PrefillLayout prefill_layout(int32_t num_seqs, int64_t total_blocks, int32_t H, int32_t D);
+
+// Whether the workspace holds segment states for this shape.
+inline bool segments_allowed(int32_t num_seqs, int32_t H, int32_t D) {
+  return (int64_t)num_seqs * H * (D / 16) <= KDA_SEGMENT_SLICE_LIMIT;
+}
+// The library's choice of segments per sequence: the largest P >= 3 whose
+// chain workgroups (pass 1: 2P - 3 units per head, pass 2: P - 1) fit one per
+// compute unit, with at least two blocks per segment of the longest
+// sequence; else 1.
+int32_t auto_segments(int32_t num_seqs, int32_t H, int32_t D, int64_t max_blocks);
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);

@@ -90,6 +90,20 @@ size_t record_bytes(int D) { return D == 128 ? Rec<128>::kBytes : Rec<16>::kByte
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// MI355X compute units: one chain workgroup fills one.
+constexpr int kChipCUs = 256;
+
+int32_t auto_segments(int32_t num_seqs, int32_t H, int32_t D, int64_t max_blocks) {
+  if (!segments_allowed(num_seqs, H, D)) return 1;
+  const int64_t slices = (int64_t)num_seqs * H * (D / 16);
+  int32_t best = 1;
+  for (int32_t P = 3; P <= KDA_MAX_SEGMENTS; ++P) {
+    const int64_t units = slices * (2 * P - 3 > P - 1 ? 2 * P - 3 : P - 1);
+    if (units <= kChipCUs && 2 * (int64_t)P <= max_blocks) best = P;
+  }
+  return best;
+}
+
 PrefillLayout prefill_layout(int32_t num_seqs, int64_t total_blocks, int32_t H, int32_t D) {
   PrefillLayout L;
   size_t off = 0;
@@ -98,7 +112,12 @@ PrefillLayout prefill_layout(int32_t num_seqs, int64_t total_blocks, int32_t H, 
   L.blk_info = off;    off = align256(off + 2 * sizeof(int32_t) * (size_t)total_blocks);
   L.records = off;
   L.record_bytes = record_bytes(D);
-  off += L.record_bytes * (size_t)total_blocks * (size_t)H;
+  off = align256(off + L.record_bytes * (size_t)total_blocks * (size_t)H);
+  L.segs = 0;
+  if (segments_allowed(num_seqs, H, D)) {
+    L.segs = off;
+    off += sizeof(float) * (size_t)num_seqs * KDA_MAX_SEGMENTS * H * 3 * D * D;
+  }
   L.total = off;
   return L;
 }
@@ -502,6 +521,9 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
 //    read between B(c + 1) and B(c + 2); they are overwritten after B(c + 2);
 //  - delta of block c (dbuf[c % 2]) is written before B(c + 2), read between
 //    B(c + 2) and B(c + 3), and overwritten after B(c + 3).
+constexpr int kUnitFull = 0;           // chain unit modes (see chain_kernel)
+constexpr int kUnitLocal = 1;
+constexpr int kUnitTransition = 2;
 constexpr int kLoaders = 4;            // loader waves per workgroup
 constexpr int kInFlight = 4;           // blocks each loader keeps in flight
 constexpr int kRing = 3;               // LDS slots
@@ -538,7 +560,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     const int32_t* __restrict__ seq_blk_off, const int32_t* __restrict__ seq_ck_off,
     const char* __restrict__ records, const float* initial_state, float* final_state,
     float* __restrict__ ckpts, TIn* __restrict__ o, int N, int H, int ckpt_interval,
-    float scale, int total_blocks) {
+    float scale, int total_blocks, float* __restrict__ segs, int P, int pass) {
   using Cfg = ChainCfg<D, TIn>;
   using R = Rec<D>;
   constexpr int NCW = Cfg::kHalves;
@@ -546,17 +568,46 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   __shared__ f32x4 xbuf[2][NCW][2][2][kWave];   // [set][wave][K~+ S, (Q~ S)^T][token tile]
   __shared__ bf16x8 dbuf[2][2][kWave];          // [set][hi, lo]: delta of both token tiles
 
+  // Work unit: (sequence, head, segment, mode). Without segments (P = 1) a
+  // unit is a whole (sequence, head) run. With P segments of whole blocks,
+  // pass 0 runs segment 0 in full and, for every middle segment, its local
+  // state (zero start) and its transition (identity start, zero values);
+  // pass 1 runs segments 1 .. P-1 in full from the scanned start states.
   const int NH = N * H;
+  const int U = P == 1 ? 1 : (pass == 0 ? 2 * P - 3 : P - 1);
+  const int NU = NH * U;
   const int b = blockIdx.x;
-  const int s = b / NH, nh = b % NH;   // the slices of one head share an XCD when NH % 8 == 0
+  const int s = b / NU, q = b % NU;   // the slices of one unit share an XCD when NU % 8 == 0
+  const int nh = q % NH, u = q / NH;
   const int n = nh / H, h = nh % H;
+  int seg = 0, mode = kUnitFull;
+  if (P > 1) {
+    if (pass == 0) {
+      if (u > 0) {
+        seg = 1 + (u - 1) / 2;
+        mode = (u - 1) % 2 == 0 ? kUnitLocal : kUnitTransition;
+      }
+    } else {
+      seg = 1 + u;
+    }
+  }
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int mm = lane % 16, gq = lane / 16;
-  const int t_begin = cu[n];
-  const int len = cu[n + 1] - t_begin;
-  const int nblk = (len + kBT - 1) / kBT;
-  if (nblk == 0 && wave >= NCW) return;   // only the initial -> final state copy remains
-  const char* rec0 = records + ((size_t)h * total_blocks + seq_blk_off[n]) * R::kBytes;
+  const int seq_t0 = cu[n], seq_len = cu[n + 1] - seq_t0;
+  const int seq_nblk = (seq_len + kBT - 1) / kBT;
+  const int bps = (seq_nblk + P - 1) / P;                     // blocks per segment
+  const int blk0 = min(seg * bps, seq_nblk), blk1 = min(blk0 + bps, seq_nblk);
+  const int seg_off = kBT * blk0;                             // tokens of the sequence before it
+  const int t_begin = seq_t0 + seg_off;
+  const int len = max(0, min(seq_len - seg_off, kBT * (blk1 - blk0)));
+  const int nblk = blk1 - blk0;
+  const bool write_o = mode == kUnitFull, v_on = mode != kUnitTransition;
+  if (nblk == 0 && wave >= NCW) return;   // only the start -> end state copy remains
+  const char* rec0 = records + ((size_t)h * total_blocks + seq_blk_off[n] + blk0) * R::kBytes;
+  // segment states, [N][KDA_MAX_SEGMENTS][H][3][D][D]: start, local, transition
+  auto seg_state = [&](int p, int kind) __attribute__((always_inline)) {
+    return segs + ((((size_t)n * KDA_MAX_SEGMENTS + p) * H + h) * 3 + kind) * D * D;
+  };
   auto slot_of = [&](int c) __attribute__((always_inline)) { return ring + (c % kRing) * Cfg::kSlot; };
 
   if (wave == NCW + kLoaders) {
@@ -581,7 +632,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       for (int u = 0; u < 2; ++u) {
         const f32x4 out = scale * mfma32(dl, Lf[u], mfma32(dh, Lf[u], P[u]));
         const int tt = 16 * u + mm;
-        if (tt < cnt) {
+        if (tt < cnt && write_o) {
           TIn* dst = o + ((size_t)(t_begin + kBT * c + tt) * H + h) * D + 16 * s + 4 * gq;
           if constexpr (sizeof(TIn) == 2) *(bf16x4*)dst = to_bf16x4(out);
           else *(f32x4*)dst = out;
@@ -644,7 +695,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
           const int e = (fr - R::kFrags) * 1024 + lane * 16;
           const int tt = e / kVRow, c0 = (e % kVRow) / (int)sizeof(TIn);
           const u32x4 zero = {0u, 0u, 0u, 0u};
-          const u32x4 x = tt < cnt ? src[i] : zero;
+          const u32x4 x = tt < cnt && v_on ? src[i] : zero;
           TIn el[kVec];
           __builtin_memcpy(el, &x, 16);
           TIn* vt = (TIn*)(slot + R::kBytes);
@@ -692,18 +743,32 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   // the products of this block have consumed the registers it replaces.
   const int hf = wave;
   const int col = 16 * s + mm;
-  const size_t state_base = (size_t)nh * D * D;
+  // start and end states of the unit (NULL start: zero, or the identity for
+  // a transition; NULL end: not stored)
+  const float* init = nullptr;
+  float* fin = nullptr;
+  if (mode == kUnitFull) {
+    init = seg == 0 ? (initial_state ? initial_state + (size_t)nh * D * D : nullptr) : seg_state(seg, 0);
+    if (seg == P - 1) fin = final_state ? final_state + (size_t)nh * D * D : nullptr;
+    else if (pass == 0) fin = seg_state(1, 0);
+  } else {
+    fin = seg_state(seg, mode == kUnitLocal ? 1 : 2);
+  }
   constexpr int TW = Cfg::kTilesPerWave, PW = Cfg::kBlocksPerWave;
   const int t0 = hf * TW;                 // first row tile of this wave
   f32x4 acc[TW];
 #pragma unroll
   for (int t = 0; t < TW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (initial_state) {
+  if (init) {
 #pragma unroll
     for (int t = 0; t < TW; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[t][i] = initial_state[state_base + (size_t)(16 * (t0 + t) + 4 * gq + i) * D + col];
+      for (int i = 0; i < 4; ++i) acc[t][i] = init[(size_t)(16 * (t0 + t) + 4 * gq + i) * D + col];
+  } else if (mode == kUnitTransition) {
+#pragma unroll
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][i] = 16 * (t0 + t) + 4 * gq + i == col ? 1.f : 0.f;
   }
 
   if (nblk > 0) {
@@ -828,7 +893,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
         dbuf[j % 2][1][lane] = dlw;
       }
       const int mid = kBT * j + kChunk;   // checkpoint after the block's first 16 tokens
-      if (ckpt_interval > 0 && mid <= len && mid % ckpt_interval == 0) {
+      if (ckpt_interval > 0 && write_o && mid <= len && (seg_off + mid) % ckpt_interval == 0) {
         const bf16x4 zero = {};
         const bf16x8 dh_m = cat(dh0, zero), dl_m = cat(dlo0, zero);
         const char* cslot = slot_of(j);
@@ -839,7 +904,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
           const f32x4 p16 = *(const f32x4*)(cslot + R::kPc + (D + 16 * (t0 + t) + 4 * gq) * 4);
           sm[t] = p16 * acc[t] + (p16 / pc[t]) * upd;
         }
-        store_state(sm, mid / ckpt_interval - 1);
+        store_state(sm, (seg_off + mid) / ckpt_interval - 1);
       }
 #pragma unroll
       for (int t = 0; t < TW; ++t)
@@ -847,7 +912,8 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       read_khpc(nslot);
       partials(j + 1);
       const int end = kBT * (j + 1);
-      if (ckpt_interval > 0 && end <= len && end % ckpt_interval == 0) store_state(acc, end / ckpt_interval - 1);
+      if (ckpt_interval > 0 && write_o && end <= len && (seg_off + end) % ckpt_interval == 0)
+        store_state(acc, (seg_off + end) / ckpt_interval - 1);
     };
 
     lds_barrier();
@@ -861,12 +927,57 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     for (int j = 0; j < nblk; ++j) step(j);
     lds_barrier();
   }
-  if (final_state) {
+  if (fin) {
 #pragma unroll
     for (int t = 0; t < TW; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        final_state[state_base + (size_t)(16 * (t0 + t) + 4 * gq + i) * D + col] = acc[t][i];
+      for (int i = 0; i < 4; ++i) fin[(size_t)(16 * (t0 + t) + 4 * gq + i) * D + col] = acc[t][i];
+  }
+}
+
+// ---- 4. the scan over segments (with segments only) ------------------------------------
+// S_in(p) = M_{p-1} S_in(p-1) + local(p-1) for p = 2 .. P-1 (S_in(1) is the end
+// state of segment 0). The end state of a segment is linear in its start
+// state: end = M start + local, with M its transition (the recurrence run from
+// the identity with zero values) and local the run from a zero state. Columns
+// stay independent, so one workgroup takes one 16-column slice of one
+// (sequence, head): it needs its own columns of S_in and local, and all of M.
+// fp32, one output row and 16 / kPerRow column groups per thread.
+template <int D>
+__global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ segs, int N, int H, int P) {
+  constexpr int kOut = D * 16 / 256;                 // outputs per thread: 8 at D = 128, 1 at D = 16
+  constexpr int kPerRow = 16 / kOut;                 // threads per state row
+  const int NH = N * H;
+  const int s = blockIdx.x / NH, nh = blockIdx.x % NH;
+  const int n = nh / H, h = nh % H;
+  const int tid = threadIdx.x, r = tid / kPerRow, c0 = (tid % kPerRow) * kOut;
+  auto seg_state = [&](int p, int kind) __attribute__((always_inline)) {
+    return segs + ((((size_t)n * KDA_MAX_SEGMENTS + p) * H + h) * 3 + kind) * D * D;
+  };
+  __shared__ float X[D][16];                         // S_in(p - 1), this slice's columns
+  for (int e = tid; e < D * 16; e += 256) X[e / 16][e % 16] = seg_state(1, 0)[(size_t)(e / 16) * D + 16 * s + e % 16];
+  __syncthreads();
+  for (int p = 2; p < P; ++p) {
+    const float* M = seg_state(p - 1, 2) + (size_t)r * D;
+    const float* Lc = seg_state(p - 1, 1) + (size_t)r * D + 16 * s + c0;
+    float y[kOut];
+#pragma unroll
+    for (int c = 0; c < kOut; ++c) y[c] = Lc[c];
+    for (int k4 = 0; k4 < D; k4 += 4) {
+      const f32x4 m4 = *(const f32x4*)(M + k4);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int c = 0; c < kOut; ++c) y[c] += m4[kk] * X[k4 + kk][c0 + c];
+    }
+    __syncthreads();
+    float* out = seg_state(p, 0) + (size_t)r * D + 16 * s + c0;
+#pragma unroll
+    for (int c = 0; c < kOut; ++c) {
+      X[r][c0 + c] = y[c];
+      out[c] = y[c];
+    }
+    __syncthreads();
   }
 }
 
@@ -898,13 +1009,24 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     if (e != hipSuccess) return e;
   }
   using Cfg = ChainCfg<D, TIn>;
-  const unsigned blocks = (unsigned)((int64_t)a.num_seqs * a.H * (D / 16));   // one per 16-column slice
+  const int64_t slices = (int64_t)a.num_seqs * a.H * (D / 16);   // one workgroup per 16-column slice
+  const int P = a.segments;
+  float* segs = P > 1 ? (float*)(ws + L.segs) : nullptr;
   auto chain = a.gate == KDA_GATE_NONE ? chain_kernel<D, TIn, true> : chain_kernel<D, TIn, false>;
-  hipLaunchKernelGGL(chain, dim3(blocks), dim3(Cfg::kThreads), 0, a.stream, (const TIn*)a.v,
-                     a.cu_seqlens, seq_blk_off, seq_ck_off, records, a.initial_state,
-                     a.final_state, a.checkpoints, (TIn*)a.o, a.num_seqs, a.H, a.ckpt_interval,
-                     a.scale, (int)a.total_blocks);
-  return hipGetLastError();
+  auto run_chain = [&](int units, int pass) {
+    hipLaunchKernelGGL(chain, dim3((unsigned)(slices * units)), dim3(Cfg::kThreads), 0, a.stream,
+                       (const TIn*)a.v, a.cu_seqlens, seq_blk_off, seq_ck_off, records, a.initial_state,
+                       a.final_state, a.checkpoints, (TIn*)a.o, a.num_seqs, a.H, a.ckpt_interval,
+                       a.scale, (int)a.total_blocks, segs, P, pass);
+    return hipGetLastError();
+  };
+  if (P == 1) return run_chain(1, 0);
+  if ((e = run_chain(2 * P - 3, 0)) != hipSuccess) return e;
+  if (P > 2) {
+    hipLaunchKernelGGL(scan_kernel<D>, dim3((unsigned)slices), dim3(256), 0, a.stream, segs, a.num_seqs, a.H, P);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return run_chain(P - 1, 1);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {

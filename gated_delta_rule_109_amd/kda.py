@@ -30,14 +30,19 @@ FE_ALL = FE_L2NORM_QK | FE_GATE_LOGITS | FE_BETA_LOGITS
 GATE_CHANNEL, GATE_HEAD, GATE_NONE = 0, 1, 2     # KDA, Gated DeltaNet, DeltaNet
 
 
-class Options(ctypes.Structure):
-    """kda_options: which inputs are raw (FE_* flags), the norm epsilon, and
-    the gate layout (GATE_CHANNEL: g [.., H, D]; GATE_HEAD: g [.., H];
-    GATE_NONE: no g)."""
-    _fields_ = [("flags", ctypes.c_uint32), ("norm_eps", ctypes.c_float), ("gate", ctypes.c_int32)]
+MAX_SEGMENTS = 16
 
-    def __init__(self, flags=0, norm_eps=1e-6, gate=GATE_CHANNEL):
-        super().__init__(int(flags), float(norm_eps), int(gate))
+
+class Options(ctypes.Structure):
+    """kda_options: which inputs are raw (FE_* flags), the norm epsilon, the
+    gate layout (GATE_CHANNEL: g [.., H, D]; GATE_HEAD: g [.., H]; GATE_NONE:
+    no g), and the prefill's segments per sequence (0: the library's choice,
+    1: none, 2 .. MAX_SEGMENTS: forced)."""
+    _fields_ = [("flags", ctypes.c_uint32), ("norm_eps", ctypes.c_float), ("gate", ctypes.c_int32),
+                ("segments", ctypes.c_int32)]
+
+    def __init__(self, flags=0, norm_eps=1e-6, gate=GATE_CHANNEL, segments=0):
+        super().__init__(int(flags), float(norm_eps), int(gate), int(segments))
 
 _lib = None
 _vp = ctypes.c_void_p

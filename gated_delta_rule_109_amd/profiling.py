@@ -36,9 +36,12 @@ import numpy as np
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 # the kernels of one plain kda_prefill_chunked call on the benchmarked shape
-# (D = 128, bf16 q/k/v, no front end)
-PREFILL_KERNELS = ("kda::plan_kernel", "kda::prep_kernel<128, unsigned short, false>",
-                   "kda::chain_kernel<128, unsigned short, false>")
+# (B = 1, H = 32, T = 8192, D = 128, bf16 q/k/v, no front end), with their
+# grids in work-items (the same instantiations also run other shapes in the
+# same program, so a dispatch is selected by kernel and grid)
+PREFILL_KERNELS = (("kda::plan_kernel", 1024),
+                   ("kda::prep_kernel<128, unsigned short, false>", 32 * 256 * 128),
+                   ("kda::chain_kernel<128, unsigned short, false>", 256 * 448))
 CALIB_KERNEL = "AbsFunctor"
 
 
@@ -66,17 +69,18 @@ def kernel_key(name):
 
 
 def per_kernel(d, counter):
-    """{kernel name with template arguments: (dispatches, mean KiB per
-    dispatch)} for one counter."""
+    """{(kernel name with template arguments, grid work-items): (dispatches,
+    mean KiB per dispatch)} for one counter."""
     acc = {}
     for r in csv.DictReader(open(_counter_csv(d))):
         if r["Counter_Name"] != counter:
             continue
         name = r["Kernel_Name"]
+        grid = int(float(r.get("Grid_Size") or 0))
         if "kda::" in name:
-            key = kernel_key(name)
+            key = (kernel_key(name), grid)
         elif CALIB_KERNEL in name:
-            key = CALIB_KERNEL
+            key = (CALIB_KERNEL, 0)
         else:
             continue
         n, s = acc.get(key, (0, 0.0))
@@ -88,10 +92,11 @@ def summarize(fetch_dir, write_dir, calib_mib):
     f = per_kernel(fetch_dir, "FETCH_SIZE")
     w = per_kernel(write_dir, "WRITE_SIZE")
     calib_kib = calib_mib * 1024.0
-    if CALIB_KERNEL not in f or CALIB_KERNEL not in w:
+    cal = (CALIB_KERNEL, 0)
+    if cal not in f or cal not in w:
         raise RuntimeError("calibration kernel missing from the counter runs (run bench.py with --calibrate)")
-    ff = calib_kib / f[CALIB_KERNEL][1]     # true bytes per counted byte
-    fw = calib_kib / w[CALIB_KERNEL][1]
+    ff = calib_kib / f[cal][1]     # true bytes per counted byte
+    fw = calib_kib / w[cal][1]
     rows = []
     total = 0.0
     for k in PREFILL_KERNELS:
@@ -102,9 +107,9 @@ def summarize(fetch_dir, write_dir, calib_mib):
         total += fb + wb
         rows.append((k, f[k][0], f[k][1], w[k][1], fb, wb))
     others = [(k, f[k][0], f[k][1], w[k][1], f[k][1] * ff * 1024, w[k][1] * fw * 1024)
-              for k in sorted(f) if k in w and k not in PREFILL_KERNELS and k != CALIB_KERNEL]
+              for k in sorted(f) if k in w and k not in PREFILL_KERNELS and k != cal]
     return {"fetch_factor": ff, "write_factor": fw, "rows": rows, "others": others,
-            "bytes_per_call": total, "calib": (f[CALIB_KERNEL][1], w[CALIB_KERNEL][1])}
+            "bytes_per_call": total, "calib": (f[cal][1], w[cal][1])}
 
 
 def render(res, calib_mib, command, algorithmic_bytes):
@@ -116,17 +121,17 @@ def render(res, calib_mib, command, algorithmic_bytes):
             f"{calib_mib} MiB; the counters read {res['calib'][0]:.4g} KiB (FETCH_SIZE) and "
             f"{res['calib'][1]:.4g} KiB (WRITE_SIZE), so FETCH_SIZE is scaled by {res['fetch_factor']:.3f} "
             f"and WRITE_SIZE by {res['write_factor']:.3f}.", "",
-            "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB (scaled) |",
-            "|---|---|---|---|---|---|"]
-    for k, n, fk, wk, fb, wb in res["rows"]:
-        out.append(f"| `{k}` | {n} | {fk:.4g} | {wk:.4g} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
+            "| kernel | grid (work-items) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB (scaled) |",
+            "|---|---|---|---|---|---|---|"]
+    for (k, grid), n, fk, wk, fb, wb in res["rows"]:
+        out.append(f"| `{k}` | {grid} | {n} | {fk:.4g} | {wk:.4g} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
     tot = res["bytes_per_call"]
     if res.get("others"):
         out += ["", "Other kda kernels in the same run (not part of the call above; per dispatch):", "",
-                "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB (scaled) |",
-                "|---|---|---|---|---|---|"]
-        for k, n, fk, wk, fb, wb in res["others"]:
-            out.append(f"| `{k}` | {n} | {fk:.4g} | {wk:.4g} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
+                "| kernel | grid (work-items) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB (scaled) |",
+                "|---|---|---|---|---|---|---|"]
+        for (k, grid), n, fk, wk, fb, wb in res["others"]:
+            out.append(f"| `{k}` | {grid} | {n} | {fk:.4g} | {wk:.4g} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
     out += ["", f"HBM bytes per `kda_prefill_chunked` call: {tot / 1e6:.1f} MB, against "
             f"{algorithmic_bytes / 1e6:.1f} MB algorithmic (ratio {tot / algorithmic_bytes:.2f}).", "",
             "traffic-record: " + json.dumps({"bytes_per_call": round(tot), "source_digest": source_digest(),

@@ -107,10 +107,27 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
 #define KDA_FE_GATE_LOGITS 2u
 #define KDA_FE_BETA_LOGITS 4u
 typedef enum { KDA_GATE_CHANNEL = 0, KDA_GATE_HEAD = 1, KDA_GATE_NONE = 2 } kda_gate;
+/* segments (prefill only): a long sequence's recurrence split into segments
+ * that run side by side ([K3-DD] 4-1 KDA names "KDA Context Parallelism"; the
+ * split rests on the recurrence being linear in the state):
+ *   pass 1: segment 0 runs in full; every middle segment p runs from a zero
+ *           state (its local state) and, with zero values, from the identity
+ *           (its transition M_p);
+ *   scan:   S_in(p) = M_{p-1} S_in(p-1) + local(p-1);
+ *   pass 2: segments 1 .. P-1 run in full from S_in(p).
+ * Each segment holds whole 32-token blocks. It pays when the chain would
+ * otherwise leave most compute units idle: few sequences times heads. A
+ * value of 0 lets the library choose (1 for most shapes); 1 turns it off;
+ * 2 .. KDA_MAX_SEGMENTS forces that many segments per sequence. Forcing is
+ * accepted only where the workspace holds the segment states:
+ * num_seqs * H * (Dv / 16) <= KDA_SEGMENT_SLICE_LIMIT. */
+#define KDA_MAX_SEGMENTS 16
+#define KDA_SEGMENT_SLICE_LIMIT 80
 typedef struct {
   uint32_t flags;   /* OR of KDA_FE_*; other bits are invalid */
   float norm_eps;   /* >= 0 and finite; used only with KDA_FE_L2NORM_QK */
   int32_t gate;     /* a kda_gate value */
+  int32_t segments; /* 0 = library's choice, 1 = off, 2 .. KDA_MAX_SEGMENTS (prefill) */
 } kda_options;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -125,8 +142,10 @@ int64_t kda_prefill_num_checkpoints(const int32_t* cu_seqlens_host, int32_t num_
 /* Bytes of device workspace kda_prefill_chunked needs for these lengths and
  * shapes (0 if the arguments are invalid). The workspace holds per-block
  * tables and the per-block decayed operands of the chunked form (about
- * 1.2 KiB per token and head at D = 128); its contents are scratch and need
- * no initialisation. */
+ * 1.2 KiB per token and head at D = 128), plus, where segments may be used
+ * (num_seqs * H * (Dv / 16) <= KDA_SEGMENT_SLICE_LIMIT), three fp32 states
+ * per sequence, head and segment; its contents are scratch and need no
+ * initialisation. */
 size_t kda_prefill_workspace_size(const int32_t* cu_seqlens_host, int32_t num_seqs,
                                   int32_t H, int32_t Dk, int32_t Dv);
 

@@ -62,8 +62,14 @@ def test_workspace_size(L):
     # plus tables
     w = kda.workspace_size(cu(8192), 32, 128)
     assert 256 * 32 * 39 * 1024 <= w < 256 * 32 * 39 * 1024 + 8192
+    # few slices (sequences x heads x D/16 <= 80): segment states are added,
+    # 3 fp32 D x D states per sequence, head and segment (16 segments at most)
     w16 = kda.workspace_size(cu(64), 2, 16)
-    assert 2 * 2 * 13 * 1024 <= w16 < 2 * 2 * 13 * 1024 + 2048
+    seg16 = 1 * 16 * 2 * 3 * 16 * 16 * 4
+    assert 2 * 2 * 13 * 1024 + seg16 <= w16 < 2 * 2 * 13 * 1024 + seg16 + 2048
+    w4 = kda.workspace_size(cu(8192), 4, 128)
+    seg128 = 1 * 16 * 4 * 3 * 128 * 128 * 4
+    assert 256 * 4 * 39 * 1024 + seg128 <= w4 < 256 * 4 * 39 * 1024 + seg128 + 4096
     # a ragged tail still takes a whole block
     assert kda.workspace_size(cu(33, 1), 1, 128) >= 3 * 39 * 1024
     assert kda.workspace_size(cu(10), 2, 64) == 0          # unsupported D
@@ -174,6 +180,12 @@ def test_prefill_options_argument_errors(L):
                 kda.Options(gate=-1), kda.Options(kda.FE_GATE_LOGITS, gate=kda.GATE_NONE)):
         assert call(ctypes.byref(bad)) == kda.KDA_ERR_INVALID_ARG
     assert call(None, g=None) == kda.KDA_ERR_INVALID_ARG
+    # segments: 0 .. 16; forcing needs few slices (here 1 x 2 x 8 = 16 <= 80)
+    for bad in (kda.Options(segments=17), kda.Options(segments=-1)):
+        assert call(ctypes.byref(bad)) == kda.KDA_ERR_INVALID_ARG
+    assert call(ctypes.byref(kda.Options(segments=4))) == kda.KDA_ERR_WORKSPACE
+    assert call(ctypes.byref(kda.Options(segments=4)), H=16) == kda.KDA_ERR_INVALID_ARG   # 128 slices
+    assert call(ctypes.byref(kda.Options(segments=1)), H=16) == kda.KDA_ERR_WORKSPACE
     # no gate: g may be NULL (the next failing check is the workspace)
     assert call(ctypes.byref(kda.Options(gate=kda.GATE_NONE)), g=None) == kda.KDA_ERR_WORKSPACE
     # valid descriptor: the next check that fails is the workspace size

@@ -720,3 +720,77 @@ def test_calls_replay_from_a_captured_graph():
         torch.cuda.synchronize()
         for a, b in zip(got, (o, fin, dout, state)):
             assert torch.equal(a, b), f"replay with inputs {seed} differs from the eager call"
+
+
+# ------------------------------------------- segment-parallel prefill
+@pytest.mark.parametrize("P", [2, 3, 5, 16])
+@pytest.mark.parametrize("D", [128, 16])
+def test_prefill_segments_forced(P, D):
+    """One long sequence split into P segments (local states, transitions,
+    scan, second pass): outputs, the final state and checkpoints every 48
+    tokens (some inside segments, some on their edges) against the oracle."""
+    T, H = 1000, 2
+    print(f"case: segments P={P} D={D}", flush=True)
+    inp = make_inputs(T, H, D, seed=181 + P + D, lengths=[T], initial_state=True)
+    o, fin, ck = kda.prefill(to_dev(inp.q, torch.bfloat16), to_dev(inp.k, torch.bfloat16),
+                             to_dev(inp.v, torch.bfloat16), to_dev(inp.g), to_dev(inp.beta),
+                             cu_seqlens=inp.cu_seqlens, initial_state=to_dev(inp.initial_state),
+                             ckpt_interval=48, options=kda.Options(segments=P))
+    torch.cuda.synchronize()
+    o_ref, f_ref, ck_ref = oracle(inp, ckpt=48)
+    check_outputs(o.float().cpu().numpy(), o_ref, inp.cu_seqlens, H)
+    check_states(fin.cpu().numpy(), f_ref, "final")
+    check_states(ck.cpu().numpy(), ck_ref, "checkpoint")
+
+
+def test_prefill_segments_varlen_with_empty_segments():
+    """Several sequences, one empty and some shorter than the segment count
+    (empty segments: transition = identity, local = zero)."""
+    lengths = [300, 0, 77, 500, 31]
+    H, D, P = 2, 128, 6
+    print(f"case: segments varlen P={P}", flush=True)
+    inp = make_inputs(sum(lengths), H, D, seed=191, lengths=lengths, initial_state=True)
+    o, fin, ck = kda.prefill(to_dev(inp.q, torch.bfloat16), to_dev(inp.k, torch.bfloat16),
+                             to_dev(inp.v, torch.bfloat16), to_dev(inp.g), to_dev(inp.beta),
+                             cu_seqlens=inp.cu_seqlens, initial_state=to_dev(inp.initial_state),
+                             ckpt_interval=32, options=kda.Options(segments=P))
+    torch.cuda.synchronize()
+    o_ref, f_ref, ck_ref = oracle(inp, ckpt=32)
+    check_outputs(o.float().cpu().numpy(), o_ref, inp.cu_seqlens, H)
+    check_states(fin.cpu().numpy(), f_ref, "final")
+    check_states(ck.cpu().numpy(), ck_ref, "checkpoint")
+
+
+def test_prefill_segments_deltanet():
+    """No decay: the transitions run on the hi/lo chain; forced 4 segments."""
+    T, H, D = 700, 2, 128
+    print("case: segments DeltaNet", flush=True)
+    inp = make_inputs(T, H, D, seed=197, lengths=[T], initial_state=True)
+    o, fin, _ = kda.prefill(to_dev(inp.q, torch.bfloat16), to_dev(inp.k, torch.bfloat16),
+                            to_dev(inp.v, torch.bfloat16), None, to_dev(inp.beta), cu_seqlens=inp.cu_seqlens,
+                            initial_state=to_dev(inp.initial_state),
+                            options=kda.Options(gate=kda.GATE_NONE, segments=4))
+    torch.cuda.synchronize()
+    gc = var_oracle.gate_per_channel(None, var_oracle.GATE_NONE, inp.q.shape)
+    o_ref, f_ref, _ = reference.prefill(inp.q, inp.k, inp.v, gc, inp.beta, cu_seqlens=inp.cu_seqlens,
+                                        initial_state=inp.initial_state)
+    check_outputs(o.float().cpu().numpy(), o_ref, inp.cu_seqlens, H)
+    check_states(fin.cpu().numpy(), f_ref, "final")
+
+
+def test_prefill_segments_chosen_by_the_library_full_size():
+    """B=1, H=4, T=8192, D=128 (the per-GPU share of 32 heads over 8 GPUs):
+    the library splits the sequence by itself; heads 0 and 3 against the
+    oracle, and every head close to the unsegmented call."""
+    T, H, D = 8192, 4, 128
+    print("case: segments auto H=4 T=8192", flush=True)
+    q, k, v, g, beta, cu, _ = make_inputs_device(T, H, D, seed=211, device=DEV)
+    o, fin, _ = kda.prefill(q, k, v, g, beta, cu_seqlens=cu)
+    o1, fin1, _ = kda.prefill(q, k, v, g, beta, cu_seqlens=cu, options=kda.Options(segments=1))
+    torch.cuda.synchronize()
+    heads = [0, 3]
+    o_ref, f_ref, _ = _sampled_heads_oracle(q, k, v, g, beta, cu, None, heads)
+    check_outputs(o[:, heads].float().cpu().numpy(), o_ref, cu.numpy(), len(heads))
+    check_states(fin[:, heads].cpu().numpy(), f_ref, "final")
+    assert rel_err(fin.cpu().numpy(), fin1.cpu().numpy()) <= 1e-3
+    assert rel_err(o.float().cpu().numpy(), o1.float().cpu().numpy()) <= 2e-2

@@ -8,16 +8,29 @@ import pytest
 
 from gated_delta_rule_109_amd import profiling as P
 
-FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+GRID = {"plan": 1024, "prep": 32 * 256 * 128, "chain": 256 * 448}
+
+
+def grid_of(name):
+    for key, g in GRID.items():
+        if key + "_kernel" in name:
+            return g
+    return 0
 
 
 def write_counters(d, rows):
+    """rows: (kernel, counter, value[, grid]); the grid defaults to the
+    benchmarked call's grid for that kernel."""
     os.makedirs(d, exist_ok=True)
     with open(os.path.join(d, "kda_counter_collection.csv"), "w", newline="") as fh:
         w = csv.DictWriter(fh, FIELDS)
         w.writeheader()
-        for i, (k, c, v) in enumerate(rows):
-            w.writerow({"Dispatch_Id": i, "Kernel_Name": k, "Counter_Name": c, "Counter_Value": v})
+        for i, row in enumerate(rows):
+            k, c, v = row[:3]
+            grid = row[3] if len(row) > 3 else grid_of(k)
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": k, "Grid_Size": grid, "Counter_Name": c,
+                        "Counter_Value": v})
 
 
 PLAN = "kda::plan_kernel(int const*, int)"
@@ -32,7 +45,8 @@ def test_traffic_summary_scales_by_the_calibration_kernel(tmp_path):
     # the calibration kernel reads and writes 256 MiB; the counters read half
     # of that for FETCH_SIZE and all of it for WRITE_SIZE
     write_counters(f, [(ABS, "FETCH_SIZE", 128 * 1024), (PLAN, "FETCH_SIZE", 1), (PREP, "FETCH_SIZE", 1000),
-                       (PREP_GEN, "FETCH_SIZE", 5000), (CHAIN, "FETCH_SIZE", 2000), (CHAIN, "FETCH_SIZE", 4000)])
+                       (PREP_GEN, "FETCH_SIZE", 5000), (CHAIN, "FETCH_SIZE", 2000), (CHAIN, "FETCH_SIZE", 4000),
+                       (CHAIN, "FETCH_SIZE", 99999, 4 * 8 * 448)])      # a smaller call: not counted
     write_counters(w, [(ABS, "WRITE_SIZE", 256 * 1024), (PLAN, "WRITE_SIZE", 1), (PREP, "WRITE_SIZE", 300),
                        (PREP_GEN, "WRITE_SIZE", 9), (CHAIN, "WRITE_SIZE", 100)])
     res = P.summarize(f, w, 256)
@@ -41,7 +55,7 @@ def test_traffic_summary_scales_by_the_calibration_kernel(tmp_path):
     # chain fetch averaged over its two dispatches
     want = (2 * (1 + 1000 + 3000) + (1 + 300 + 100)) * 1024
     assert res["bytes_per_call"] == pytest.approx(want)
-    assert [r[0] for r in res["others"]] == ["kda::prep_kernel<128, unsigned short, true>"]
+    assert [r[0][0] for r in res["others"]] == ["kda::prep_kernel<128, unsigned short, true>"]
 
 
 def test_traffic_record_follows_the_sources(tmp_path):
