@@ -34,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from gated_delta_rule_109_amd import kda, profiling  # noqa: E402
-from gated_delta_rule_109_amd.workloads import make_inputs, make_inputs_device  # noqa: E402
+from gated_delta_rule_109_amd.workloads import make_inputs, make_inputs_device, varlen_lengths  # noqa: E402
 
 # rocprofv3 byte-counter summary of the prefill (HBM bytes per call); used for
 # roofline.traffic only while it matches the current kernel sources.
@@ -148,32 +148,9 @@ def cpu_baseline(T, H, D, heads):
                       f"heads), {passes} passes; tokens/s scaled by {heads}/{H}", "seconds": round(dt, 3)}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=50,
-                    help="untimed steps first (the clocks take a few dozen calls to settle)")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0 = auto)")
-    ap.add_argument("--calibrate", type=int, default=0, metavar="MIB",
-                    help="before timing, run torch.abs over a float32 tensor of MIB MiB (a kernel of known "
-                         "size for calibrating rocprofv3 byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(heads and sequences shard across GPUs with no exchange; see the design notes)",
-              file=sys.stderr)
-        sys.exit(2)
-
-    dev = torch.device("cuda:0")
-    if args.calibrate > 0:
-        a = torch.ones(args.calibrate * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            torch.abs(a, out=b)
-        torch.cuda.synchronize()
-        del a, b
+def bench_prefill(args, dev, flush):
+    """The benchmarked call: B=1, H=32, T=8192, D=128. Returns the headline
+    fields and the inputs (reused by the side figures)."""
     T, H, D = 8192, 32, 128
     q, k, v, g, beta, cu, _ = make_inputs_device(T, H, D, seed=2, device=dev)
     plan = kda.make_plan(cu, H, D, dev)
@@ -183,27 +160,59 @@ def main():
     def step():
         kda.prefill(q, k, v, g, beta, plan=plan, o=o, final_state=fin)
 
-    flush = Flush(dev)
     torch.cuda.synchronize()
     wall, ms = time_events(step, args.steps, args.warmup, flush)
     ev_ms = float(np.mean(ms))
-    ms_step = ev_ms
     flops = prefill_flops(T, H, D)
     nbytes = prefill_bytes(T, H, D)
-    tokens_per_s = T / (ms_step * 1e-3)
     _, bb = time_events(step, args.steps, 5)                 # back to back, no flush
-    bb_ms = float(np.mean(bb))
+    ach_gbps = nbytes / (ev_ms * 1e-3) / 1e9
+    tr = profiling.read_record(TRAFFIC_PROFILE)
+    rec = {
+        "metric": "KDA prefill tokens/s (B=1, H=32, T=8192, D=128)",
+        "value": round(T / (ev_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ev_ms, 4),
+        "timing": "mean of per-call HIP-event times; a 1 GiB read evicts L2 and the MALL before every call",
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, device-generated; q,k L2-normalised, g floored at ln 0.5)",
+        "config": {"workload": "single-sequence KDA prefill", "batch": 1, "heads": H, "seq_len": T,
+                   "head_dim": D, "chunk": C, "chain_step_tokens": 2 * C, "initial_state": False},
+        "roofline": {"kernel": "kda_prefill_chunked (plan + prep + chain kernels, one C-ABI call)",
+                     "bound": "hbm", "achieved": round(ach_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(ach_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": tr["bytes_per_call"] if tr else None,
+                     "algorithmic_bytes_per_launch": nbytes, "launch_ms": round(ev_ms, 4)},
+        "back_to_back_ms": round(float(np.mean(bb)), 4),
+        "wall_s_timed_steps": round(wall, 4),
+        "prefill_tflops": round(flops / (ev_ms * 1e-3) / 1e12, 2),
+        "prefill_mfma_frac_of_peak": round(flops / (ev_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+    }
+    return rec, (q, k, v, g, beta, plan, o, fin)
 
+
+def bench_prefill_side(args, dev, flush, inputs):
+    """Side figures on prefill: the front end, the gate variants, 4 heads with
+    and without segments, and the packed varlen append-prefill."""
+    T, H, D = 8192, 32, 128
+    q, k, v, g, beta, plan, o, fin = inputs
+    rec = {}
     # the same prefill from raw projections, with the fused front end
     rq, rk, rv, rg, rbeta, _, _ = make_inputs_device(T, H, D, seed=2, device=dev, raw=True)
     fe = kda.Options(kda.FE_ALL, 1e-6)
-
-    def fstep():
-        kda.prefill(rq, rk, rv, rg, rbeta, plan=plan, o=o, final_state=fin, options=fe)
-
-    _, fms = time_events(fstep, args.steps, args.warmup, flush)
+    _, fms = time_events(lambda: kda.prefill(rq, rk, rv, rg, rbeta, plan=plan, o=o, final_state=fin, options=fe),
+                         args.steps, args.warmup, flush)
     f_ms = float(np.mean(fms))
     del rq, rk, rv, rg, rbeta
+    rec["prefill_front_end"] = {"workload": "the same prefill from raw q, k and gate/beta logits "
+                                            "(L2 norm, -softplus gate, sigmoid beta fused into the prep kernel)",
+                                "launch_ms": round(f_ms, 4), "tokens_per_s": round(T / (f_ms * 1e-3), 1)}
 
     # the same prefill for Gated DeltaNet (one decay per token and head) and DeltaNet (no decay)
     g_head = g[..., 0].contiguous()
@@ -214,6 +223,9 @@ def main():
                                                 options=opt), args.steps, args.warmup, flush)
         vms[name] = float(np.mean(ts))
     del g_head
+    rec["prefill_variants"] = {"workload": "the same prefill for Gated DeltaNet (g [T, H]) and DeltaNet (no g)",
+                               "gdn_launch_ms": round(vms["gdn"], 4),
+                               "deltanet_launch_ms": round(vms["deltanet"], 4)}
 
     # the per-GPU share of 32 heads over 8 GPUs: 4 heads, the same sequence length.
     # The chain then fills 32 of 256 compute units; the library splits the
@@ -229,9 +241,33 @@ def main():
                                                 options=opt), args.steps, args.warmup, flush)
         seg_ms[name] = float(np.mean(ts))
     del q4, k4, v4, g4, b4
+    rec["prefill_4_heads"] = {"workload": "B=1, H=4, T=8192, D=128 (32 heads over 8 GPUs, one GPU's share)",
+                              "one_segment_ms": round(seg_ms["one_segment"], 4),
+                              "library_choice_ms": round(seg_ms["library_choice"], 4),
+                              "segments_speedup": round(seg_ms["one_segment"] / seg_ms["library_choice"], 3)}
 
-    # decode: 256 sequences x 32 heads
-    N = 256
+    # append-prefill over packed varlen input: 16 sequences (lognormal lengths,
+    # median 4096, clipped to [1, 32768]) with cached fp32 initial states
+    vl = varlen_lengths()
+    vq, vk, vv, vg, vb, vcu, vs0 = make_inputs_device(sum(vl), H, D, seed=6, device=dev, lengths=vl,
+                                                      initial_state=True)
+    vplan = kda.make_plan(vcu, H, D, dev)
+    vo = torch.empty_like(vv)
+    vfin = torch.empty(len(vl), H, D, D, dtype=torch.float32, device=dev)
+    _, vts = time_events(lambda: kda.prefill(vq, vk, vv, vg, vb, plan=vplan, initial_state=vs0, o=vo,
+                                             final_state=vfin), max(args.steps // 4, 3),
+                         max(args.warmup // 10, 2), flush)
+    var_ms = float(np.mean(vts))
+    del vq, vk, vv, vg, vb, vs0, vo, vfin, vplan
+    rec["prefill_varlen"] = {"workload": f"16 packed sequences, {sum(vl)} tokens (longest {max(vl)}), H=32, "
+                                         "D=128, cached initial states",
+                             "launch_ms": round(var_ms, 4), "tokens_per_s": round(sum(vl) / (var_ms * 1e-3), 1)}
+    return rec
+
+
+def bench_decode(args, dev, flush):
+    """256 sequences x 32 heads, D=128: one token per call, and 4 per call."""
+    N, H, D = 256, 32, 128
     dq, dk, dv, dg, dbeta, _, ds0 = make_inputs_device(N, H, D, seed=3, device=dev, lengths=[1] * N,
                                                        initial_state=True)
     state = ds0.contiguous()
@@ -243,9 +279,13 @@ def main():
     _, dms = time_events(dstep, max(args.steps, 20), args.warmup, flush)
     d_ms = float(np.mean(dms))
     _, dbb = time_events(dstep, max(args.steps, 20), 5)
-    d_bb_ms = float(np.mean(dbb))
-    d_bytes = 8 * D * D * N * H
-    d_gbps = d_bytes / (d_ms * 1e-3) / 1e9
+    d_gbps = 8 * D * D * N * H / (d_ms * 1e-3) / 1e9
+    rec = {"decode": {"workload": "256 sequences x 32 heads, D=128, one token, fp32 states in place",
+                      "ms": round(d_ms, 4), "back_to_back_ms": round(float(np.mean(dbb)), 4),
+                      "head_tokens_per_s": round(N * H / (d_ms * 1e-3), 1),
+                      "GBps": round(d_gbps, 1), "hbm_frac": round(d_gbps / HBM_PEAK_GBPS, 4),
+                      "tflops": round(7 * D * D * N * H / (d_ms * 1e-3) / 1e12, 3)}}
+    del dq, dk, dv, dg, dbeta, state, dout
 
     # multi-token decode: the same 256 x 32 heads, 4 draft tokens each, all committed
     TD = 4
@@ -255,66 +295,62 @@ def main():
     tbeta = tbeta.view(N, TD, H)
     tstate = ts0.contiguous()
     tout = torch.empty_like(tv)
-
-    def tstep():
-        kda.decode_tokens(tq, tk, tv, tg, tbeta, tstate, o=tout)
-
-    _, tms = time_events(tstep, max(args.steps, 20), args.warmup, flush)
+    _, tms = time_events(lambda: kda.decode_tokens(tq, tk, tv, tg, tbeta, tstate, o=tout),
+                         max(args.steps, 20), args.warmup, flush)
     t_ms = float(np.mean(tms))
     # per head: fp32 state in and out, and per token bf16 q, k, v, o, fp32 g, beta
-    t_bytes = N * H * (8 * D * D + TD * (4 * 2 * D + 4 * D + 4))
-    t_gbps = t_bytes / (t_ms * 1e-3) / 1e9
+    t_gbps = N * H * (8 * D * D + TD * (4 * 2 * D + 4 * D + 4)) / (t_ms * 1e-3) / 1e9
+    rec["decode_tokens"] = {"workload": f"256 sequences x 32 heads, D=128, {TD} tokens per sequence "
+                                        "in one call, all committed",
+                            "ms": round(t_ms, 4), "head_tokens_per_s": round(N * H * TD / (t_ms * 1e-3), 1),
+                            "GBps": round(t_gbps, 1), "hbm_frac": round(t_gbps / HBM_PEAK_GBPS, 4),
+                            "ms_per_token": round(t_ms / TD, 4)}
+    return rec
 
-    ach_gbps = nbytes / (ev_ms * 1e-3) / 1e9
-    tr = profiling.read_record(TRAFFIC_PROFILE)
-    rec = {
-        "metric": "KDA prefill tokens/s (B=1, H=32, T=8192, D=128)",
-        "value": round(tokens_per_s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "timing": "mean of per-call HIP-event times; a 1 GiB read evicts L2 and the MALL before every call",
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded, device-generated; q,k L2-normalised, g floored at ln 0.5)",
-        "config": {"workload": "single-sequence KDA prefill", "batch": 1, "heads": H, "seq_len": T,
-                   "head_dim": D, "chunk": C, "chain_step_tokens": 2 * C, "initial_state": False},
-        "roofline": {"kernel": "kda_prefill_chunked (plan + prep + chain kernels, one C-ABI call)",
-                     "bound": "hbm", "achieved": round(ach_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(ach_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": tr["bytes_per_call"] if tr else None,
-                     "algorithmic_bytes_per_launch": nbytes, "launch_ms": round(ev_ms, 4)},
-        "back_to_back_ms": round(bb_ms, 4),
-        "wall_s_timed_steps": round(wall, 4),
-        "prefill_tflops": round(flops / (ev_ms * 1e-3) / 1e12, 2),
-        "prefill_mfma_frac_of_peak": round(flops / (ev_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-        "prefill_front_end": {"workload": "the same prefill from raw q, k and gate/beta logits "
-                                          "(L2 norm, -softplus gate, sigmoid beta fused into the prep kernel)",
-                              "launch_ms": round(f_ms, 4), "tokens_per_s": round(T / (f_ms * 1e-3), 1)},
-        "prefill_variants": {"workload": "the same prefill for Gated DeltaNet (g [T, H]) and DeltaNet (no g)",
-                             "gdn_launch_ms": round(vms["gdn"], 4), "deltanet_launch_ms": round(vms["deltanet"], 4)},
-        "prefill_4_heads": {"workload": "B=1, H=4, T=8192, D=128 (32 heads over 8 GPUs, one GPU's share)",
-                            "one_segment_ms": round(seg_ms["one_segment"], 4),
-                            "library_choice_ms": round(seg_ms["library_choice"], 4),
-                            "segments_speedup": round(seg_ms["one_segment"] / seg_ms["library_choice"], 3)},
-        "decode": {"workload": "256 sequences x 32 heads, D=128, one token, fp32 states in place",
-                   "ms": round(d_ms, 4), "back_to_back_ms": round(d_bb_ms, 4), "head_tokens_per_s": round(N * H / (d_ms * 1e-3), 1),
-                   "GBps": round(d_gbps, 1), "hbm_frac": round(d_gbps / HBM_PEAK_GBPS, 4),
-                   "tflops": round(7 * D * D * N * H / (d_ms * 1e-3) / 1e12, 3)},
-        "decode_tokens": {"workload": f"256 sequences x 32 heads, D=128, {TD} tokens per sequence "
-                                      "in one call, all committed",
-                          "ms": round(t_ms, 4), "head_tokens_per_s": round(N * H * TD / (t_ms * 1e-3), 1),
-                          "GBps": round(t_gbps, 1), "hbm_frac": round(t_gbps / HBM_PEAK_GBPS, 4),
-                          "ms_per_token": round(t_ms / TD, 4)},
-    }
-    rec["measured_peaks"] = measured_peaks(dev, flush)
-    if not args.no_cpu:
-        heads = args.cpu_heads or H
-        rec["cpu_baseline"] = cpu_baseline(T, H, D, heads)
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first (the clocks take a few dozen calls to settle)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0 = auto)")
+    ap.add_argument("--calibrate", type=int, default=0, metavar="MIB",
+                    help="before timing, run torch.abs over a float32 tensor of MIB MiB (a kernel of known "
+                         "size for calibrating rocprofv3 byte counters)")
+    ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
+                    help="run only the benchmarked prefill call (and the measured peaks), or only decode "
+                         "(for counter passes that must see one workload)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(heads and sequences shard across GPUs with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    dev = torch.device("cuda:0")
+    if args.calibrate > 0:
+        a = torch.ones(args.calibrate * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.abs(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
+    flush = Flush(dev)
+    rec = {}
+    if args.only in ("all", "prefill"):
+        head, inputs = bench_prefill(args, dev, flush)
+        rec.update(head)
+        if args.only == "all":
+            rec.update(bench_prefill_side(args, dev, flush, inputs))
+        del inputs
+    if args.only in ("all", "decode"):
+        rec.update(bench_decode(args, dev, flush))
+    if args.only in ("all", "prefill"):
+        rec["measured_peaks"] = measured_peaks(dev, flush)
+    if args.only == "all" and not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(8192, 32, 128, args.cpu_heads or 32)
     print(json.dumps(rec), flush=True)
 
 

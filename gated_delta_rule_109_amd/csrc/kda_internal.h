@@ -58,6 +58,7 @@ struct PrefillLayout {
   size_t seq_blk_off;     // int32 [N + 1]
   size_t seq_ck_off;      // int32 [N + 1]
   size_t blk_info;        // int2  [total_blocks] (first token, valid tokens)
+  size_t seq_order;       // int32 [N] sequences by block count, longest first
   size_t records;         // per (block, head) operand records
   size_t record_bytes;    // bytes of one record
   size_t segs;            // fp32 [N][KDA_MAX_SEGMENTS][H][3][D][D] segment states, or 0

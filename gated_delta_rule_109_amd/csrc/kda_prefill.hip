@@ -110,6 +110,7 @@ PrefillLayout prefill_layout(int32_t num_seqs, int64_t total_blocks, int32_t H, 
   L.seq_blk_off = off; off = align256(off + sizeof(int32_t) * (size_t)(num_seqs + 1));
   L.seq_ck_off = off;  off = align256(off + sizeof(int32_t) * (size_t)(num_seqs + 1));
   L.blk_info = off;    off = align256(off + 2 * sizeof(int32_t) * (size_t)total_blocks);
+  L.seq_order = off;   off = align256(off + sizeof(int32_t) * (size_t)num_seqs);
   L.records = off;
   L.record_bytes = record_bytes(D);
   off = align256(off + L.record_bytes * (size_t)total_blocks * (size_t)H);
@@ -123,10 +124,12 @@ PrefillLayout prefill_layout(int32_t num_seqs, int64_t total_blocks, int32_t H, 
 }
 
 // ---- 1. plan ----------------------------------------------------------------------
+constexpr int kMaxSortedSeqs = 1024;   // longest-first chain order up to this many sequences
+
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu, int N,
                                                     int ckpt_interval, int32_t* seq_blk_off,
                                                     int32_t* seq_ck_off, int2* blk_info,
-                                                    int total_blocks) {
+                                                    int total_blocks, int32_t* seq_order) {
   __shared__ int s_c[1024], s_k[1024];
   __shared__ int carry_c, carry_k;
   const int tid = threadIdx.x;
@@ -174,6 +177,25 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     const int t0 = cu[lo] + kBT * (c - seq_blk_off[lo]);
     const int cnt = min(kBT, cu[lo + 1] - t0);
     blk_info[c] = make_int2(t0, cnt);
+  }
+  // Chain order: sequences by block count, longest first (ties by index), so
+  // that when the chain's workgroups outnumber the compute units the longest
+  // recurrences start first. Ranked by counting over block counts in LDS for
+  // N <= kMaxSortedSeqs; beyond that, the given order.
+  __shared__ int s_nb[kMaxSortedSeqs];
+  const bool sorted = N <= kMaxSortedSeqs;
+  if (sorted) {
+    for (int n = tid; n < N; n += 1024) s_nb[n] = seq_blk_off[n + 1] - seq_blk_off[n];
+    __syncthreads();
+  }
+  for (int n = tid; n < N; n += 1024) {
+    int rank = n;
+    if (sorted) {
+      const int bn = s_nb[n];
+      rank = 0;
+      for (int m = 0; m < N; ++m) rank += s_nb[m] > bn || (s_nb[m] == bn && m < n);
+    }
+    seq_order[rank] = n;
   }
 }
 
@@ -560,7 +582,8 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     const int32_t* __restrict__ seq_blk_off, const int32_t* __restrict__ seq_ck_off,
     const char* __restrict__ records, const float* initial_state, float* final_state,
     float* __restrict__ ckpts, TIn* __restrict__ o, int N, int H, int ckpt_interval,
-    float scale, int total_blocks, float* __restrict__ segs, int P, int pass) {
+    float scale, int total_blocks, float* __restrict__ segs, int P, int pass,
+    const int32_t* __restrict__ seq_order) {
   using Cfg = ChainCfg<D, TIn>;
   using R = Rec<D>;
   constexpr int NCW = Cfg::kHalves;
@@ -573,13 +596,21 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   // pass 0 runs segment 0 in full and, for every middle segment, its local
   // state (zero start) and its transition (identity start, zero values);
   // pass 1 runs segments 1 .. P-1 in full from the scanned start states.
-  const int NH = N * H;
+  //
+  // Placement: units are ranked with the longest sequences first (seq_order),
+  // and workgroup b takes rank 8 (b / (8 S)) + b % 8 and slice (b / 8) % S of
+  // the S = D / 16 slices. So the slices of a unit run on one XCD (b mod 8),
+  // sharing the records through its L2, and the longest recurrences start
+  // first. Grid slots past the last unit have nothing to do.
+  constexpr int S = D / 16;
   const int U = P == 1 ? 1 : (pass == 0 ? 2 * P - 3 : P - 1);
-  const int NU = NH * U;
+  const int NU = N * H * U;
   const int b = blockIdx.x;
-  const int s = b / NU, q = b % NU;   // the slices of one unit share an XCD when NU % 8 == 0
-  const int nh = q % NH, u = q / NH;
-  const int n = nh / H, h = nh % H;
+  const int s = (b / 8) % S, rank = 8 * (b / (8 * S)) + b % 8;
+  if (rank >= NU) return;
+  const int n = seq_order[rank / (H * U)];
+  const int u = (rank / H) % U, h = rank % H;
+  const int nh = n * H + h;
   int seg = 0, mode = kUnitFull;
   if (P > 1) {
     if (pass == 0) {
@@ -954,30 +985,35 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ segs, int
   auto seg_state = [&](int p, int kind) __attribute__((always_inline)) {
     return segs + ((((size_t)n * KDA_MAX_SEGMENTS + p) * H + h) * 3 + kind) * D * D;
   };
-  __shared__ float X[D][16];                         // S_in(p - 1), this slice's columns
+  // M of the step, staged with coalesced float4 loads (rows padded by 16
+  // bytes against bank conflicts), and S_in(p - 1) for this slice's columns
+  __shared__ __attribute__((aligned(16))) float sM[D][D + 4];
+  __shared__ float X[D][16];
   for (int e = tid; e < D * 16; e += 256) X[e / 16][e % 16] = seg_state(1, 0)[(size_t)(e / 16) * D + 16 * s + e % 16];
-  __syncthreads();
   for (int p = 2; p < P; ++p) {
-    const float* M = seg_state(p - 1, 2) + (size_t)r * D;
+    const f32x4* M4 = (const f32x4*)seg_state(p - 1, 2);
+    __syncthreads();                                 // X written, sM free
+    for (int e = tid; e < D * D / 4; e += 256) *(f32x4*)&sM[e / (D / 4)][4 * (e % (D / 4))] = M4[e];
     const float* Lc = seg_state(p - 1, 1) + (size_t)r * D + 16 * s + c0;
     float y[kOut];
 #pragma unroll
     for (int c = 0; c < kOut; ++c) y[c] = Lc[c];
+    __syncthreads();
+#pragma unroll 4
     for (int k4 = 0; k4 < D; k4 += 4) {
-      const f32x4 m4 = *(const f32x4*)(M + k4);
+      const f32x4 m4 = *(const f32x4*)&sM[r][k4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int c = 0; c < kOut; ++c) y[c] += m4[kk] * X[k4 + kk][c0 + c];
     }
-    __syncthreads();
+    __syncthreads();                                 // every read of X done
     float* out = seg_state(p, 0) + (size_t)r * D + 16 * s + c0;
 #pragma unroll
     for (int c = 0; c < kOut; ++c) {
       X[r][c0 + c] = y[c];
       out[c] = y[c];
     }
-    __syncthreads();
   }
 }
 
@@ -990,8 +1026,9 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   int2* blk_info = (int2*)(ws + L.blk_info);
   char* records = ws + L.records;
 
+  int32_t* seq_order = (int32_t*)(ws + L.seq_order);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, a.num_seqs,
-                     a.ckpt_interval, seq_blk_off, seq_ck_off, blk_info, (int)a.total_blocks);
+                     a.ckpt_interval, seq_blk_off, seq_ck_off, blk_info, (int)a.total_blocks, seq_order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.total_blocks > 0) {
@@ -1010,14 +1047,16 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   }
   using Cfg = ChainCfg<D, TIn>;
   const int64_t slices = (int64_t)a.num_seqs * a.H * (D / 16);   // one workgroup per 16-column slice
+  const int64_t nh = (int64_t)a.num_seqs * a.H;
   const int P = a.segments;
   float* segs = P > 1 ? (float*)(ws + L.segs) : nullptr;
   auto chain = a.gate == KDA_GATE_NONE ? chain_kernel<D, TIn, true> : chain_kernel<D, TIn, false>;
   auto run_chain = [&](int units, int pass) {
-    hipLaunchKernelGGL(chain, dim3((unsigned)(slices * units)), dim3(Cfg::kThreads), 0, a.stream,
+    const int64_t groups = (nh * units + 7) / 8;     // 8 units x D/16 slices per group of workgroups
+    hipLaunchKernelGGL(chain, dim3((unsigned)(groups * 8 * (D / 16))), dim3(Cfg::kThreads), 0, a.stream,
                        (const TIn*)a.v, a.cu_seqlens, seq_blk_off, seq_ck_off, records, a.initial_state,
                        a.final_state, a.checkpoints, (TIn*)a.o, a.num_seqs, a.H, a.ckpt_interval,
-                       a.scale, (int)a.total_blocks, segs, P, pass);
+                       a.scale, (int)a.total_blocks, segs, P, pass, seq_order);
     return hipGetLastError();
   };
   if (P == 1) return run_chain(1, 0);

@@ -42,6 +42,15 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 PREFILL_KERNELS = (("kda::plan_kernel", 1024),
                    ("kda::prep_kernel<128, unsigned short, false>", 32 * 256 * 128),
                    ("kda::chain_kernel<128, unsigned short, false>", 256 * 448))
+# one kda_decode_step over 256 sequences x 32 heads at D = 128 (one workgroup of
+# 256 threads per head)
+DECODE_KERNELS = (("kda::decode_kernel<128, unsigned short, true, false>", 256 * 32 * 256),)
+WORKLOADS = {
+    "prefill": (PREFILL_KERNELS, "KDA prefill HBM traffic (B=1, H=32, T=8192, D=128, bf16 q/k/v)",
+                "kda_prefill_chunked"),
+    "decode": (DECODE_KERNELS, "KDA decode HBM traffic (256 sequences x 32 heads, D=128, one token, bf16 q/k/v)",
+               "kda_decode_step"),
+}
 CALIB_KERNEL = "AbsFunctor"
 
 
@@ -88,7 +97,7 @@ def per_kernel(d, counter):
     return {k: (n, s / n) for k, (n, s) in acc.items()}
 
 
-def summarize(fetch_dir, write_dir, calib_mib):
+def summarize(fetch_dir, write_dir, calib_mib, kernels=PREFILL_KERNELS):
     f = per_kernel(fetch_dir, "FETCH_SIZE")
     w = per_kernel(write_dir, "WRITE_SIZE")
     calib_kib = calib_mib * 1024.0
@@ -99,7 +108,7 @@ def summarize(fetch_dir, write_dir, calib_mib):
     fw = calib_kib / w[cal][1]
     rows = []
     total = 0.0
-    for k in PREFILL_KERNELS:
+    for k in kernels:
         if k not in f or k not in w:
             raise RuntimeError(f"{k} missing from the counter runs")
         fb = f[k][1] * ff * 1024
@@ -107,13 +116,14 @@ def summarize(fetch_dir, write_dir, calib_mib):
         total += fb + wb
         rows.append((k, f[k][0], f[k][1], w[k][1], fb, wb))
     others = [(k, f[k][0], f[k][1], w[k][1], f[k][1] * ff * 1024, w[k][1] * fw * 1024)
-              for k in sorted(f) if k in w and k not in PREFILL_KERNELS and k != cal]
+              for k in sorted(f) if k in w and k not in kernels and k != cal]
     return {"fetch_factor": ff, "write_factor": fw, "rows": rows, "others": others,
             "bytes_per_call": total, "calib": (f[cal][1], w[cal][1])}
 
 
-def render(res, calib_mib, command, algorithmic_bytes):
-    out = ["# KDA prefill HBM traffic (B=1, H=32, T=8192, D=128, bf16 q/k/v)", "",
+def render(res, calib_mib, command, algorithmic_bytes, title=WORKLOADS["prefill"][1],
+           call=WORKLOADS["prefill"][2]):
+    out = [f"# {title}", "",
            "Commands (run from the repository root on one MI355X; one counter per pass):", "", "```"]
     out += [c for c in command]
     out += ["```", "",
@@ -132,7 +142,7 @@ def render(res, calib_mib, command, algorithmic_bytes):
                 "|---|---|---|---|---|---|---|"]
         for (k, grid), n, fk, wk, fb, wb in res["others"]:
             out.append(f"| `{k}` | {grid} | {n} | {fk:.4g} | {wk:.4g} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
-    out += ["", f"HBM bytes per `kda_prefill_chunked` call: {tot / 1e6:.1f} MB, against "
+    out += ["", f"HBM bytes per `{call}` call: {tot / 1e6:.1f} MB, against "
             f"{algorithmic_bytes / 1e6:.1f} MB algorithmic (ratio {tot / algorithmic_bytes:.2f}).", "",
             "traffic-record: " + json.dumps({"bytes_per_call": round(tot), "source_digest": source_digest(),
                                               "fetch_factor": round(res["fetch_factor"], 4),
@@ -153,19 +163,24 @@ def read_record(path):
 
 
 def kernel_stats(d):
-    """[(name, calls, avg us, min us, max us, share %)] of the kda kernels in a
-    rocprofv3 --kernel-trace --stats output directory."""
-    hits = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    """[(name, grid work-items, calls, avg us, min us, max us, share %)] of the
+    kda kernels, one row per kernel and grid, from the per-dispatch
+    kernel_trace.csv of a rocprofv3 --kernel-trace run (share: of all kernel
+    time in the trace)."""
+    hits = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
     if not hits:
-        raise FileNotFoundError(f"no kernel_stats.csv under {d}")
-    rows = []
+        raise FileNotFoundError(f"no kernel_trace.csv under {d}")
+    acc, total = {}, 0.0
     for r in csv.DictReader(open(hits[0])):
-        if "kda::" not in r["Name"]:
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        total += dur
+        if "kda::" not in r["Kernel_Name"]:
             continue
-        name = kernel_key(r["Name"])
-        rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
-                     float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
-    return rows
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        acc.setdefault((kernel_key(r["Kernel_Name"]), grid), []).append(dur)
+    rows = [(k, g, len(v), float(np.mean(v)), min(v), max(v), 100.0 * sum(v) / total)
+            for (k, g), v in acc.items()]
+    return sorted(rows, key=lambda r: -r[6])
 
 
 MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE")
@@ -175,17 +190,19 @@ PEAK_KERNEL = "mfma_loop"   # the reference loop of libkda_peak.so
 
 
 def mfma_summary(d):
-    """[(kernel, dispatches, MFMA busy %, bf16 MFMA GFLOP per dispatch)]: busy
+    """[(kernel, grid work-items, dispatches, MFMA busy %, bf16 MFMA GFLOP per
+    dispatch)], one row per kernel and grid: busy
     cycles over all SIMDs / (GPU-active cycles of one XCD x SIMD_NUM); FLOPs =
     MOPS x 512. The CSV holds GRBM_GUI_ACTIVE summed over the XCDs, so it is
     divided by XCD_NUM (the vendor's MfmaUtil takes its maximum over them)."""
     acc = {}
     for r in csv.DictReader(open(_counter_csv(d))):
         name = r["Kernel_Name"]
+        grid = int(float(r.get("Grid_Size") or 0))
         if "kda::" in name:
-            key = kernel_key(name)
+            key = (kernel_key(name), grid)
         elif PEAK_KERNEL in name:
-            key = kernel_key(name.replace("(anonymous namespace)::", "")) + " (reference loop)"
+            key = (kernel_key(name.replace("(anonymous namespace)::", "")) + " (reference loop)", grid)
         else:
             continue
         c = r["Counter_Name"]
@@ -201,7 +218,7 @@ def mfma_summary(d):
         busy = np.mean(per["SQ_VALU_MFMA_BUSY_CYCLES"])
         active = np.mean(per["GRBM_GUI_ACTIVE"]) / XCD_NUM
         flops = np.mean(per["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) * 512
-        rows.append((key, n, 100.0 * busy / (active * SIMD_NUM), flops / 1e9))
+        rows.append((key[0], key[1], n, 100.0 * busy / (active * SIMD_NUM), flops / 1e9))
     return rows
 
 
@@ -214,9 +231,10 @@ def render_mfma(rows, title, command):
             "bf16 MFMA FLOPs = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512. This counts every MFMA the kernels issue "
             "(hi/lo split terms and padding included), not the model FLOPs. The reference loop "
             "(independent MFMA chains, libkda_peak.so; <0> = 16x16x32, <1> = 32x32x16) shows what the counter reads for a matrix-bound kernel.",
-            "", "| kernel | dispatches | MFMA busy % | bf16 MFMA GFLOP per dispatch |", "|---|---|---|---|"]
-    for key, n, util, gf in rows:
-        out.append(f"| `{key}` | {n} | {util:.2f} | {gf:.2f} |")
+            "", "| kernel | grid (work-items) | dispatches | MFMA busy % | bf16 MFMA GFLOP per dispatch |",
+            "|---|---|---|---|---|"]
+    for key, grid, n, util, gf in rows:
+        out.append(f"| `{key}` | {grid} | {n} | {util:.2f} | {gf:.2f} |")
     return "\n".join(out) + "\n"
 
 
@@ -225,9 +243,9 @@ def render_stats(rows, title, command, bench_line):
     out += list(command)
     out += ["```", "", "rocprofv3 kernel statistics of the kda kernels (durations in microseconds; share is "
             "of all GPU kernel time in the run, input generation included):", "",
-            "| kernel | calls | average | min | max | share |", "|---|---|---|---|---|---|"]
-    for name, n, avg, mn, mx, pct in rows:
-        out.append(f"| `{name}` | {n} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.1f} % |")
+            "| kernel | grid (work-items) | calls | average | min | max | share |", "|---|---|---|---|---|---|---|"]
+    for name, grid, n, avg, mn, mx, pct in rows:
+        out.append(f"| `{name}` | {grid} | {n} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.1f} % |")
     if bench_line:
         out += ["", "bench.py line of the same build (no profiler):", "", "```", bench_line.strip(), "```"]
     return "\n".join(out) + "\n"
@@ -241,6 +259,8 @@ def main(argv=None):
     ap.add_argument("--algorithmic-bytes", type=int)
     ap.add_argument("--stats", help="rocprofv3 --kernel-trace --stats output directory (kernel-time summary)")
     ap.add_argument("--mfma", help="rocprofv3 --pmc output directory with the MFMA counters")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="prefill",
+                    help="which call the byte-counter summary adds up")
     ap.add_argument("--title", default="KDA kernels")
     ap.add_argument("--bench-line", help="file whose last line is the bench.py JSON line")
     ap.add_argument("--command", action="append", default=[])
@@ -254,7 +274,9 @@ def main(argv=None):
     else:
         if not (a.fetch and a.write and a.calib_mib and a.algorithmic_bytes):
             ap.error("--fetch, --write, --calib-mib and --algorithmic-bytes are required")
-        text = render(summarize(a.fetch, a.write, a.calib_mib), a.calib_mib, a.command, a.algorithmic_bytes)
+        kernels, title, call = WORKLOADS[a.workload]
+        text = render(summarize(a.fetch, a.write, a.calib_mib, kernels), a.calib_mib, a.command,
+                      a.algorithmic_bytes, title, call)
     if a.out:
         with open(a.out, "w") as fh:
             fh.write(text)

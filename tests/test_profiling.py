@@ -87,9 +87,9 @@ def test_mfma_busy_uses_one_xcd_of_active_cycles(tmp_path):
                        ("void (anonymous namespace)::mfma_loop<1>(float*, int)", "SQ_INSTS_VALU_MFMA_MOPS_BF16", 0),
                        ("void (anonymous namespace)::mfma_loop<1>(float*, int)", "GRBM_GUI_ACTIVE", 8000)])
     rows = {r[0]: r for r in P.mfma_summary(d)}
-    assert rows["kda::chain_kernel<128, unsigned short, false>"][2] == pytest.approx(50.0)
-    assert rows["kda::chain_kernel<128, unsigned short, false>"][3] == pytest.approx(2e6 * 512 / 1e9)
-    assert rows["mfma_loop<1> (reference loop)"][2] == pytest.approx(100.0)
+    assert rows["kda::chain_kernel<128, unsigned short, false>"][3] == pytest.approx(50.0)
+    assert rows["kda::chain_kernel<128, unsigned short, false>"][4] == pytest.approx(2e6 * 512 / 1e9)
+    assert rows["mfma_loop<1> (reference loop)"][3] == pytest.approx(100.0)
 
 
 def test_kernel_key_keeps_template_arguments():
