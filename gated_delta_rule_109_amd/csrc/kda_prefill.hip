@@ -23,14 +23,16 @@
 // first 16 tokens of a block (a checkpoint position when the interval is an
 // odd multiple of 16) is Diag(P_16) S + Diag(P_16 / Pc) Kh[<16]^T delta[<16].
 //
-// Three kernels, all on the caller's stream:
-//  1. plan_kernel   (1 workgroup): per-sequence block / checkpoint offsets and
-//                   a block -> (first token, valid tokens) table.
+// Kernels, all on the caller's stream:
+//  1. plan_kernel   (1 workgroup): per-sequence block / checkpoint offsets, a
+//                   block -> (first token, valid tokens) table, and the
+//                   sequences ranked longest first for the chain's placement.
 //  2. prep_kernel   (one workgroup per block and head, fully parallel): gates,
 //                   decayed operands, A and L on MFMA, T by forward
 //                   substitution; writes one "record" per (block, head) whose
 //                   byte layout is exactly the MFMA operand fragments the chain
-//                   kernel consumes, lane by lane.
+//                   kernel consumes, lane by lane. A second instantiation takes
+//                   the gate layout and the front end at run time.
 //  3. chain_kernel  (one workgroup per sequence, head and 16-column slice of the
 //                   state): the sequential recurrence over blocks. Columns of S
 //                   evolve independently, so each slice runs on its own. The
@@ -38,6 +40,10 @@
 //                   compute waves (half the rows each); loader waves stream
 //                   records into an LDS ring several blocks ahead and an
 //                   output wave forms and stores the output tiles.
+//  4. scan_kernel   (with segments only): when a sequence is split into
+//                   segments that the chain runs side by side, the start state
+//                   of each segment from the segments' transitions and local
+//                   states; the chain then runs once more from those states.
 //
 // Precision: MFMA operands are bf16 with fp32 accumulation. The decayed key of
 // the state update (Kh), T, V - Kp S and delta enter as two-term bf16 splits

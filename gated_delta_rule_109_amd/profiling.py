@@ -54,14 +54,24 @@ WORKLOADS = {
 CALIB_KERNEL = "AbsFunctor"
 
 
+def _code_only(text):
+    """Source text without comments and with whitespace collapsed: a comment
+    or layout change leaves the compiled kernels, and so the digest, alone."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest():
-    """sha256 over the HIP sources and headers the library is built from."""
+    """sha256 over the code (comments dropped) of the HIP sources and headers
+    the library is built from, and of the public header."""
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")) + glob.glob(os.path.join(PKG, "csrc", "*.h")))
+    files.append(os.path.join(os.path.dirname(PKG), "include", "kda.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -95,3 +95,9 @@ def test_mfma_busy_uses_one_xcd_of_active_cycles(tmp_path):
 def test_kernel_key_keeps_template_arguments():
     assert P.kernel_key(CHAIN) == "kda::chain_kernel<128, unsigned short, false>"
     assert P.kernel_key(PLAN) == "kda::plan_kernel"
+
+
+def test_digest_ignores_comments_but_not_code():
+    code = "int f(int a) {  // add one\n  return a + 1; /* done */\n}\n"
+    assert P._code_only(code) == P._code_only("int f(int a) {\n return a + 1;\n}")
+    assert P._code_only(code) != P._code_only(code.replace("a + 1", "a + 2"))
