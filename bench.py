@@ -143,7 +143,16 @@ def cpu_baseline(T, H, D, heads):
         dt = time.perf_counter() - t0
         if dt >= 5.0 or passes >= 50:
             break
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": passes * T * heads / H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model,
             "sample": f"prefill T={T}, {heads} of {H} heads, D={D} (fp64 token recurrence, OpenMP over "
                       f"heads), {passes} passes; tokens/s scaled by {heads}/{H}", "seconds": round(dt, 3)}
 
@@ -189,6 +198,8 @@ def bench_prefill(args, dev, flush):
                      "unit": "GB/s", "frac": round(ach_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": tr["bytes_per_call"] if tr else None,
                      "algorithmic_bytes_per_launch": nbytes, "launch_ms": round(ev_ms, 4)},
+        "launch_ms_stats": {"mean": round(ev_ms, 4), "median": round(float(np.median(ms)), 4),
+                            "min": round(float(np.min(ms)), 4), "max": round(float(np.max(ms)), 4)},
         "back_to_back_ms": round(float(np.mean(bb)), 4),
         "wall_s_timed_steps": round(wall, 4),
         "prefill_tflops": round(flops / (ev_ms * 1e-3) / 1e12, 2),
@@ -259,6 +270,21 @@ def bench_prefill_side(args, dev, flush, inputs):
                          max(args.warmup // 10, 2), flush)
     var_ms = float(np.mean(vts))
     del vq, vk, vv, vg, vb, vs0, vo, vfin, vplan
+    # long prefill with sparse state caching: B=1, H=32, T=131072, a checkpoint
+    # every 32768 tokens
+    TL, CK = 131072, 32768
+    lq, lk, lv, lg, lb, lcu, _ = make_inputs_device(TL, H, D, seed=7, device=dev)
+    lplan = kda.make_plan(lcu, H, D, dev, ckpt_interval=CK)
+    lo = torch.empty_like(lv)
+    lfin = torch.empty(1, H, D, D, dtype=torch.float32, device=dev)
+    lck = torch.empty(TL // CK, H, D, D, dtype=torch.float32, device=dev)
+    _, lts = time_events(lambda: kda.prefill(lq, lk, lv, lg, lb, plan=lplan, o=lo, final_state=lfin,
+                                             checkpoints=lck), 3, 2, flush)
+    long_ms = float(np.mean(lts))
+    del lq, lk, lv, lg, lb, lo, lfin, lck, lplan
+    rec["prefill_long"] = {"workload": "B=1, H=32, T=131072, D=128, a checkpoint every 32768 tokens",
+                           "launch_ms": round(long_ms, 4), "tokens_per_s": round(TL / (long_ms * 1e-3), 1),
+                           "hbm_frac": round(prefill_bytes(TL, H, D) / (long_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
     rec["prefill_varlen"] = {"workload": f"16 packed sequences, {sum(vl)} tokens (longest {max(vl)}), H=32, "
                                          "D=128, cached initial states",
                              "launch_ms": round(var_ms, 4), "tokens_per_s": round(sum(vl) / (var_ms * 1e-3), 1)}
@@ -351,6 +377,7 @@ def main():
         rec["measured_peaks"] = measured_peaks(dev, flush)
     if args.only == "all" and not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(8192, 32, 128, args.cpu_heads or 32)
+        rec["gpu_over_cpu"] = round(rec["value"] / rec["cpu_baseline"]["value"], 1)
     print(json.dumps(rec), flush=True)
 
 
