@@ -253,8 +253,11 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
 
   // Heads vary fastest across consecutive workgroups: the H heads of one token
   // row are contiguous in q, k, v and g, so neighbouring workgroups read
-  // neighbouring memory.
-  const int h = blockIdx.x, c = blockIdx.y;
+  // neighbouring memory. Blocks run last to first: the chain starts from block
+  // 0, and the records written last are the ones still held in the 256 MB
+  // memory-side cache (MALL) when it reads them (measured: 357 -> 341 us per
+  // call on the 8192-token, 32-head prefill).
+  const int h = blockIdx.x, c = gridDim.y - 1 - blockIdx.y;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int mm = lane % 16, gq = lane / 16;
