@@ -538,9 +538,10 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
 //    in flight in their registers, and publish block j + 1 into a small LDS
 //    ring before barrier B(j + 1). (Global->LDS DMA was measured to move only
 //    about 16 B per clock per CU on gfx950, too slow for this stream.)
-//  - one output wave forms each block's output tiles from the partial (Q~ S)^T
-//    products and delta the compute waves leave in LDS, and stores them, so
-//    the output product sits off the compute waves' dependent chain.
+//  - one output wave forms each block's output tiles from the bf16 state and
+//    delta the compute waves leave in LDS ((Q~ S)^T + delta^T L^T), and stores
+//    them, so the output products sit off the compute waves' dependent chain
+//    and their MFMA pipes.
 // One barrier per block. Barrier B0 ends the prologue; block j's compute step
 // runs between barriers B(j+1) and B(j+2); a final barrier follows the last.
 //
@@ -548,8 +549,9 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
 //  - block c is stored to slot c % 3 before B(c); the compute waves read it
 //    (as the next block's operands) and the output wave reads its L between
 //    B(c) and B(c + 2); the loaders overwrite it only after B(c + 2);
-//  - the partials of block c (xbuf[c % 2]) are written before B(c + 1) and
-//    read between B(c + 1) and B(c + 2); they are overwritten after B(c + 2);
+//  - the K~+ S partials and the bf16 state of block c (xbuf[c % 2],
+//    sbuf[c % 2]) are written before B(c + 1) and read between B(c + 1) and
+//    B(c + 2); they are overwritten after B(c + 2);
 //  - delta of block c (dbuf[c % 2]) is written before B(c + 2), read between
 //    B(c + 2) and B(c + 3), and overwritten after B(c + 3).
 constexpr int kUnitFull = 0;           // chain unit modes (see chain_kernel)
@@ -572,7 +574,7 @@ struct ChainCfg {
   static constexpr int kFrags = R::kFrags + kVFrags;                 // 1 KiB wave-loads per block
   static constexpr int kPerLoader = (kFrags + kLoaders - 1) / kLoaders;
   static constexpr int kSlot = kFrags * 1024;
-  static constexpr int kXBytes = 2 * kHalves * 2 * 2 * kWave * 16;   // xbuf
+  static constexpr int kXBytes = 2 * kHalves * 2 * kWave * 16 + 2 * R::NP * kWave * 16;   // xbuf, sbuf
   static constexpr int kDBytes = 2 * 2 * kWave * 16;                 // dbuf
   static_assert(kVBytes % 1024 == 0, "whole V fragments");
   static_assert(kRing == 3, "buffer lifetimes");
@@ -597,7 +599,8 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   using R = Rec<D>;
   constexpr int NCW = Cfg::kHalves;
   __shared__ __attribute__((aligned(1024))) char ring[kRing * Cfg::kSlot];
-  __shared__ f32x4 xbuf[2][NCW][2][2][kWave];   // [set][wave][K~+ S, (Q~ S)^T][token tile]
+  __shared__ f32x4 xbuf[2][NCW][2][kWave];      // [set][wave][token tile]: partial K~+ S
+  __shared__ bf16x8 sbuf[2][R::NP][kWave];      // [set][k block]: bf16 state, B-operand fragments
   __shared__ bf16x8 dbuf[2][2][kWave];          // [set][hi, lo]: delta of both token tiles
 
   // Work unit: (sequence, head, segment, mode). Without segments (P = 1) a
@@ -652,17 +655,24 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
 
   if (wave == NCW + kLoaders) {
     // ---------------- output wave ----------------
-    // O^T = (Q~ S)^T + delta^T L^T: with delta as the A operand the
-    // accumulator holds token 16u + mm, columns 4gq .. 4gq + 3 in each lane.
+    // O^T = (Q~ S)^T + delta^T L^T: with S^T and delta as the A operands
+    // the accumulator holds token 16u + mm, columns 4gq .. 4gq + 3 in each
+    // lane. (Q~ S)^T is formed here from the bf16 state the compute waves
+    // publish, off their MFMA pipes.
     f32x4 P[2];
     bf16x8 Lf[2];
     auto fetch = [&](int c) __attribute__((always_inline)) {   // between B(c + 1) and B(c + 2)
+      const char* slot = slot_of(c);
+      bf16x8 sf[R::NP];
+#pragma unroll
+      for (int p = 0; p < R::NP; ++p) sf[p] = sbuf[c % 2][p][lane];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        P[u] = xbuf[c % 2][0][1][u][lane];
+        Lf[u] = *(const bf16x8*)(slot + R::kL + u * 1024 + lane * 16);
+        P[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 1; w < NCW; ++w) P[u] += xbuf[c % 2][w][1][u][lane];
-        Lf[u] = *(const bf16x8*)(slot_of(c) + R::kL + u * 1024 + lane * 16);
+        for (int p = 0; p < R::NP; ++p)
+          P[u] = mfma32(sf[p], *(const bf16x8*)(slot + R::kQt + (u * R::NP + p) * 1024 + lane * 16), P[u]);
       }
     };
     auto emit = [&](int c) __attribute__((always_inline)) {    // between B(c + 2) and B(c + 3)
@@ -775,12 +785,14 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   // ---------------- compute waves ----------------
   // Compute wave hf holds rows [hf * D/kHalves, (hf + 1) * D/kHalves) of the
   // slice. Right after the state update it forms the next block's partial
-  // K~+ S over its rows (kept in registers and published to LDS) and partial
-  // (Q~ S)^T (for the output wave). After the next barrier each wave adds its
-  // partner's K~+ S partial to its own; with two halves that sum is the same
-  // bitwise in both waves (fp32 addition commutes), so both derive the same
-  // delta (with more waves every wave sums all partials in wave order). Each operand group of the next block is read from LDS right after
-  // the products of this block have consumed the registers it replaces.
+  // K~+ S over its rows (kept in registers and published to LDS) and
+  // publishes its rows of the state in bf16 (for the output wave). After the
+  // next barrier each wave adds its partner's K~+ S partial to its own; with
+  // two halves that sum is the same bitwise in both waves (fp32 addition
+  // commutes), so both derive the same delta (with more waves every wave sums
+  // all partials in wave order). Each operand group of the next block is read
+  // from LDS right after the products of this block have consumed the
+  // registers it replaces.
   const int hf = wave;
   const int col = 16 * s + mm;
   // start and end states of the unit (NULL start: zero, or the identity for
@@ -814,20 +826,17 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   if (nblk > 0) {
     const int ck_base = ckpt_interval > 0 ? seq_ck_off[n] : 0;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    bf16x8 kp[2][PW], qt[2][PW];       // next block's K~+ and Q~ fragments
+    bf16x8 kp[2][PW];                  // next block's K~+ fragments
     bf16x8 th[2], tl[2];               // T hi / lo per token tile
     f32x4 vv[2];                       // V[16u + 4gq .. +3][mm]
     bf16x8 khh[TW], khl[TW];           // Kh hi / lo per row tile
     f32x4 pc[TW];                      // Pc of rows 16rt + 4gq .. +3
-    auto read_kpqt = [&](const char* slot) __attribute__((always_inline)) {
+    auto read_kp = [&](const char* slot) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int qq = 0; qq < PW; ++qq) {
-          const int f = u * R::NP + hf * PW + qq;
-          kp[u][qq] = *(const bf16x8*)(slot + R::kKp + f * 1024 + lane * 16);
-          qt[u][qq] = *(const bf16x8*)(slot + R::kQt + f * 1024 + lane * 16);
-        }
+        for (int qq = 0; qq < PW; ++qq)
+          kp[u][qq] = *(const bf16x8*)(slot + R::kKp + (u * R::NP + hf * PW + qq) * 1024 + lane * 16);
     };
     auto read_tv = [&](const char* slot) __attribute__((always_inline)) {
 #pragma unroll
@@ -848,11 +857,12 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
         pc[t] = *(const f32x4*)(slot + R::kPc + (16 * rt + 4 * gq) * 4);
       }
     };
-    // partial products of a block over this wave's rows: K~+ S stays in u_own
-    // and goes to LDS for the partner, (Q~ S)^T goes to LDS for the output wave
+    // partial K~+ S of a block over this wave's rows: it stays in u_own and
+    // goes to LDS for the partner; the bf16 state goes to LDS for the output
+    // wave, which forms (Q~ S)^T from it
     f32x4 u_own[2];
     auto partials = [&](int c) __attribute__((always_inline)) {
-      f32x4 U[2] = {z, z}, P[2] = {z, z}, UL[2] = {z, z};
+      f32x4 U[2] = {z, z}, UL[2] = {z, z};
 #pragma unroll
       for (int qq = 0; qq < PW; ++qq) {
         const bf16x4 zero = {};
@@ -861,10 +871,10 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
         split_bf16(acc[2 * qq], h0, l0);
         if (two) split_bf16(acc[2 * qq + 1], h1, l1);
         const bf16x8 Bs = cat(h0, h1);
+        sbuf[c % 2][hf * PW + qq][lane] = Bs;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           U[u] = mfma32(kp[u][qq], Bs, U[u]);
-          P[u] = mfma32(Bs, qt[u][qq], P[u]);
           if constexpr (kSplitS) UL[u] = mfma32(kp[u][qq], cat(l0, l1), UL[u]);
         }
       }
@@ -872,8 +882,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       for (int u = 0; u < 2; ++u) {
         if constexpr (kSplitS) U[u] += UL[u];
         u_own[u] = U[u];
-        if (NCW > 1) xbuf[c % 2][hf][0][u][lane] = U[u];
-        xbuf[c % 2][hf][1][u][lane] = P[u];
+        if (NCW > 1) xbuf[c % 2][hf][u][lane] = U[u];
       }
     };
     auto store_state = [&](const f32x4* st, int idx) __attribute__((always_inline)) {
@@ -889,22 +898,22 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       lds_barrier();
       f32x4 U0 = u_own[0], U1 = u_own[1];
       if constexpr (NCW == 2) {
-        U0 += xbuf[j % 2][hf ^ 1][0][0][lane];
-        U1 += xbuf[j % 2][hf ^ 1][0][1][lane];
+        U0 += xbuf[j % 2][hf ^ 1][0][lane];
+        U1 += xbuf[j % 2][hf ^ 1][1][lane];
       } else if constexpr (NCW > 2) {   // every wave sums all partials in the same order
-        U0 = xbuf[j % 2][0][0][0][lane];
-        U1 = xbuf[j % 2][0][0][1][lane];
+        U0 = xbuf[j % 2][0][0][lane];
+        U1 = xbuf[j % 2][0][1][lane];
 #pragma unroll
         for (int w = 1; w < NCW; ++w) {
-          U0 += xbuf[j % 2][w][0][0][lane];
-          U1 += xbuf[j % 2][w][0][1][lane];
+          U0 += xbuf[j % 2][w][0][lane];
+          U1 += xbuf[j % 2][w][1][lane];
         }
       }
       // the partner's partials are read before the next block's operands, so
       // the wait for them does not include theirs (LDS returns in order)
       __builtin_amdgcn_sched_barrier(0);
       const char* nslot = slot_of(j + 1);
-      read_kpqt(nslot);
+      read_kp(nslot);
       bf16x4 rh0, rl0, rh1, rl1;
       split_bf16(vv[0] - U0, rh0, rl0);
       split_bf16(vv[1] - U1, rh1, rl1);
@@ -959,7 +968,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     lds_barrier();
     {
       const char* slot0 = slot_of(0);
-      read_kpqt(slot0);
+      read_kp(slot0);
       read_tv(slot0);
       read_khpc(slot0);
     }
