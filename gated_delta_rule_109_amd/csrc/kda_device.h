@@ -82,9 +82,18 @@ __device__ __forceinline__ bf16x4 lo_half(bf16x8 a) { return __builtin_shuffleve
 __device__ __forceinline__ bf16x4 hi_half(bf16x8 a) { return __builtin_shufflevector(a, a, 4, 5, 6, 7); }
 
 // Two-term bf16 split: x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi).
+// hi is widened back to fp32 from its packed pairs (element 2i in the low
+// half of dword i, element 2i + 1 in the high half): a shift and a mask per
+// pair of values, instead of a separate conversion per value.
 __device__ __forceinline__ void split_bf16(f32x4 x, bf16x4& hi, bf16x4& lo) {
   hi = to_bf16x4(x);
-  lo = to_bf16x4(x - from_bf16x4(hi));
+  const uint2 p = __builtin_bit_cast(uint2, hi);
+  f32x4 h;
+  h[0] = __builtin_bit_cast(float, p.x << 16);
+  h[1] = __builtin_bit_cast(float, p.x & 0xffff0000u);
+  h[2] = __builtin_bit_cast(float, p.y << 16);
+  h[3] = __builtin_bit_cast(float, p.y & 0xffff0000u);
+  lo = to_bf16x4(x - h);
 }
 
 // ---- MFMA -----------------------------------------------------------------------
