@@ -559,6 +559,7 @@ constexpr int kUnitLocal = 1;
 constexpr int kUnitTransition = 2;
 constexpr int kLoaders = 4;            // loader waves per workgroup
 constexpr int kInFlight = 4;           // blocks each loader keeps in flight
+constexpr int kTouchAhead = 4;         // blocks beyond the loads that the L2 touches run
 constexpr int kRing = 3;               // LDS slots
 
 template <int D, typename TIn>
@@ -579,7 +580,7 @@ struct ChainCfg {
   static_assert(kVBytes % 1024 == 0, "whole V fragments");
   static_assert(kRing == 3, "buffer lifetimes");
   static_assert(kRing * kSlot + kXBytes + kDBytes <= 160 * 1024, "LDS");
-  static_assert(kInFlight * kPerLoader < 64, "vmcnt field");
+  static_assert(kInFlight * (kPerLoader + 1) < 64, "vmcnt field");   // + one L2 touch per block
 };
 
 // kSplitS: K~+ S takes the state as a bf16 hi/lo pair (two MFMAs per tile)
@@ -704,6 +705,27 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     // ---------------- loader waves ----------------
     const int lw = wave - NCW;
     u32x4 buf[kInFlight][Cfg::kPerLoader];
+    // L2 touches: with each block it loads, every loader also reads one dword
+    // of the record kTouchAhead blocks further on. The workgroups of the S
+    // slices of a head split the record's 128-byte lines between them: lane
+    // l of loader w takes line 64w + l of its share, and lanes past the share
+    // repeat its last line (so only the first loader covers new lines, and
+    // the others add one request each: touching the share from every loader
+    // measured 0.330 ms instead of 0.323). That record reaches this XCD's L2 once,
+    // early, and the 16-byte loads of all S workgroups later hit there.
+    // Measured on the 8192-token, 32-head prefill: 0.341 -> 0.323 ms per call
+    // (while many lines are still on their way from HBM, each compute unit
+    // holds all its requests for them outstanding). The touched values are
+    // folded into a value that is never stored, after the same in-flight
+    // delay as the block loads, so they cost no wait.
+    constexpr int kLines = R::kBytes / 128;
+    constexpr int kShare = (kLines + S - 1) / S;
+    const int tline = min(s * kShare + min(lw * kWave + lane, kShare - 1), kLines - 1);
+    uint32_t touched[kInFlight];
+    uint32_t fold = 0;
+    auto touch = [&](uint32_t& dst, int j) __attribute__((always_inline)) {
+      dst = *(const uint32_t*)(rec0 + (size_t)j * R::kBytes + tline * 128);
+    };
     // Every loader issues exactly kPerLoader 16-byte loads per block
     // (fragments past the end re-read a valid address and are not stored), so
     // the loads of one block form one contiguous group in the vmcnt order. The
@@ -760,16 +782,21 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     const int last = nblk - 1;
     static_for<0, kInFlight>([&](auto A) __attribute__((always_inline)) {
       load_block(buf[A.value], min(A.value, last));
+      touch(touched[A.value], min(A.value + kTouchAhead, last));
     });
     store_block(buf[0], 0);
+    fold ^= touched[0];
     load_block(buf[0], min(kInFlight, last));
+    touch(touched[0], min(kInFlight + kTouchAhead, last));
     lds_barrier();
     auto step = [&](auto A, int j) __attribute__((always_inline)) {
       // publish block j + 1 before barrier B(j + 1), then refill its registers
       constexpr int set = (decltype(A)::value + 1) % kInFlight;
       const int c = j + 1;
       store_block(buf[set], c);
+      fold ^= touched[set];
       load_block(buf[set], min(c + kInFlight, last));
+      touch(touched[set], min(c + kInFlight + kTouchAhead, last));
       lds_barrier();
     };
     int j0 = 0;
@@ -779,6 +806,11 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       if (j0 + A.value < nblk) step(A, j0 + A.value);
     });
     lds_barrier();
+    // keeps the touches: the condition holds for no call (scale is never this
+    // value in practice, and the store would only land in the ring, after
+    // every read of it)
+    static_for<0, kInFlight>([&](auto A) __attribute__((always_inline)) { fold ^= touched[A.value]; });
+    if (fold == 0x9e3779b9u && scale == -1.2345e-30f) *(uint32_t*)ring = fold;
     return;
   }
 
