@@ -10,7 +10,9 @@ the true size over what it reads for that kernel.
 It also renders the per-kernel time table of a ``rocprofv3 --kernel-trace
 --stats`` run (``--stats DIR``), and the MFMA utilisation of a counter pass
 with SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16 and
-GRBM_GUI_ACTIVE (``--mfma DIR``).
+GRBM_GUI_ACTIVE (``--mfma DIR``), and the memory-pipe counters of two passes
+(``--pipe DIR_A DIR_B``: L1-to-L2 read requests and their latency, L1 stalls
+on pending L2 data, TA address stalls, L2 hits and misses).
 
 Usage (two counter passes of the same command, then the summary):
 
@@ -232,6 +234,68 @@ def mfma_summary(d):
     return rows
 
 
+PIPE_COUNTERS = ("TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum", "TCP_PENDING_STALL_CYCLES_sum",
+                 "TA_ADDR_STALLED_BY_TC_CYCLES_sum", "TCC_HIT_sum", "TCC_MISS_sum", "GRBM_GUI_ACTIVE")
+CU_NUM = 256                # MI355X compute units
+
+
+def pipe_summary(dirs):
+    """[(kernel, dispatches, GPU cycles, L2 read requests per CU, mean L2 read
+    latency in cycles, share of cycles the L1 stalls on pending L2 data,
+    share of cycles the TA address path stalls on the L1, L2 hit rate)] of
+    the kda kernels, one row per kernel, from counter passes that together
+    hold PIPE_COUNTERS (each pass with its own GRBM_GUI_ACTIVE). Per
+    dispatch; GRBM_GUI_ACTIVE is summed over the XCDs in the CSV (divided by
+    XCD_NUM here) and the TCP/TA counters over the compute units (divided by
+    CU_NUM for the per-CU shares)."""
+    vals = {}
+    for d in dirs:
+        per_disp = {}
+        for r in csv.DictReader(open(_counter_csv(d))):
+            if "kda::" not in r["Kernel_Name"]:
+                continue
+            key = (kernel_key(r["Kernel_Name"]), r["Dispatch_Id"])
+            per_disp.setdefault(key, {}).setdefault(r["Counter_Name"], 0.0)
+            per_disp[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        for (k, _), cs in per_disp.items():
+            cyc = cs.get("GRBM_GUI_ACTIVE", 0.0) / XCD_NUM
+            for c, v in cs.items():
+                if c == "GRBM_GUI_ACTIVE":
+                    continue
+                vals.setdefault(k, {}).setdefault(c, []).append((v, cyc))
+            vals.setdefault(k, {}).setdefault("GRBM_GUI_ACTIVE", []).append((cyc, cyc))
+    rows = []
+    for k, cs in sorted(vals.items()):
+        if not all(c in cs for c in PIPE_COUNTERS):
+            continue
+        mean = lambda c: float(np.mean([v for v, _ in cs[c]]))
+        share = lambda c: float(np.mean([v / CU_NUM / cyc for v, cyc in cs[c] if cyc > 0]))
+        req = mean("TCP_TCC_READ_REQ_sum")
+        if req < CU_NUM:            # kernels with next to no memory traffic (the plan kernel)
+            continue
+        hits, misses = mean("TCC_HIT_sum"), mean("TCC_MISS_sum")
+        rows.append((k, len(cs["TCP_TCC_READ_REQ_sum"]), mean("GRBM_GUI_ACTIVE"), req / CU_NUM,
+                     mean("TCP_TCC_READ_REQ_LATENCY_sum") / req, 100.0 * share("TCP_PENDING_STALL_CYCLES_sum"),
+                     100.0 * share("TA_ADDR_STALLED_BY_TC_CYCLES_sum"), 100.0 * hits / max(hits + misses, 1.0)))
+    return rows
+
+
+def render_pipe(rows, title, command):
+    out = [f"# {title}", "", "Commands (run from the repository root on one MI355X; one pass per counter group):",
+           "", "```"]
+    out += list(command)
+    out += ["```", "",
+            "Per dispatch, averaged over the dispatches of each kernel. GRBM_GUI_ACTIVE arrives summed over the "
+            "8 XCDs and is divided by 8; the TCP and TA counters are summed over the 256 compute units and are "
+            "divided by 256 for the per-CU columns.", "",
+            "| kernel | dispatches | GPU cycles | L2 read requests per CU | mean L2 read latency (cycles) | "
+            "L1 stalled on pending L2 data (share of cycles, per CU) | TA address path stalled by L1 (share) | "
+            "L2 hit rate |", "|---|---|---|---|---|---|---|---|"]
+    for k, n, cyc, req, lat, pend, tas, hit in rows:
+        out.append(f"| `{k}` | {n} | {cyc:.3g} | {req:.4g} | {lat:.0f} | {pend:.0f} % | {tas:.0f} % | {hit:.0f} % |")
+    return "\n".join(out) + "\n"
+
+
 def render_mfma(rows, title, command):
     out = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```"]
     out += list(command)
@@ -269,6 +333,8 @@ def main(argv=None):
     ap.add_argument("--algorithmic-bytes", type=int)
     ap.add_argument("--stats", help="rocprofv3 --kernel-trace --stats output directory (kernel-time summary)")
     ap.add_argument("--mfma", help="rocprofv3 --pmc output directory with the MFMA counters")
+    ap.add_argument("--pipe", nargs="+", help="rocprofv3 --pmc output directories with the memory-pipe counters")
+    ap.add_argument("--note", action="append", default=[], help="paragraph appended to the summary")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="prefill",
                     help="which call the byte-counter summary adds up")
     ap.add_argument("--title", default="KDA kernels")
@@ -281,12 +347,16 @@ def main(argv=None):
         text = render_stats(kernel_stats(a.stats), a.title, a.command, line)
     elif a.mfma:
         text = render_mfma(mfma_summary(a.mfma), a.title, a.command)
+    elif a.pipe:
+        text = render_pipe(pipe_summary(a.pipe), a.title, a.command)
     else:
         if not (a.fetch and a.write and a.calib_mib and a.algorithmic_bytes):
             ap.error("--fetch, --write, --calib-mib and --algorithmic-bytes are required")
         kernels, title, call = WORKLOADS[a.workload]
         text = render(summarize(a.fetch, a.write, a.calib_mib, kernels), a.calib_mib, a.command,
                       a.algorithmic_bytes, title, call)
+    for note in a.note:
+        text += "\n" + note.strip() + "\n"
     if a.out:
         with open(a.out, "w") as fh:
             fh.write(text)

@@ -101,3 +101,40 @@ def test_digest_ignores_comments_but_not_code():
     code = "int f(int a) {  // add one\n  return a + 1; /* done */\n}\n"
     assert P._code_only(code) == P._code_only("int f(int a) {\n return a + 1;\n}")
     assert P._code_only(code) != P._code_only(code.replace("a + 1", "a + 2"))
+
+
+def test_memory_pipe_summary_per_cu_and_per_request(tmp_path):
+    """Two passes of one chain dispatch: latency = latency sum / requests,
+    shares = per-CU stall cycles / the active cycles of one XCD, hit rate from
+    the L2 hit and miss counts; a kernel with next to no requests is left out."""
+    def write(d, rows):
+        os.makedirs(d, exist_ok=True)
+        with open(os.path.join(d, "kda_counter_collection.csv"), "w", newline="") as fh:
+            w = csv.DictWriter(fh, FIELDS)
+            w.writeheader()
+            for disp, k, c, v in rows:
+                w.writerow({"Dispatch_Id": disp, "Kernel_Name": k, "Grid_Size": grid_of(k),
+                            "Counter_Name": c, "Counter_Value": v})
+    cyc = 1000.0                                   # per XCD; the CSV holds the sum over 8
+    a, b = str(tmp_path / "a"), str(tmp_path / "b")
+    write(a, [(1, CHAIN, "GRBM_GUI_ACTIVE", 8 * cyc),
+              (1, CHAIN, "TCP_TCC_READ_REQ_sum", 256 * 400),
+              (1, CHAIN, "TCP_TCC_READ_REQ_LATENCY_sum", 256 * 400 * 300),
+              (1, CHAIN, "TCP_PENDING_STALL_CYCLES_sum", 256 * 0.5 * cyc),
+              (2, PLAN, "GRBM_GUI_ACTIVE", 8 * cyc),
+              (2, PLAN, "TCP_TCC_READ_REQ_sum", 3),
+              (2, PLAN, "TCP_TCC_READ_REQ_LATENCY_sum", 900),
+              (2, PLAN, "TCP_PENDING_STALL_CYCLES_sum", 0)])
+    write(b, [(1, CHAIN, "GRBM_GUI_ACTIVE", 8 * cyc),
+              (1, CHAIN, "TA_ADDR_STALLED_BY_TC_CYCLES_sum", 256 * 0.25 * cyc),
+              (1, CHAIN, "TCC_HIT_sum", 870), (1, CHAIN, "TCC_MISS_sum", 130),
+              (2, PLAN, "GRBM_GUI_ACTIVE", 8 * cyc),
+              (2, PLAN, "TA_ADDR_STALLED_BY_TC_CYCLES_sum", 0),
+              (2, PLAN, "TCC_HIT_sum", 1), (2, PLAN, "TCC_MISS_sum", 1)])
+    rows = P.pipe_summary([a, b])
+    assert len(rows) == 1
+    k, n, cycles, req, lat, pend, tas, hit = rows[0]
+    assert k == P.kernel_key(CHAIN) and n == 1
+    assert cycles == pytest.approx(cyc) and req == pytest.approx(400)
+    assert lat == pytest.approx(300) and pend == pytest.approx(50) and tas == pytest.approx(25)
+    assert hit == pytest.approx(87)
