@@ -22,7 +22,8 @@ namespace kda {
 // columns [32w, 32w + 32); lane l owns the 4 columns 32w + 4(l % 8) .. +3 and
 // the 16 rows (l / 8) + 8i, i = 0..15. One float4 load instruction of the wave
 // covers 8 rows x 128 contiguous bytes. The reduction over rows is three
-// cross-lane xor steps (lane bits 3..5): a wave holds whole columns, so the
+// butterfly steps over lane bits 3..5 (a DPP row rotate for bit 3, a
+// ds_swizzle for bit 4, ds_bpermute for bit 5): a wave holds whole columns, so the
 // token loop needs no LDS traffic and no barrier after the token vectors are
 // staged.
 //
@@ -60,6 +61,7 @@ __global__ __launch_bounds__(D == 128 ? 256 : 64) void decode_kernel(
   constexpr int kRowGroups = kWave / kColGroups;        // lanes sharing a column group
   constexpr int kRowsPerLane = D / kRowGroups;
   constexpr int kColsPerWave = 4 * kColGroups;
+  constexpr int kRowSteps = D == 128 ? 3 : 4;           // butterfly steps over a column group's lanes
   static_assert(kThreads / kWave * kColsPerWave == D, "layout covers D columns");
 
   const uint32_t head = blockIdx.x;                     // n * H + h
@@ -143,19 +145,21 @@ __global__ __launch_bounds__(D == 128 ? 256 : 64) void decode_kernel(
         qq += qr * qr;
       }
     }
-#pragma unroll
-    for (int m = kColGroups; m < kWave; m <<= 1) {
+    // butterfly over the lanes of a column group (lane bits log2(kColGroups)
+    // .. 5): every lane ends with the same sums
+    static_for<0, kRowSteps>([&](auto I) __attribute__((always_inline)) {
+      constexpr int m = kColGroups << decltype(I)::value;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        u[c] += __shfl_xor(u[c], m);
-        w[c] += __shfl_xor(w[c], m);
+        u[c] += lane_xor<m>(u[c]);
+        w[c] += lane_xor<m>(w[c]);
       }
-      kq += __shfl_xor(kq, m);
+      kq += lane_xor<m>(kq);
       if constexpr (kGeneral) {
-        kk += __shfl_xor(kk, m);
-        qq += __shfl_xor(qq, m);
+        kk += lane_xor<m>(kk);
+        qq += lane_xor<m>(qq);
       }
-    }
+    });
     // inverse norms of this token's k and q rows (1 without the front end)
     const float rk = norm ? inv_norm(kk, fe_eps) : 1.f, rq = norm ? inv_norm(qq, fe_eps) : 1.f;
     if constexpr (kGeneral) {

@@ -96,6 +96,23 @@ __device__ __forceinline__ void split_bf16(f32x4 x, bf16x4& hi, bf16x4& lo) {
   lo = to_bf16x4(x - h);
 }
 
+// ---- cross-lane -----------------------------------------------------------------
+// The value of lane l ^ M (M a power of two below 64), for butterfly sums.
+// M = 8: a DPP rotate by 8 inside 16-lane rows (a VALU operand modifier, no
+// LDS crossbar); other M < 32: ds_swizzle in bitmask mode (xor M, no address
+// operand); M = 32: ds_bpermute. All three give exactly lane l ^ M.
+template <int M>
+__device__ __forceinline__ float lane_xor(float x) {
+  static_assert(M > 0 && M < 64 && (M & (M - 1)) == 0, "power of two below the wave width");
+  if constexpr (M == 8) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+  } else if constexpr (M < 32) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), (M << 10) | 0x1F));
+  } else {
+    return __shfl_xor(x, M);
+  }
+}
+
 // ---- MFMA -----------------------------------------------------------------------
 // D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16). Lane l holds
 //   A[l%16][8*(l/16) + j], B[8*(l/16) + j][l%16] (j = 0..7),
