@@ -302,11 +302,15 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
 #pragma unroll
       for (int c = 0; c < kChPerLane; c += 4) {
         f32x4 xk, xq;
+        // the raw k rows also go to sK, so phase 1 does not read them again
         if constexpr (sizeof(TIn) == 2) {
-          xk = from_bf16x4(*(const bf16x4*)(k + off + c));
+          const bf16x4 rawk = *(const bf16x4*)(k + off + c);
+          *(bf16x4*)&sK[t][part * kChPerLane + c] = rawk;
+          xk = from_bf16x4(rawk);
           xq = from_bf16x4(*(const bf16x4*)(q + off + c));
         } else {
           xk = *(const f32x4*)(k + off + c);
+          *(f32x4*)&sK[t][part * kChPerLane + c] = xk;
           xq = *(const f32x4*)(q + off + c);
         }
 #pragma unroll
@@ -336,14 +340,26 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
   if (tid < D) {
     const int ch = tid;
     float a[kBT], kf[kBT];
+    // with the front end's norms, phase 0 has already staged the k rows
+    const bool k_staged = kGeneral && (fe_flags & KDA_FE_L2NORM_QK);
+    if (k_staged) {
 #pragma unroll
-    for (int t = 0; t < kBT; ++t) {
-      const int tc = min(t, cnt - 1);
-      a[t] = g_at(tc, ch);
-      const TIn kraw = k[row(tc) + ch];
-      sK[t][ch] = kraw;
-      if constexpr (sizeof(TIn) == 2) kf[t] = bf16_to_f32(kraw);
-      else kf[t] = kraw;
+      for (int t = 0; t < kBT; ++t) {
+        a[t] = g_at(min(t, cnt - 1), ch);
+        const TIn kraw = sK[t][ch];
+        if constexpr (sizeof(TIn) == 2) kf[t] = bf16_to_f32(kraw);
+        else kf[t] = kraw;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < kBT; ++t) {
+        const int tc = min(t, cnt - 1);
+        a[t] = g_at(tc, ch);
+        const TIn kraw = k[row(tc) + ch];
+        sK[t][ch] = kraw;
+        if constexpr (sizeof(TIn) == 2) kf[t] = bf16_to_f32(kraw);
+        else kf[t] = kraw;
+      }
     }
 #pragma unroll
     for (int t = 0; t < kBT; ++t) {
