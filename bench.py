@@ -1,10 +1,13 @@
 """Benchmark of the KDA hot path on one MI355X.
 
-A step is one kda_prefill_chunked call over the single-sequence prefill
-workload (B=1, H=32, T=8192, D=128, bf16 q/k/v, fp32 g/beta, zero initial
-state, fp32 final state), with inputs resident in HBM. The decode workload
-(256 sequences x 32 heads, D=128, fp32 states updated in place) is timed the
-same way and reported beside it.
+A step is one kda_prefill_chunked call over the long prefill with sparse
+state caching: B=1, H=32, T=131072, D=128, bf16 q/k/v, fp32 g/beta, zero
+initial state, a fp32 state checkpoint every 32768 tokens (4 checkpoints) and
+the fp32 final state, with inputs resident in HBM. This is the largest
+single-GPU workload and the one the prefill MFMA target is stated on. The
+8192-token single-sequence prefill, the packed varlen append-prefill, the
+variants and the decode workload (256 sequences x 32 heads, fp32 states
+updated in place) are timed the same way and reported beside it.
 
 Timing: before every call (warm-up and timed), a 1 GiB buffer is read. This
 evicts L2 and the 256 MB MALL, so each call finds its inputs in HBM and not in
@@ -18,7 +21,8 @@ Kimi K3 아키텍처", Methods 1) FlashKDA):
   prefill FLOPs per chunk-head   12C^3 + 8C^2 D + 6C D^2   (C = 16)
   decode  FLOPs per head-token   7 D^2,  bytes per head-token 8 D^2
 Prefill algorithmic bytes per token-head: q, k, v bf16 (3 x 2D) + g fp32 (4D)
-+ beta (4) + o bf16 (2D) = 1540 B at D = 128, plus the fp32 states once.
++ beta (4) + o bf16 (2D) = 1540 B at D = 128, plus the fp32 states once
+(initial states read, final state and checkpoints written).
 """
 import argparse
 import ctypes
@@ -36,9 +40,10 @@ sys.path.insert(0, ROOT)
 from gated_delta_rule_109_amd import kda, profiling  # noqa: E402
 from gated_delta_rule_109_amd.workloads import make_inputs, make_inputs_device, varlen_lengths  # noqa: E402
 
-# rocprofv3 byte-counter summary of the prefill (HBM bytes per call); used for
-# roofline.traffic only while it matches the current kernel sources.
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "kda_prefill_b1_h32_t8192_hbm_traffic.md")
+# rocprofv3 byte-counter summary of the benchmarked prefill (HBM bytes per
+# call); used for roofline.traffic only while it matches the current kernel
+# sources.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "kda_prefill_b1_h32_t131072_hbm_traffic.md")
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
@@ -49,9 +54,11 @@ def prefill_flops(T, H, D):
     return -(-T // C) * H * (12 * C ** 3 + 8 * C ** 2 * D + 6 * C * D ** 2)
 
 
-def prefill_bytes(T, H, D, n_seqs=1, init=False):
+def prefill_bytes(T, H, D, n_seqs=1, init=False, n_ckpt=0):
+    """Algorithmic bytes of one call: q, k, v, g, beta, o per token-head, the
+    final states, the initial states when given, and the checkpoints."""
     per_tok_head = 3 * 2 * D + 4 * D + 4 + 2 * D
-    return T * H * per_tok_head + n_seqs * H * D * D * 4 * (2 if init else 1)
+    return T * H * per_tok_head + (n_seqs * (2 if init else 1) + n_ckpt) * H * D * D * 4
 
 
 class Flush:
@@ -129,56 +136,78 @@ def host_cores():
     return max(1, min(n, 16))
 
 
-def cpu_baseline(T, H, D, heads):
-    """The fp64 oracle on the host cores over a bounded sample of the prefill
-    workload (the first `heads` heads of the same seeded input)."""
-    from oracle import reference
-    inp = make_inputs(T, heads, D, seed=2)
-    threads = min(heads, host_cores())
-    # repeat the sample until about 5 s of CPU time have passed, for a steady rate
-    passes, t0 = 0, time.perf_counter()
-    while True:
-        reference.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, threads=threads)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= 5.0 or passes >= 50:
-            break
-    model = ""
+def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
+                return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"value": passes * T * heads / H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "cpu_model": model,
-            "sample": f"prefill T={T}, {heads} of {H} heads, D={D} (fp64 token recurrence, OpenMP over "
-                      f"heads), {passes} passes; tokens/s scaled by {heads}/{H}", "seconds": round(dt, 3)}
+    return ""
 
 
-def bench_prefill(args, dev, flush):
-    """The benchmarked call: B=1, H=32, T=8192, D=128. Returns the headline
-    fields and the inputs (reused by the side figures)."""
-    T, H, D = 8192, 32, 128
-    q, k, v, g, beta, cu, _ = make_inputs_device(T, H, D, seed=2, device=dev)
-    plan = kda.make_plan(cu, H, D, dev)
+def cpu_baseline(inputs, T_sample, min_seconds=10.0):
+    """The fp64 oracle on the host cores over a bounded sample of the
+    benchmarked workload: its first T_sample tokens on all heads (the same
+    seeded device input, copied to the host), repeated until min_seconds have
+    passed. Reported in tokens/s of the whole workload's shape (all heads)."""
+    from oracle import reference
+    q, k, v, g, beta = inputs[:5]
+    H = q.shape[1]
+    host = [t[:T_sample].float().cpu().numpy() for t in (q, k, v, g, beta)]
+    threads = host_cores()
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        reference.prefill(*host, threads=threads, want_o=True)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or passes >= 50:
+            break
+    return {"value": round(passes * T_sample / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"the first {T_sample} of the {q.shape[0]} tokens of the benchmarked input, all {H} heads, "
+                      f"D={q.shape[2]} (fp64 token recurrence, OpenMP over heads, outputs and final state), "
+                      f"{passes} passes", "seconds": round(dt, 3)}
+
+
+def prefill_record(name, T, H, D, ms, n_seqs=1, init=False, n_ckpt=0, traffic=None):
+    """Throughput, roofline and model-MFMA figures of a prefill call."""
+    ev_ms = float(np.mean(ms))
+    flops = prefill_flops(T, H, D) if n_seqs == 1 else None
+    nbytes = prefill_bytes(T, H, D, n_seqs, init, n_ckpt)
+    gbps = nbytes / (ev_ms * 1e-3) / 1e9
+    rec = {"workload": name, "launch_ms": round(ev_ms, 4), "tokens_per_s": round(T / (ev_ms * 1e-3), 1),
+           "hbm_GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+           "algorithmic_bytes": nbytes}
+    if flops is not None:
+        rec["model_tflops"] = round(flops / (ev_ms * 1e-3) / 1e12, 2)
+        rec["model_mfma_frac"] = round(flops / (ev_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+    return rec
+
+
+def bench_prefill_long(args, dev, flush):
+    """The benchmarked call: B=1, H=32, T=131072, D=128, a checkpoint every
+    32768 tokens. Returns the headline fields and the inputs."""
+    T, H, D, CK = 131072, 32, 128, 32768
+    q, k, v, g, beta, cu, _ = make_inputs_device(T, H, D, seed=7, device=dev)
+    plan = kda.make_plan(cu, H, D, dev, ckpt_interval=CK)
     o = torch.empty_like(v)
     fin = torch.empty(1, H, D, D, dtype=torch.float32, device=dev)
+    ck = torch.empty(T // CK, H, D, D, dtype=torch.float32, device=dev)
 
     def step():
-        kda.prefill(q, k, v, g, beta, plan=plan, o=o, final_state=fin)
+        kda.prefill(q, k, v, g, beta, plan=plan, o=o, final_state=fin, checkpoints=ck)
 
     torch.cuda.synchronize()
     wall, ms = time_events(step, args.steps, args.warmup, flush)
     ev_ms = float(np.mean(ms))
     flops = prefill_flops(T, H, D)
-    nbytes = prefill_bytes(T, H, D)
-    _, bb = time_events(step, args.steps, 5)                 # back to back, no flush
+    nbytes = prefill_bytes(T, H, D, n_ckpt=T // CK)
+    _, bb = time_events(step, max(args.steps // 2, 3), 3)     # back to back, no flush
     ach_gbps = nbytes / (ev_ms * 1e-3) / 1e9
     tr = profiling.read_record(TRAFFIC_PROFILE)
     rec = {
-        "metric": "KDA prefill tokens/s (B=1, H=32, T=8192, D=128)",
+        "metric": "KDA prefill tokens/s (B=1, H=32, T=131072, D=128, checkpoint every 32768)",
         "value": round(T / (ev_ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -191,9 +220,10 @@ def bench_prefill(args, dev, flush):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded, device-generated; q,k L2-normalised, g floored at ln 0.5)",
-        "config": {"workload": "single-sequence KDA prefill", "batch": 1, "heads": H, "seq_len": T,
-                   "head_dim": D, "chunk": C, "chain_step_tokens": 2 * C, "initial_state": False},
-        "roofline": {"kernel": "kda_prefill_chunked (plan + prep + chain kernels, one C-ABI call)",
+        "config": {"workload": "long KDA prefill with sparse state caching", "batch": 1, "heads": H,
+                   "seq_len": T, "head_dim": D, "chunk": C, "checkpoint_interval": CK, "checkpoints": T // CK,
+                   "initial_state": False},
+        "roofline": {"kernel": "kda_prefill_chunked (every kernel of one C-ABI call)",
                      "bound": "hbm", "achieved": round(ach_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(ach_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": tr["bytes_per_call"] if tr else None,
@@ -205,42 +235,38 @@ def bench_prefill(args, dev, flush):
         "prefill_tflops": round(flops / (ev_ms * 1e-3) / 1e12, 2),
         "prefill_mfma_frac_of_peak": round(flops / (ev_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
     }
-    return rec, (q, k, v, g, beta, plan, o, fin)
+    return rec, (q, k, v, g, beta)
 
 
-def bench_prefill_side(args, dev, flush, inputs):
-    """Side figures on prefill: the front end, the gate variants, 4 heads with
-    and without segments, and the packed varlen append-prefill."""
+def bench_prefill_8k(args, dev, flush):
+    """B=1, H=32, T=8192, D=128: the single-sequence prefill, plus the front
+    end and the gate variants on the same shape."""
     T, H, D = 8192, 32, 128
-    q, k, v, g, beta, plan, o, fin = inputs
-    rec = {}
-    # the same prefill from raw projections, with the fused front end
+    q, k, v, g, beta, cu, _ = make_inputs_device(T, H, D, seed=2, device=dev)
+    plan = kda.make_plan(cu, H, D, dev)
+    o = torch.empty_like(v)
+    fin = torch.empty(1, H, D, D, dtype=torch.float32, device=dev)
+    _, ms = time_events(lambda: kda.prefill(q, k, v, g, beta, plan=plan, o=o, final_state=fin),
+                        args.steps, args.warmup, flush)
+    rec = {"prefill_8k": prefill_record("B=1, H=32, T=8192, D=128, zero initial state", T, H, D, ms)}
+    if args.only == "prefill_8k":
+        return rec
     rq, rk, rv, rg, rbeta, _, _ = make_inputs_device(T, H, D, seed=2, device=dev, raw=True)
     fe = kda.Options(kda.FE_ALL, 1e-6)
     _, fms = time_events(lambda: kda.prefill(rq, rk, rv, rg, rbeta, plan=plan, o=o, final_state=fin, options=fe),
                          args.steps, args.warmup, flush)
-    f_ms = float(np.mean(fms))
     del rq, rk, rv, rg, rbeta
-    rec["prefill_front_end"] = {"workload": "the same prefill from raw q, k and gate/beta logits "
-                                            "(L2 norm, -softplus gate, sigmoid beta fused into the prep kernel)",
-                                "launch_ms": round(f_ms, 4), "tokens_per_s": round(T / (f_ms * 1e-3), 1)}
-
-    # the same prefill for Gated DeltaNet (one decay per token and head) and DeltaNet (no decay)
+    rec["prefill_front_end"] = prefill_record(
+        "the same prefill from raw q, k and gate/beta logits (L2 norm, -softplus gate, sigmoid beta fused)",
+        T, H, D, fms)
     g_head = g[..., 0].contiguous()
-    vms = {}
     for name, gate, gv in (("gdn", kda.GATE_HEAD, g_head), ("deltanet", kda.GATE_NONE, None)):
         opt = kda.Options(gate=gate)
         _, ts = time_events(lambda: kda.prefill(q, k, v, gv, beta, plan=plan, o=o, final_state=fin,
                                                 options=opt), args.steps, args.warmup, flush)
-        vms[name] = float(np.mean(ts))
-    del g_head
-    rec["prefill_variants"] = {"workload": "the same prefill for Gated DeltaNet (g [T, H]) and DeltaNet (no g)",
-                               "gdn_launch_ms": round(vms["gdn"], 4),
-                               "deltanet_launch_ms": round(vms["deltanet"], 4)}
-
-    # the per-GPU share of 32 heads over 8 GPUs: 4 heads, the same sequence length.
-    # The chain then fills 32 of 256 compute units; the library splits the
-    # sequence into segments that run side by side (against one segment).
+        rec[f"prefill_{name}"] = {"workload": f"the same prefill, {name} gate", "launch_ms": round(float(np.mean(ts)), 4)}
+    del g_head, q, k, v, g, beta, o, fin
+    # one GPU's share of 32 heads over 8 GPUs: 4 heads, the same sequence length
     H4 = 4
     q4, k4, v4, g4, b4, cu4, _ = make_inputs_device(T, H4, D, seed=5, device=dev)
     plan4 = kda.make_plan(cu4, H4, D, dev)
@@ -251,14 +277,18 @@ def bench_prefill_side(args, dev, flush, inputs):
         _, ts = time_events(lambda: kda.prefill(q4, k4, v4, g4, b4, plan=plan4, o=o4, final_state=fin4,
                                                 options=opt), args.steps, args.warmup, flush)
         seg_ms[name] = float(np.mean(ts))
-    del q4, k4, v4, g4, b4
     rec["prefill_4_heads"] = {"workload": "B=1, H=4, T=8192, D=128 (32 heads over 8 GPUs, one GPU's share)",
                               "one_segment_ms": round(seg_ms["one_segment"], 4),
                               "library_choice_ms": round(seg_ms["library_choice"], 4),
                               "segments_speedup": round(seg_ms["one_segment"] / seg_ms["library_choice"], 3)}
+    return rec
 
-    # append-prefill over packed varlen input: 16 sequences (lognormal lengths,
-    # median 4096, clipped to [1, 32768]) with cached fp32 initial states
+
+def bench_varlen(args, dev, flush):
+    """Append-prefill over packed varlen input: 16 sequences (lognormal
+    lengths, median 4096, clipped to [1, 32768]) with cached fp32 initial
+    states."""
+    H, D = 32, 128
     vl = varlen_lengths()
     vq, vk, vv, vg, vb, vcu, vs0 = make_inputs_device(sum(vl), H, D, seed=6, device=dev, lengths=vl,
                                                       initial_state=True)
@@ -266,29 +296,11 @@ def bench_prefill_side(args, dev, flush, inputs):
     vo = torch.empty_like(vv)
     vfin = torch.empty(len(vl), H, D, D, dtype=torch.float32, device=dev)
     _, vts = time_events(lambda: kda.prefill(vq, vk, vv, vg, vb, plan=vplan, initial_state=vs0, o=vo,
-                                             final_state=vfin), max(args.steps // 4, 3),
-                         max(args.warmup // 10, 2), flush)
-    var_ms = float(np.mean(vts))
-    del vq, vk, vv, vg, vb, vs0, vo, vfin, vplan
-    # long prefill with sparse state caching: B=1, H=32, T=131072, a checkpoint
-    # every 32768 tokens
-    TL, CK = 131072, 32768
-    lq, lk, lv, lg, lb, lcu, _ = make_inputs_device(TL, H, D, seed=7, device=dev)
-    lplan = kda.make_plan(lcu, H, D, dev, ckpt_interval=CK)
-    lo = torch.empty_like(lv)
-    lfin = torch.empty(1, H, D, D, dtype=torch.float32, device=dev)
-    lck = torch.empty(TL // CK, H, D, D, dtype=torch.float32, device=dev)
-    _, lts = time_events(lambda: kda.prefill(lq, lk, lv, lg, lb, plan=lplan, o=lo, final_state=lfin,
-                                             checkpoints=lck), 3, 2, flush)
-    long_ms = float(np.mean(lts))
-    del lq, lk, lv, lg, lb, lo, lfin, lck, lplan
-    rec["prefill_long"] = {"workload": "B=1, H=32, T=131072, D=128, a checkpoint every 32768 tokens",
-                           "launch_ms": round(long_ms, 4), "tokens_per_s": round(TL / (long_ms * 1e-3), 1),
-                           "hbm_frac": round(prefill_bytes(TL, H, D) / (long_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
-    rec["prefill_varlen"] = {"workload": f"16 packed sequences, {sum(vl)} tokens (longest {max(vl)}), H=32, "
-                                         "D=128, cached initial states",
-                             "launch_ms": round(var_ms, 4), "tokens_per_s": round(sum(vl) / (var_ms * 1e-3), 1)}
-    return rec
+                                             final_state=vfin), max(args.steps // 2, 3),
+                         max(args.warmup // 5, 2), flush)
+    return {"prefill_varlen": prefill_record(
+        f"16 packed sequences, {sum(vl)} tokens (longest {max(vl)}), H=32, D=128, cached initial states",
+        sum(vl), H, D, vts, n_seqs=len(vl), init=True)}
 
 
 def bench_decode(args, dev, flush):
@@ -338,16 +350,18 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=50,
-                    help="untimed steps first (the clocks take a few dozen calls to settle)")
+    ap.add_argument("--warmup", type=int, default=10,
+                    help="untimed steps first (the clocks take some calls to settle)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0 = auto)")
+    ap.add_argument("--cpu-tokens", type=int, default=32768,
+                    help="tokens of the benchmarked input in the CPU sample")
     ap.add_argument("--calibrate", type=int, default=0, metavar="MIB",
                     help="before timing, run torch.abs over a float32 tensor of MIB MiB (a kernel of known "
                          "size for calibrating rocprofv3 byte counters)")
-    ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
-                    help="run only the benchmarked prefill call (and the measured peaks), or only decode "
-                         "(for counter passes that must see one workload)")
+    ap.add_argument("--only", choices=("all", "prefill", "prefill_8k", "varlen", "decode"), default="all",
+                    help="run only the benchmarked long prefill (and the measured peaks), only the "
+                         "8192-token prefill, only the varlen append-prefill, or only decode (for "
+                         "counter passes that must see one workload)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -365,19 +379,28 @@ def main():
         del a, b
     flush = Flush(dev)
     rec = {}
+    inputs = None
     if args.only in ("all", "prefill"):
-        head, inputs = bench_prefill(args, dev, flush)
+        head, inputs = bench_prefill_long(args, dev, flush)
         rec.update(head)
-        if args.only == "all":
-            rec.update(bench_prefill_side(args, dev, flush, inputs))
-        del inputs
+        print(f"bench: long prefill {rec['ms_per_step']} ms", file=sys.stderr, flush=True)
+    if args.only == "all" and not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(inputs, args.cpu_tokens)
+        rec["gpu_over_cpu"] = round(rec["value"] / rec["cpu_baseline"]["value"], 1)
+        print("bench: cpu baseline done", file=sys.stderr, flush=True)
+    inputs = None
+    torch.cuda.empty_cache()
+    if args.only in ("all", "prefill_8k"):
+        rec.update(bench_prefill_8k(args, dev, flush))
+        print("bench: 8k prefill done", file=sys.stderr, flush=True)
+    if args.only in ("all", "varlen"):
+        rec.update(bench_varlen(args, dev, flush))
+        print("bench: varlen done", file=sys.stderr, flush=True)
     if args.only in ("all", "decode"):
         rec.update(bench_decode(args, dev, flush))
+        print("bench: decode done", file=sys.stderr, flush=True)
     if args.only in ("all", "prefill"):
         rec["measured_peaks"] = measured_peaks(dev, flush)
-    if args.only == "all" and not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(8192, 32, 128, args.cpu_heads or 32)
-        rec["gpu_over_cpu"] = round(rec["value"] / rec["cpu_baseline"]["value"], 1)
     print(json.dumps(rec), flush=True)
 
 
