@@ -49,6 +49,10 @@ bool options_ok(const kda_options* opt) {
 }
 int32_t gate_of(const kda_options* opt) { return opt ? opt->gate : KDA_GATE_CHANNEL; }
 
+// Decode multiplies the state by alpha = exp(clamp(g, g_min, 0)) directly, so
+// any finite floor at or below 0 is usable.
+bool decode_floor_ok(float g_min) { return g_min >= -FLT_MAX && g_min <= 0.f; }
+
 bool aligned16(std::initializer_list<const void*> ps) {
   for (const void* p : ps)
     if ((uintptr_t)p & 15) return false;
@@ -81,12 +85,13 @@ int64_t kda_prefill_num_checkpoints(const int32_t* cu_seqlens_host, int32_t num_
   return total;
 }
 
-size_t kda_prefill_workspace_size(const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
-                                  int32_t Dk, int32_t Dv) {
-  int64_t tokens, blocks;
-  if (H <= 0 || !supported_dims(Dk, Dv) || !scan_lengths(cu_seqlens_host, num_seqs, &tokens, &blocks))
-    return 0;
-  return kda::prefill_layout(num_seqs, blocks, H, Dk).total;
+size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t Dk,
+                                  int32_t Dv) {
+  if (num_seqs < 0 || total_tokens < 0 || H <= 0 || !supported_dims(Dk, Dv)) return 0;
+  // sum_n ceil(L_n / 32) <= sum_n (L_n / 32 + 1) for any lengths with this total
+  const int64_t max_blocks = total_tokens / kda::kBlockTokens + num_seqs;
+  if (max_blocks > INT32_MAX) return 0;
+  return kda::prefill_layout(num_seqs, max_blocks, H, Dk).total;
 }
 
 kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_dtype dtype,
@@ -149,7 +154,7 @@ kda_status kda_prefill_chunked_ex(const void* q, const void* k, const void* v, k
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.cu_seqlens = cu_seqlens;
   a.num_seqs = num_seqs; a.H = H; a.D = Dk;
-  a.total_tokens = tokens; a.total_blocks = blocks;
+  a.total_tokens = tokens; a.total_blocks = blocks; a.num_checkpoints = nck > 0 ? nck : 0;
   a.scale = scale; a.g_min = g_min;
   a.fe_flags = opt ? opt->flags : 0u; a.fe_eps = opt ? opt->norm_eps : 0.f;
   a.gate = gate_of(opt);
@@ -170,6 +175,7 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
   if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
   if (!supported_dims(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
   if (N < 0 || H <= 0 || (int64_t)N * H > INT32_MAX) return KDA_ERR_INVALID_ARG;
+  if (!decode_floor_ok(g_min)) return KDA_ERR_INVALID_ARG;
   if (N == 0) return KDA_OK;
   if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
   if (!aligned16({q, k, v, g, beta, state, o})) return KDA_ERR_INVALID_ARG;
@@ -193,6 +199,7 @@ kda_status kda_decode_tokens(const void* q, const void* k, const void* v, kda_dt
   const bool need_g = gate_of(opt) != KDA_GATE_NONE;
   if (!supported_dims(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
   if (T < 1 || T > KDA_DECODE_MAX_TOKENS) return KDA_ERR_INVALID_ARG;
+  if (!decode_floor_ok(g_min)) return KDA_ERR_INVALID_ARG;
   if (N < 0 || H <= 0 || (int64_t)N * H > INT32_MAX || (int64_t)N * T * H > INT32_MAX)
     return KDA_ERR_INVALID_ARG;
   if (N == 0) return KDA_OK;

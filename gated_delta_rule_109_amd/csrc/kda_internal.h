@@ -38,6 +38,7 @@ struct PrefillArgs {
   int32_t num_seqs, H, D;
   int64_t total_tokens;
   int64_t total_blocks;       // sum_n ceil(L_n / kBlockTokens), from the host copy
+  int64_t num_checkpoints;    // from the host copy: checkpoints past it are not written
   float scale, g_min;
   uint32_t fe_flags = 0;      // KDA_FE_* (0: inputs used as given)
   float fe_eps = 0.f;

@@ -45,16 +45,24 @@
 //                   of each segment from the segments' transitions and local
 //                   states; the chain then runs once more from those states.
 //
-// Precision: MFMA operands are bf16 with fp32 accumulation. The decayed key of
-// the state update (Kh), T, V - Kp S and delta enter as two-term bf16 splits
-// (hi + lo), which keeps the fp32 state within ~1e-4 of the fp64 recurrence;
-// Kp S, Qt S and L delta use single bf16 operands.
+// Precision: MFMA operands are bf16 with fp32 accumulation. Every product that
+// feeds the state takes its operands as two-term bf16 splits (x = hi + lo,
+// three MFMAs: hi hi + hi lo + lo hi): A = Kp Km^T in prep, and in the chain
+// Kp S (both the key and the state split), T (V - Kp S) and Kh^T delta. A
+// single bf16 term in any of these leaves errors of up to 1.5e-3 relative in
+// the final state when channels decay slowly (alpha near 1), which is the
+// regime the per-channel gate exists for; with all of them split the final
+// state stays near 1e-5 at every decay rate. Q~ S and L delta only reach the
+// outputs: L is formed with three terms (its diagonal exactly, as q_t . k_t in
+// fp32) and stored as one bf16 term, and Q~ S takes one term of each operand.
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_plan.h"
 
 namespace kda {
 
 constexpr int kBT = kBlockTokens;   // tokens per block (two chunks)
+static_assert(plan::kBT == kBlockTokens, "one block size");
 
 // ---- record layout ----------------------------------------------------------
 // One record per (block, head), stored head-major (record h * total_blocks + b);
@@ -69,7 +77,8 @@ constexpr int kBT = kBlockTokens;   // tokens per block (two chunks)
 //    the order in which two 16-token accumulator tiles (tokens 0-15, 16-31)
 //    concatenate.
 // Lane l below has mm = l % 16, g = l / 16; "x 8" lists j = 0..7.
-//   Kp  [u][p]  (u = token tile, p < NP):  Kp[16u + mm][ch(p, 8g + j)]  bf16 x 8
+//   Kp  [u][p]  (u = token tile, p < NP):  Kp[16u + mm][ch(p, 8g + j)]  bf16 x 8 (hi)
+//   Kpl [u][p]:                            Kp - hi, rounded to bf16 (lo)
 //   Qt  [u][p]:                            Qt[16u + mm][ch(p, 8g + j)]  bf16 x 8
 //   Kh  [rt][hi, lo]  (rt = row tile):     Kh[tok(8g + j)][16rt + mm]   bf16 x 8
 //   T   [u]  (2 KiB, 32 bytes per lane):   T[16u + mm][tok(8g + j)]     hi x 8, lo x 8
@@ -83,7 +92,8 @@ struct Rec {
   static constexpr int NT = D / 16;          // 16-row tiles of S
   static constexpr int NP = (NT + 1) / 2;    // 32-deep k blocks over channels
   static constexpr int kKp = 0;
-  static constexpr int kQt = kKp + 2 * NP * 1024;
+  static constexpr int kKpl = kKp + 2 * NP * 1024;
+  static constexpr int kQt = kKpl + 2 * NP * 1024;
   static constexpr int kKh = kQt + 2 * NP * 1024;
   static constexpr int kT = kKh + 2 * NT * 1024;
   static constexpr int kL = kT + 4 * 1024;
@@ -132,10 +142,13 @@ PrefillLayout prefill_layout(int32_t num_seqs, int64_t total_blocks, int32_t H, 
 // ---- 1. plan ----------------------------------------------------------------------
 constexpr int kMaxSortedSeqs = 1024;   // longest-first chain order up to this many sequences
 
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu, int N,
-                                                    int ckpt_interval, int32_t* seq_blk_off,
-                                                    int32_t* seq_ck_off, int2* blk_info,
-                                                    int total_blocks, int32_t* seq_order) {
+// Per-sequence block and checkpoint offsets (prefix sums saturated at the host
+// copy's totals), the (first row, valid rows) of every block, and the chain's
+// sequence order. Index arithmetic and its clamping: kda_plan.h.
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu, int N, int64_t total_tokens,
+                                                    int ckpt_interval, int num_checkpoints,
+                                                    int32_t* seq_blk_off, int32_t* seq_ck_off,
+                                                    int2* blk_info, int total_blocks, int32_t* seq_order) {
   __shared__ int s_c[1024], s_k[1024];
   __shared__ int carry_c, carry_k;
   const int tid = threadIdx.x;
@@ -143,28 +156,28 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   __syncthreads();
   for (int base = 0; base < N; base += 1024) {
     const int n = base + tid;
-    const int len = n < N ? cu[n + 1] - cu[n] : 0;
-    const int vc = (len + kBT - 1) / kBT;
-    const int vk = ckpt_interval > 0 ? len / ckpt_interval : 0;
-    s_c[tid] = vc;
-    s_k[tid] = vk;
+    int s0 = 0, s1 = 0;
+    if (n < N) plan::clamp_seq(cu, n, total_tokens, s0, s1);
+    const int len = s1 - s0;
+    s_c[tid] = plan::seq_blocks(len);
+    s_k[tid] = ckpt_interval > 0 ? len / ckpt_interval : 0;
     __syncthreads();
     for (int d = 1; d < 1024; d <<= 1) {  // inclusive Hillis-Steele scan
       const int ac = tid >= d ? s_c[tid - d] : 0;
       const int ak = tid >= d ? s_k[tid - d] : 0;
       __syncthreads();
-      s_c[tid] += ac;
-      s_k[tid] += ak;
+      s_c[tid] = plan::sat_add(s_c[tid], ac, total_blocks);
+      s_k[tid] = plan::sat_add(s_k[tid], ak, num_checkpoints);
       __syncthreads();
     }
     if (n < N) {
-      seq_blk_off[n] = carry_c + s_c[tid] - vc;
-      seq_ck_off[n] = carry_k + s_k[tid] - vk;
+      seq_blk_off[n] = plan::sat_add(carry_c, tid > 0 ? s_c[tid - 1] : 0, total_blocks);
+      seq_ck_off[n] = plan::sat_add(carry_k, tid > 0 ? s_k[tid - 1] : 0, num_checkpoints);
     }
     __syncthreads();
     if (tid == 1023) {
-      carry_c += s_c[1023];
-      carry_k += s_k[1023];
+      carry_c = plan::sat_add(carry_c, s_c[1023], total_blocks);
+      carry_k = plan::sat_add(carry_k, s_k[1023], num_checkpoints);
     }
     __syncthreads();
   }
@@ -174,14 +187,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   }
   __syncthreads();
   for (int c = tid; c < total_blocks; c += 1024) {
-    // last n with seq_blk_off[n] <= c (skips empty sequences)
-    int lo = 0, hi = N - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (seq_blk_off[mid] <= c) lo = mid; else hi = mid - 1;
-    }
-    const int t0 = cu[lo] + kBT * (c - seq_blk_off[lo]);
-    const int cnt = min(kBT, cu[lo + 1] - t0);
+    const int n = plan::owner_of(seq_blk_off, N, c);
+    int s0, s1, t0, cnt;
+    plan::clamp_seq(cu, n, total_tokens, s0, s1);
+    plan::block_rows(s0, s1, c - seq_blk_off[n], total_tokens, t0, cnt);
     blk_info[c] = make_int2(t0, cnt);
   }
   // Chain order: sequences by block count, longest first (ties by index), so
@@ -428,7 +437,14 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       if (!(wave == which || (kWaves == 1 && wave == 0))) continue;
-      bf16x8 X[2][R::NP], Km[2][R::NP];
+      // which 0: Kp and A = diag(beta) Kp Km^T; which 1: Qt and L = Qt Km^T.
+      // Both products take three bf16 terms (hi hi + lo hi + hi lo). The
+      // diagonal of L is q_t . k_t (the decays cancel), formed here in fp32
+      // from the inputs: a token's own term then keeps its relative accuracy
+      // when q_t . k_t nearly cancels (with a zero start state it is the whole
+      // output of a sequence's first token).
+      bf16x8 X[2][R::NP], Xl[2][R::NP], Km[2][R::NP], Kml[2][R::NP];
+      float qk[2] = {0.f, 0.f};          // partial q_t . k_t over this lane's channels
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -438,14 +454,33 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
           const float rs = which ? rq(t) : rk(t);
           const f32x4 x0 = (which ? piece(q, t, c0) : kpiece(t, c0)) * rs;
           const f32x4 x1 = (which ? piece(q, t, c1) : kpiece(t, c1)) * rs;
-          X[u][p] = cat(to_bf16x4(x0 * P0), to_bf16x4(x1 * P1));
           const f32x4 k0 = which ? kpiece(t, c0) * rk(t) : x0, k1 = which ? kpiece(t, c1) * rk(t) : x1;
           f32x4 r0, r1;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) { r0[i] = k0[i] / P0[i]; r1[i] = k1[i] / P1[i]; }
-          Km[u][p] = cat(to_bf16x4(r0), to_bf16x4(r1));
+          for (int i = 0; i < 4; ++i) {
+            r0[i] = k0[i] / P0[i];
+            r1[i] = k1[i] / P1[i];
+            qk[u] += x0[i] * k0[i] + x1[i] * k1[i];
+          }
+          bf16x4 h0, l0, h1, l1;
+          split_bf16(r0, h0, l0);
+          split_bf16(r1, h1, l1);
+          Km[u][p] = cat(h0, h1);
+          Kml[u][p] = cat(l0, l1);
+          split_bf16(x0 * P0, h0, l0);
+          split_bf16(x1 * P1, h1, l1);
+          X[u][p] = cat(h0, h1);
+          Xl[u][p] = cat(l0, l1);
+          if (which == 0) *(bf16x8*)(rec + R::kKpl + (u * R::NP + p) * 1024 + lane * 16) = Xl[u][p];
           *(bf16x8*)(rec + (which ? R::kQt : R::kKp) + (u * R::NP + p) * 1024 + lane * 16) = X[u][p];
         }
+      // q_t . k_t of token 16u + mm: the four lanes mm + 16 gq hold its channels
+      // (wave-uniform branch: every lane takes part)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        qk[u] += __shfl_xor(qk[u], 16);
+        qk[u] += __shfl_xor(qk[u], 32);
+      }
 #pragma unroll
       for (int ut = 0; ut < 2; ++ut) {
         bf16x4 lfrag[2];
@@ -454,8 +489,17 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
           if (us <= ut) {
 #pragma unroll
-            for (int p = 0; p < R::NP; ++p)
-              acc = which ? mfma32(Km[us][p], X[ut][p], acc) : mfma32(X[ut][p], Km[us][p], acc);
+            for (int p = 0; p < R::NP; ++p) {
+              if (which) {
+                acc = mfma32(Km[us][p], X[ut][p], acc);
+                acc = mfma32(Km[us][p], Xl[ut][p], acc);
+                acc = mfma32(Kml[us][p], X[ut][p], acc);
+              } else {
+                acc = mfma32(X[ut][p], Km[us][p], acc);
+                acc = mfma32(Xl[ut][p], Km[us][p], acc);
+                acc = mfma32(X[ut][p], Kml[us][p], acc);
+              }
+            }
           }
           if (which == 0) {
 #pragma unroll
@@ -466,7 +510,10 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
           } else {
             f32x4 lv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) lv[i] = 16 * us + 4 * gq + i <= 16 * ut + mm ? acc[i] : 0.f;
+            for (int i = 0; i < 4; ++i) {
+              const int sr = 16 * us + 4 * gq + i, tr = 16 * ut + mm;
+              lv[i] = sr < tr ? acc[i] : (sr == tr ? qk[ut] : 0.f);
+            }
             lfrag[us] = to_bf16x4(lv);
           }
         }
@@ -561,10 +608,11 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
 // One barrier per block. Barrier B0 ends the prologue; block j's compute step
 // runs between barriers B(j+1) and B(j+2); a final barrier follows the last.
 //
-// Buffer lifetimes (3 ring slots, 2 partial-product sets, 2 delta sets):
-//  - block c is stored to slot c % 3 before B(c); the compute waves read it
-//    (as the next block's operands) and the output wave reads its L between
-//    B(c) and B(c + 2); the loaders overwrite it only after B(c + 2);
+// Buffer lifetimes (2 ring slots, 2 partial-product sets, 2 delta sets):
+//  - block c is stored to slot c % 2 before B(c); between B(c) and B(c + 1)
+//    the compute waves read it (as the next block's operands, its P_16 too)
+//    and the output wave reads its Q~ and L into registers; the loaders
+//    overwrite it only after B(c + 1);
 //  - the K~+ S partials and the bf16 state of block c (xbuf[c % 2],
 //    sbuf[c % 2]) are written before B(c + 1) and read between B(c + 1) and
 //    B(c + 2); they are overwritten after B(c + 2);
@@ -576,7 +624,7 @@ constexpr int kUnitTransition = 2;
 constexpr int kLoaders = 4;            // loader waves per workgroup
 constexpr int kInFlight = 4;           // blocks each loader keeps in flight
 constexpr int kTouchAhead = 4;         // blocks beyond the loads that the L2 touches run
-constexpr int kRing = 3;               // LDS slots
+constexpr int kRing = 2;               // LDS slots
 
 template <int D, typename TIn>
 struct ChainCfg {
@@ -594,19 +642,18 @@ struct ChainCfg {
   static constexpr int kXBytes = 2 * kHalves * 2 * kWave * 16 + 2 * R::NP * kWave * 16;   // xbuf, sbuf
   static constexpr int kDBytes = 2 * 2 * kWave * 16;                 // dbuf
   static_assert(kVBytes % 1024 == 0, "whole V fragments");
-  static_assert(kRing == 3, "buffer lifetimes");
+  static_assert(kRing == 2, "buffer lifetimes");
   static_assert(kRing * kSlot + kXBytes + kDBytes <= 160 * 1024, "LDS");
   static_assert(kInFlight * (kPerLoader + 1) < 64, "vmcnt field");   // + one L2 touch per block
 };
 
-// kSplitS: K~+ S takes the state as a bf16 hi/lo pair (two MFMAs per tile)
-// instead of one bf16 value. Used without a decay (DeltaNet): K~+ is then
-// exactly the bf16 key, nothing forgets the state, and K~+ S nearly cancels V,
-// so the state's bf16 rounding dominates the error of V - K~+ S (measured: final
-// states about 1.5e-3 relative with one bf16 term, at every length).
-template <int D, typename TIn, bool kSplitS>
+// K~+ S takes both the key and the state as bf16 hi / lo pairs (hi hi + hi lo +
+// lo hi): with slow decay K~+ is close to the bf16 key, the state is long
+// lived and K~+ S nearly cancels V, so a single bf16 term of either operand
+// dominates the error of V - K~+ S.
+template <int D, typename TIn>
 __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
-    const TIn* __restrict__ v, const int32_t* __restrict__ cu,
+    const TIn* __restrict__ v, const int32_t* __restrict__ cu, int64_t total_tokens, int nck,
     const int32_t* __restrict__ seq_blk_off, const int32_t* __restrict__ seq_ck_off,
     const char* __restrict__ records, const float* initial_state, float* final_state,
     float* __restrict__ ckpts, TIn* __restrict__ o, int N, int H, int ckpt_interval,
@@ -653,10 +700,10 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   }
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int mm = lane % 16, gq = lane / 16;
-  const int seq_t0 = cu[n], seq_len = cu[n + 1] - seq_t0;
-  const int seq_nblk = (seq_len + kBT - 1) / kBT;
-  const int bps = (seq_nblk + P - 1) / P;                     // blocks per segment
-  const int blk0 = min(seg * bps, seq_nblk), blk1 = min(blk0 + bps, seq_nblk);
+  int seq_t0, seq_t1, blk0, blk1;
+  plan::clamp_seq(cu, n, total_tokens, seq_t0, seq_t1);
+  const int seq_len = seq_t1 - seq_t0;
+  plan::segment_blocks(plan::seq_blocks(seq_len), seg, P, seq_blk_off[n], total_blocks, blk0, blk1);
   const int seg_off = kBT * blk0;                             // tokens of the sequence before it
   const int t_begin = seq_t0 + seg_off;
   const int len = max(0, min(seq_len - seg_off, kBT * (blk1 - blk0)));
@@ -677,19 +724,27 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     // lane. (Q~ S)^T is formed here from the bf16 state the compute waves
     // publish, off their MFMA pipes.
     f32x4 P[2];
-    bf16x8 Lf[2];
-    auto fetch = [&](int c) __attribute__((always_inline)) {   // between B(c + 1) and B(c + 2)
+    bf16x8 Lf[2], Qn[2][R::NP], Ln[2];
+    // Q~ and L of block c, read between B(c) and B(c + 1), while its slot is valid
+    auto preload = [&](int c) __attribute__((always_inline)) {
       const char* slot = slot_of(c);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        Ln[u] = *(const bf16x8*)(slot + R::kL + u * 1024 + lane * 16);
+#pragma unroll
+        for (int p = 0; p < R::NP; ++p) Qn[u][p] = *(const bf16x8*)(slot + R::kQt + (u * R::NP + p) * 1024 + lane * 16);
+      }
+    };
+    auto fetch = [&](int c) __attribute__((always_inline)) {   // between B(c + 1) and B(c + 2)
       bf16x8 sf[R::NP];
 #pragma unroll
       for (int p = 0; p < R::NP; ++p) sf[p] = sbuf[c % 2][p][lane];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        Lf[u] = *(const bf16x8*)(slot + R::kL + u * 1024 + lane * 16);
+        Lf[u] = Ln[u];
         P[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int p = 0; p < R::NP; ++p)
-          P[u] = mfma32(sf[p], *(const bf16x8*)(slot + R::kQt + (u * R::NP + p) * 1024 + lane * 16), P[u]);
+        for (int p = 0; p < R::NP; ++p) P[u] = mfma32(sf[p], Qn[u][p], P[u]);
       }
     };
     auto emit = [&](int c) __attribute__((always_inline)) {    // between B(c + 2) and B(c + 3)
@@ -707,10 +762,12 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       }
     };
     lds_barrier();
+    preload(0);
     for (int j = 0; j < nblk; ++j) {
       lds_barrier();
       if (j >= 1) emit(j - 1);
       fetch(j);
+      preload(j + 1);   // (past the last block it reads a stale slot, unused)
     }
     lds_barrier();
     emit(nblk - 1);
@@ -874,17 +931,20 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   if (nblk > 0) {
     const int ck_base = ckpt_interval > 0 ? seq_ck_off[n] : 0;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    bf16x8 kp[2][PW];                  // next block's K~+ fragments
+    bf16x8 kp[2][PW], kpl[2][PW];      // next block's K~+ fragments (hi, lo)
     bf16x8 th[2], tl[2];               // T hi / lo per token tile
     f32x4 vv[2];                       // V[16u + 4gq .. +3][mm]
     bf16x8 khh[TW], khl[TW];           // Kh hi / lo per row tile
-    f32x4 pc[TW];                      // Pc of rows 16rt + 4gq .. +3
+    f32x4 pc[TW], p16[TW];             // Pc and P_16 of rows 16rt + 4gq .. +3
     auto read_kp = [&](const char* slot) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int qq = 0; qq < PW; ++qq)
+        {
           kp[u][qq] = *(const bf16x8*)(slot + R::kKp + (u * R::NP + hf * PW + qq) * 1024 + lane * 16);
+          kpl[u][qq] = *(const bf16x8*)(slot + R::kKpl + (u * R::NP + hf * PW + qq) * 1024 + lane * 16);
+        }
     };
     auto read_tv = [&](const char* slot) __attribute__((always_inline)) {
 #pragma unroll
@@ -903,6 +963,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
         khh[t] = *(const bf16x8*)(slot + R::kKh + (2 * rt) * 1024 + lane * 16);
         khl[t] = *(const bf16x8*)(slot + R::kKh + (2 * rt + 1) * 1024 + lane * 16);
         pc[t] = *(const f32x4*)(slot + R::kPc + (16 * rt + 4 * gq) * 4);
+        p16[t] = *(const f32x4*)(slot + R::kPc + (D + 16 * rt + 4 * gq) * 4);
       }
     };
     // partial K~+ S of a block over this wave's rows: it stays in u_own and
@@ -918,22 +979,24 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
         bf16x4 h0, l0, h1 = zero, l1 = zero;
         split_bf16(acc[2 * qq], h0, l0);
         if (two) split_bf16(acc[2 * qq + 1], h1, l1);
-        const bf16x8 Bs = cat(h0, h1);
+        const bf16x8 Bs = cat(h0, h1), Bl = cat(l0, l1);
         sbuf[c % 2][hf * PW + qq][lane] = Bs;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           U[u] = mfma32(kp[u][qq], Bs, U[u]);
-          if constexpr (kSplitS) UL[u] = mfma32(kp[u][qq], cat(l0, l1), UL[u]);
+          UL[u] = mfma32(kp[u][qq], Bl, UL[u]);
+          UL[u] = mfma32(kpl[u][qq], Bs, UL[u]);
         }
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        if constexpr (kSplitS) U[u] += UL[u];
+        U[u] += UL[u];
         u_own[u] = U[u];
         if (NCW > 1) xbuf[c % 2][hf][u][lane] = U[u];
       }
     };
     auto store_state = [&](const f32x4* st, int idx) __attribute__((always_inline)) {
+      if (ck_base + idx >= nck) return;   // (only when the two cu_seqlens copies differ, kda_plan.h)
       float* dst = ckpts + ((size_t)(ck_base + idx) * H + h) * D * D;
 #pragma unroll
       for (int t = 0; t < TW; ++t)
@@ -993,13 +1056,11 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       if (ckpt_interval > 0 && write_o && mid <= len && (seg_off + mid) % ckpt_interval == 0) {
         const bf16x4 zero = {};
         const bf16x8 dh_m = cat(dh0, zero), dl_m = cat(dlo0, zero);
-        const char* cslot = slot_of(j);
         f32x4 sm[TW];
 #pragma unroll
         for (int t = 0; t < TW; ++t) {
           const f32x4 upd = mfma32(khl[t], dh_m, mfma32(khh[t], dl_m, mfma32(khh[t], dh_m, z)));
-          const f32x4 p16 = *(const f32x4*)(cslot + R::kPc + (D + 16 * (t0 + t) + 4 * gq) * 4);
-          sm[t] = p16 * acc[t] + (p16 / pc[t]) * upd;
+          sm[t] = p16[t] * acc[t] + (p16[t] / pc[t]) * upd;
         }
         store_state(sm, (seg_off + mid) / ckpt_interval - 1);
       }
@@ -1094,7 +1155,8 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
 
   int32_t* seq_order = (int32_t*)(ws + L.seq_order);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, a.num_seqs,
-                     a.ckpt_interval, seq_blk_off, seq_ck_off, blk_info, (int)a.total_blocks, seq_order);
+                     (int64_t)a.total_tokens, a.ckpt_interval, (int)a.num_checkpoints, seq_blk_off,
+                     seq_ck_off, blk_info, (int)a.total_blocks, seq_order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.total_blocks > 0) {
@@ -1116,11 +1178,12 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   const int64_t nh = (int64_t)a.num_seqs * a.H;
   const int P = a.segments;
   float* segs = P > 1 ? (float*)(ws + L.segs) : nullptr;
-  auto chain = a.gate == KDA_GATE_NONE ? chain_kernel<D, TIn, true> : chain_kernel<D, TIn, false>;
+  auto chain = chain_kernel<D, TIn>;
   auto run_chain = [&](int units, int pass) {
     const int64_t groups = (nh * units + 7) / 8;     // 8 units x D/16 slices per group of workgroups
     hipLaunchKernelGGL(chain, dim3((unsigned)(groups * 8 * (D / 16))), dim3(Cfg::kThreads), 0, a.stream,
-                       (const TIn*)a.v, a.cu_seqlens, seq_blk_off, seq_ck_off, records, a.initial_state,
+                       (const TIn*)a.v, a.cu_seqlens, (int64_t)a.total_tokens, (int)a.num_checkpoints,
+                       seq_blk_off, seq_ck_off, records, a.initial_state,
                        a.final_state, a.checkpoints, (TIn*)a.o, a.num_seqs, a.H, a.ckpt_interval,
                        a.scale, (int)a.total_blocks, segs, P, pass, seq_order);
     return hipGetLastError();

@@ -31,6 +31,7 @@ GATE_CHANNEL, GATE_HEAD, GATE_NONE = 0, 1, 2     # KDA, Gated DeltaNet, DeltaNet
 
 
 MAX_SEGMENTS = 16
+SEGMENT_SLICE_LIMIT = 80          # forced segments need num_seqs * H * (D / 16) <= this
 
 
 class Options(ctypes.Structure):
@@ -68,7 +69,7 @@ def lib():
         L.kda_prefill_num_checkpoints.restype = ctypes.c_int64
         L.kda_prefill_num_checkpoints.argtypes = [_i32p, _i32, _i32]
         L.kda_prefill_workspace_size.restype = ctypes.c_size_t
-        L.kda_prefill_workspace_size.argtypes = [_i32p, _i32, _i32, _i32, _i32]
+        L.kda_prefill_workspace_size.argtypes = [_i32, ctypes.c_int64, _i32, _i32, _i32]
         L.kda_prefill_chunked.restype = ctypes.c_int
         L.kda_prefill_chunked.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i32p, _i32,
                                           _i32, _i32, _i32, ctypes.c_float, ctypes.c_float, _vp,
@@ -157,9 +158,15 @@ def num_checkpoints(cu_seqlens, ckpt_interval: int) -> int:
     return int(r)
 
 
-def workspace_size(cu_seqlens, H: int, D: int) -> int:
-    cu, p = _host_cu(cu_seqlens)
-    return int(lib().kda_prefill_workspace_size(p, len(cu) - 1, H, D, D))
+def kda_check_cu(cu_host) -> int:
+    """-1 if the host offsets are malformed (cu[0] != 0 or decreasing)."""
+    return lib().kda_prefill_num_checkpoints(cu_host.numpy().ctypes.data_as(_i32p), len(cu_host) - 1, 0)
+
+
+def workspace_size(num_seqs: int, total_tokens: int, H: int, D: int) -> int:
+    """kda_prefill_workspace_size: bytes of device workspace for num_seqs
+    sequences of total_tokens packed tokens (independent of the lengths)."""
+    return int(lib().kda_prefill_workspace_size(int(num_seqs), int(total_tokens), H, D, D))
 
 
 @dataclass
@@ -174,7 +181,9 @@ class PrefillPlan:
 
 def make_plan(cu_seqlens, H: int, D: int, device, ckpt_interval: int = 0) -> PrefillPlan:
     cu_host, p = _host_cu(cu_seqlens)
-    ws = workspace_size(cu_host, H, D)
+    if int(kda_check_cu(cu_host)) < 0:
+        raise KdaError(KDA_ERR_INVALID_ARG, "cu_seqlens")
+    ws = workspace_size(len(cu_host) - 1, int(cu_host[-1]), H, D)
     workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
     return PrefillPlan(cu_host, cu_host.to(device), workspace,
                        num_checkpoints(cu_host, ckpt_interval) if ckpt_interval else 0,

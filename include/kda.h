@@ -139,15 +139,18 @@ const char* kda_status_string(kda_status status);
 int64_t kda_prefill_num_checkpoints(const int32_t* cu_seqlens_host, int32_t num_seqs,
                                     int32_t ckpt_interval);
 
-/* Bytes of device workspace kda_prefill_chunked needs for these lengths and
- * shapes (0 if the arguments are invalid). The workspace holds per-block
- * tables and the per-block decayed operands of the chunked form (about
- * 1.2 KiB per token and head at D = 128), plus, where segments may be used
- * (num_seqs * H * (Dv / 16) <= KDA_SEGMENT_SLICE_LIMIT), three fp32 states
- * per sequence, head and segment; its contents are scratch and need no
- * initialisation. */
-size_t kda_prefill_workspace_size(const int32_t* cu_seqlens_host, int32_t num_seqs,
-                                  int32_t H, int32_t Dk, int32_t Dv);
+/* Bytes of device workspace kda_prefill_chunked needs for num_seqs sequences
+ * of total_tokens packed tokens with H heads (0 if the arguments are
+ * invalid). The workspace holds per-sequence and per-block tables and the
+ * per-block decayed operands of the chunked form: 47 KiB per 32-token block
+ * and head at D = 128 (about 1.5 KiB per token and head), sized for the most
+ * blocks any split of total_tokens into num_seqs sequences can have,
+ * total_tokens / 32 + num_seqs. Where segments may be used
+ * (num_seqs * H * (Dv / 16) <= KDA_SEGMENT_SLICE_LIMIT) it also holds three
+ * fp32 Dk x Dv states per sequence, head and segment. Its contents are
+ * scratch and need no initialisation. */
+size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t Dk,
+                                  int32_t Dv);
 
 /* Chunked prefill over packed variable-length sequences.
  *
@@ -157,8 +160,15 @@ size_t kda_prefill_workspace_size(const int32_t* cu_seqlens_host, int32_t num_se
  *   g           [T, H, Dk]  fp32 log-decay, clamped to [g_min, 0] on load
  *   beta        [T, H]      fp32
  *   cu_seqlens       [num_seqs + 1] int32, DEVICE copy of the offsets
- *   cu_seqlens_host  [num_seqs + 1] int32, HOST copy (same values; used for
- *                    validation and launch sizes): cu[0] = 0, non-decreasing.
+ *   cu_seqlens_host  [num_seqs + 1] int32, HOST copy: cu[0] = 0,
+ *                    non-decreasing. It is validated and sizes the launches
+ *                    (grids, checkpoint count) without a device-to-host copy.
+ *                    PRECONDITION: both copies hold the same values. The
+ *                    kernels read the device copy (so a captured graph can
+ *                    replay with new offsets of the same totals) and clamp
+ *                    every offset they derive from it to the host copy's
+ *                    total tokens and checkpoint count, so copies that differ
+ *                    give wrong results but no access outside the buffers.
  *                    A sequence of length 0 is allowed (its final state equals
  *                    its initial state, it has no outputs).
  *   scale       readout scale (1.0 reproduces o_t = S_t^T q_t)
@@ -177,7 +187,8 @@ size_t kda_prefill_workspace_size(const int32_t* cu_seqlens_host, int32_t num_se
  *                  recurrent state is kept only at sparse token intervals).
  *                  Ignored when ckpt_interval == 0.
  *   ckpt_interval  0 (no checkpoints) or a positive multiple of KDA_CHUNK.
- *   workspace      device scratch of at least kda_prefill_workspace_size bytes,
+ *   workspace      device scratch of at least
+ *                  kda_prefill_workspace_size(num_seqs, T, H, Dk, Dv) bytes,
  *                  256-byte aligned.
  * initial_state may alias final_state (the state is read before it is written).
  * Errors: KDA_ERR_INVALID_ARG (null required pointer, negative sizes,
@@ -216,7 +227,10 @@ kda_status kda_prefill_chunked_ex(const void* q, const void* k, const void* v, k
  *   g      [N, H, Dk] fp32 log-decay (clamped to [g_min, 0]);  beta [N, H] fp32
  *   state  [N, H, Dk, Dv] fp32, read and updated IN PLACE
  *   o      [N, H, Dv] dtype
- * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_HIP. */
+ * g_min must lie in [-FLT_MAX, 0] (any finite floor; decode has no lower
+ * limit, since it multiplies the state by alpha directly).
+ * Errors: KDA_ERR_INVALID_ARG (null pointer, negative N, H <= 0, g_min
+ * outside [-FLT_MAX, 0] or NaN), KDA_ERR_UNSUPPORTED, KDA_ERR_HIP. */
 kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype dtype,
                            const float* g, const float* beta, float* state, void* o,
                            int32_t N, int32_t H, int32_t Dk, int32_t Dv, float scale,
@@ -248,7 +262,8 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
  *   opt    gate layout and front end (see kda_options), or NULL for the
  *          KDA gate with inputs used as given
  * Errors: KDA_ERR_INVALID_ARG (null required pointer, T outside
- * [1, KDA_DECODE_MAX_TOKENS], negative N, H <= 0, bad options),
+ * [1, KDA_DECODE_MAX_TOKENS], negative N, H <= 0, bad options, g_min as in
+ * kda_decode_step),
  * KDA_ERR_UNSUPPORTED, KDA_ERR_HIP. */
 kda_status kda_decode_tokens(const void* q, const void* k, const void* v, kda_dtype dtype,
                              const float* g, const float* beta, float* state,

@@ -58,22 +58,29 @@ def test_checkpoint_counts(L):
 
 
 def test_workspace_size(L):
-    # per (32-token block, head) record: 39 KiB at D = 128, 13 KiB at D = 16,
-    # plus tables
-    w = kda.workspace_size(cu(8192), 32, 128)
-    assert 256 * 32 * 39 * 1024 <= w < 256 * 32 * 39 * 1024 + 8192
-    # few slices (sequences x heads x D/16 <= 80): segment states are added,
-    # 3 fp32 D x D states per sequence, head and segment (16 segments at most)
-    w16 = kda.workspace_size(cu(64), 2, 16)
-    seg16 = 1 * 16 * 2 * 3 * 16 * 16 * 4
-    assert 2 * 2 * 13 * 1024 + seg16 <= w16 < 2 * 2 * 13 * 1024 + seg16 + 2048
-    w4 = kda.workspace_size(cu(8192), 4, 128)
-    seg128 = 1 * 16 * 4 * 3 * 128 * 128 * 4
-    assert 256 * 4 * 39 * 1024 + seg128 <= w4 < 256 * 4 * 39 * 1024 + seg128 + 4096
-    # a ragged tail still takes a whole block
-    assert kda.workspace_size(cu(33, 1), 1, 128) >= 3 * 39 * 1024
-    assert kda.workspace_size(cu(10), 2, 64) == 0          # unsupported D
-    assert kda.workspace_size([0, 5, 2], 2, 128) == 0       # malformed offsets
+    # per (32-token block, head) record: 47 KiB at D = 128, 15 KiB at D = 16,
+    # sized for the most blocks num_seqs sequences of T tokens can have,
+    # T / 32 + num_seqs, plus tables
+    rec128, rec16 = 47 * 1024, 15 * 1024
+    seg = lambda N, H, D: N * 16 * H * 3 * D * D * 4     # 16 segments at most
+    w = kda.workspace_size(1, 8192, 32, 128)             # 32 x 8 slices > 80: no segments
+    assert 257 * 32 * rec128 <= w < 257 * 32 * rec128 + 8192
+    # the size depends on the total only, not on how it is split
+    w4 = kda.workspace_size(1, 8192, 4, 128)             # 4 x 8 slices <= 80: segment states
+    assert 257 * 4 * rec128 + seg(1, 4, 128) <= w4 < 257 * 4 * rec128 + seg(1, 4, 128) + 4096
+    w16 = kda.workspace_size(1, 64, 2, 16)
+    assert 3 * 2 * rec16 + seg(1, 2, 16) <= w16 < 3 * 2 * rec16 + seg(1, 2, 16) + 2048
+    # ragged lengths never need more than T / 32 + num_seqs blocks
+    wv = kda.workspace_size(3, 97, 1, 128)
+    assert (97 // 32 + 3) * rec128 <= wv
+    for lens in ((33, 33, 31), (1, 1, 95), (97, 0, 0), (32, 32, 33)):
+        blocks = sum((x + 31) // 32 for x in lens)
+        assert blocks * rec128 <= wv
+    assert kda.workspace_size(1, 10, 2, 64) == 0          # unsupported D
+    assert kda.workspace_size(-1, 10, 2, 128) == 0
+    assert kda.workspace_size(1, -1, 2, 128) == 0
+    assert kda.workspace_size(1, 10, 0, 128) == 0
+    assert kda.workspace_size(1, 2 ** 40, 1, 128) == 0    # too many blocks
 
 
 def _prefill_status(L, **over):
@@ -126,6 +133,11 @@ def test_decode_argument_errors(L):
     assert call(state=None) == kda.KDA_ERR_INVALID_ARG
     assert call(state=ctypes.c_void_p(0x1004)) == kda.KDA_ERR_INVALID_ARG
     assert call(N=0) == kda.KDA_OK                                    # nothing to do
+    # the decay floor: any finite value at or below 0
+    assert call(g_min=0.5) == kda.KDA_ERR_INVALID_ARG
+    assert call(g_min=float("nan")) == kda.KDA_ERR_INVALID_ARG
+    assert call(g_min=float("-inf")) == kda.KDA_ERR_INVALID_ARG
+    assert call(g_min=-40.0, N=0) == kda.KDA_OK
 
 
 def test_decode_tokens_argument_errors(L):
@@ -155,11 +167,20 @@ def test_decode_tokens_argument_errors(L):
     assert call(g=None) == kda.KDA_ERR_INVALID_ARG
     assert call(g=None, fe=ctypes.byref(kda.Options(gate=kda.GATE_HEAD))) == kda.KDA_ERR_INVALID_ARG
     assert call(g=None, fe=ctypes.byref(kda.Options(gate=kda.GATE_NONE)), N=0) == kda.KDA_OK
+    assert call(g_min=1e-3) == kda.KDA_ERR_INVALID_ARG
+    assert call(g_min=float("nan"), N=0) == kda.KDA_ERR_INVALID_ARG
 
 
 def test_decode_max_tokens_matches_header():
     m = re.search(r"#define\s+KDA_DECODE_MAX_TOKENS\s+(\d+)", open(HEADER).read())
     assert m and int(m.group(1)) == kda.DECODE_MAX_TOKENS
+
+
+def test_segment_limits_match_header():
+    text = open(HEADER).read()
+    for name, value in (("KDA_MAX_SEGMENTS", kda.MAX_SEGMENTS), ("KDA_SEGMENT_SLICE_LIMIT", kda.SEGMENT_SLICE_LIMIT)):
+        m = re.search(r"#define\s+%s\s+(\d+)" % name, text)
+        assert m and int(m.group(1)) == value, name
 
 
 def test_prefill_options_argument_errors(L):
@@ -184,6 +205,7 @@ def test_prefill_options_argument_errors(L):
     for bad in (kda.Options(segments=17), kda.Options(segments=-1)):
         assert call(ctypes.byref(bad)) == kda.KDA_ERR_INVALID_ARG
     assert call(ctypes.byref(kda.Options(segments=4))) == kda.KDA_ERR_WORKSPACE
+    assert call(ctypes.byref(kda.Options(segments=16))) == kda.KDA_ERR_WORKSPACE
     assert call(ctypes.byref(kda.Options(segments=4)), H=16) == kda.KDA_ERR_INVALID_ARG   # 128 slices
     assert call(ctypes.byref(kda.Options(segments=1)), H=16) == kda.KDA_ERR_WORKSPACE
     # no gate: g may be NULL (the next failing check is the workspace)
