@@ -106,14 +106,19 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_
                                 checkpoints, o, workspace, workspace_bytes, nullptr, stream);
 }
 
-kda_status kda_prefill_chunked_ex(const void* q, const void* k, const void* v, kda_dtype dtype,
-                                  const float* g, const float* beta, const int32_t* cu_seqlens,
-                                  const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
-                                  int32_t Dk, int32_t Dv, float scale, float g_min,
-                                  const float* initial_state, float* final_state,
-                                  int32_t ckpt_interval, float* checkpoints, void* o,
-                                  void* workspace, size_t workspace_bytes,
-                                  const kda_options* opt, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The prefill behind both workspace conventions: the caller's workspace, or
+// (use_scratch) the library's static per-device scratch, looked up only after
+// every argument and the size have been checked.
+kda_status prefill_impl(const void* q, const void* k, const void* v, kda_dtype dtype, const float* g,
+                        const float* beta, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                        int32_t num_seqs, int32_t H, int32_t Dk, int32_t Dv, float scale, float g_min,
+                        const float* initial_state, float* final_state, int32_t ckpt_interval,
+                        float* checkpoints, void* o, void* workspace, size_t workspace_bytes,
+                        bool use_scratch, const kda_options* opt, hipStream_t stream) {
   if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
   if (!options_ok(opt)) return KDA_ERR_INVALID_ARG;
   const bool need_g = gate_of(opt) != KDA_GATE_NONE;
@@ -148,6 +153,16 @@ kda_status kda_prefill_chunked_ex(const void* q, const void* k, const void* v, k
     P = kda::auto_segments(num_seqs, H, Dk, max_blocks);
   }
   const kda::PrefillLayout L = kda::prefill_layout(num_seqs, blocks, H, Dk);
+  if (use_scratch) {
+    if (L.total > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
+    // the scratch of the device the work runs on: the stream's, which must be
+    // the current one (the array's address is looked up with it current)
+    int cur = -1, dev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &dev) != hipSuccess) return KDA_ERR_HIP;
+    if (dev != cur) return KDA_ERR_INVALID_ARG;
+    if (kda::noalloc_scratch(&workspace) != hipSuccess) return KDA_ERR_HIP;
+    workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255)) return KDA_ERR_WORKSPACE;
 
   kda::PrefillArgs a;
@@ -166,6 +181,35 @@ kda_status kda_prefill_chunked_ex(const void* q, const void* k, const void* v, k
   a.bf16 = dtype == KDA_BF16;
   a.stream = stream;
   return from_hip(kda::launch_prefill(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill_chunked_ex(const void* q, const void* k, const void* v, kda_dtype dtype,
+                                  const float* g, const float* beta, const int32_t* cu_seqlens,
+                                  const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
+                                  int32_t Dk, int32_t Dv, float scale, float g_min,
+                                  const float* initial_state, float* final_state,
+                                  int32_t ckpt_interval, float* checkpoints, void* o,
+                                  void* workspace, size_t workspace_bytes,
+                                  const kda_options* opt, hipStream_t stream) {
+  return prefill_impl(q, k, v, dtype, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, Dk, Dv, scale,
+                      g_min, initial_state, final_state, ckpt_interval, checkpoints, o, workspace,
+                      workspace_bytes, false, opt, stream);
+}
+
+kda_status kda_prefill_chunked_noalloc(const void* q, const void* k, const void* v, kda_dtype dtype,
+                                       const float* g, const float* beta, const int32_t* cu_seqlens,
+                                       const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
+                                       int32_t Dk, int32_t Dv, float scale, float g_min,
+                                       const float* initial_state, float* final_state,
+                                       int32_t ckpt_interval, float* checkpoints, void* o,
+                                       const kda_options* opt, hipStream_t stream) {
+  return prefill_impl(q, k, v, dtype, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, Dk, Dv, scale,
+                      g_min, initial_state, final_state, ckpt_interval, checkpoints, o, nullptr, 0, true,
+                      opt, stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtype dtype,

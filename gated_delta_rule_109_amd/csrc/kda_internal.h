@@ -81,4 +81,8 @@ int32_t auto_segments(int32_t num_seqs, int32_t H, int32_t D, int64_t max_blocks
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 
+// Device address of the static scratch (KDA_NOALLOC_SCRATCH_BYTES) on the
+// current device, looked up on the first call per device and kept.
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace kda

@@ -59,6 +59,8 @@
 #include "kda_internal.h"
 #include "kda_plan.h"
 
+#include <atomic>
+
 namespace kda {
 
 constexpr int kBT = kBlockTokens;   // tokens per block (two chunks)
@@ -1195,6 +1197,33 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return run_chain(P - 1, 1);
+}
+
+// ---- static scratch of kda_prefill_chunked_noalloc ----------------------------------
+// A workspace for callers that cannot allocate: every GPU that loads this code
+// holds its own copy until the process ends, and calls on one GPU share it.
+// In host code the array's name is not a device address: the address is
+// looked up once per device with hipGetSymbolAddress (with that device
+// current) and only that address is handed to the kernels.
+static __device__ __align__(256) char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // (two threads may both look it up; both get the same address)
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || ((uintptr_t)p & 255)) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {

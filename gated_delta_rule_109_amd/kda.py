@@ -23,7 +23,8 @@ CHUNK = 16
 LN_HALF = math.log(0.5)
 
 EXPORTED = ("kda_status_string", "kda_prefill_num_checkpoints", "kda_prefill_workspace_size",
-            "kda_prefill_chunked", "kda_prefill_chunked_ex", "kda_decode_step", "kda_decode_tokens")
+            "kda_prefill_chunked", "kda_prefill_chunked_ex", "kda_prefill_chunked_noalloc",
+            "kda_decode_step", "kda_decode_tokens")
 DECODE_MAX_TOKENS = 16
 FE_L2NORM_QK, FE_GATE_LOGITS, FE_BETA_LOGITS = 1, 2, 4
 FE_ALL = FE_L2NORM_QK | FE_GATE_LOGITS | FE_BETA_LOGITS
@@ -32,6 +33,7 @@ GATE_CHANNEL, GATE_HEAD, GATE_NONE = 0, 1, 2     # KDA, Gated DeltaNet, DeltaNet
 
 MAX_SEGMENTS = 16
 SEGMENT_SLICE_LIMIT = 80          # forced segments need num_seqs * H * (D / 16) <= this
+NOALLOC_SCRATCH_BYTES = 256 << 20  # static scratch of kda_prefill_chunked_noalloc
 
 
 class Options(ctypes.Structure):
@@ -83,6 +85,9 @@ def lib():
                                         ctypes.POINTER(Options), _vp]
         L.kda_prefill_chunked_ex.restype = ctypes.c_int
         L.kda_prefill_chunked_ex.argtypes = L.kda_prefill_chunked.argtypes[:-1] + [
+            ctypes.POINTER(Options), _vp]
+        L.kda_prefill_chunked_noalloc.restype = ctypes.c_int
+        L.kda_prefill_chunked_noalloc.argtypes = L.kda_prefill_chunked.argtypes[:-3] + [
             ctypes.POINTER(Options), _vp]
         _lib = L
     return _lib
@@ -171,20 +176,26 @@ def workspace_size(num_seqs: int, total_tokens: int, H: int, D: int) -> int:
 
 @dataclass
 class PrefillPlan:
-    """Host and device copies of cu_seqlens plus a workspace sized for them."""
+    """Host and device copies of cu_seqlens plus a workspace sized for them
+    (None for kda_prefill_chunked_noalloc, which uses the library's static
+    scratch)."""
     cu_host: torch.Tensor
     cu_dev: torch.Tensor
-    workspace: torch.Tensor
+    workspace: Optional[torch.Tensor]
     num_ckpt: int
     ckpt_interval: int
 
 
-def make_plan(cu_seqlens, H: int, D: int, device, ckpt_interval: int = 0) -> PrefillPlan:
+def make_plan(cu_seqlens, H: int, D: int, device, ckpt_interval: int = 0,
+              workspace: bool = True) -> PrefillPlan:
     cu_host, p = _host_cu(cu_seqlens)
     if int(kda_check_cu(cu_host)) < 0:
         raise KdaError(KDA_ERR_INVALID_ARG, "cu_seqlens")
-    ws = workspace_size(len(cu_host) - 1, int(cu_host[-1]), H, D)
-    workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+    if workspace:
+        ws = workspace_size(len(cu_host) - 1, int(cu_host[-1]), H, D)
+        workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
+    else:
+        workspace = None
     return PrefillPlan(cu_host, cu_host.to(device), workspace,
                        num_checkpoints(cu_host, ckpt_interval) if ckpt_interval else 0,
                        int(ckpt_interval))
@@ -196,15 +207,18 @@ def _opt_ptr(options: Optional[Options]):
 
 def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, scale=1.0, g_min=LN_HALF,
             ckpt_interval=0, out_final_state=True, plan: Optional[PrefillPlan] = None,
-            o=None, final_state=None, checkpoints=None, options: Optional[Options] = None):
+            o=None, final_state=None, checkpoints=None, options: Optional[Options] = None,
+            noalloc: bool = False):
     """kda_prefill_chunked on packed [T, H, D] tensors (kda_prefill_chunked_ex
     when Options are given: gate layout, and q, k, g, beta raw as the flags
-    say).
+    say; kda_prefill_chunked_noalloc when noalloc is set: no workspace, the
+    library's static scratch instead).
 
     Returns (o, final_state or None, checkpoints or None)."""
     T, H, D = q.shape
     if plan is None:
-        plan = make_plan([0, T] if cu_seqlens is None else cu_seqlens, H, D, q.device, ckpt_interval)
+        plan = make_plan([0, T] if cu_seqlens is None else cu_seqlens, H, D, q.device, ckpt_interval,
+                         workspace=not noalloc)
     N = len(plan.cu_host) - 1
     if int(plan.cu_host[-1]) != T:
         raise ValueError(f"cu_seqlens ends at {int(plan.cu_host[-1])}, but q holds {T} tokens")
@@ -223,7 +237,15 @@ def prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, scale=1.0, g_
     args = (_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(g), _ptr(beta), _ptr(plan.cu_dev),
             plan.cu_host.numpy().ctypes.data_as(_i32p), N, H, D, v.shape[2], float(scale),
             float(g_min), _ptr(initial_state), _ptr(final_state), plan.ckpt_interval,
-            _ptr(checkpoints), _ptr(o), _ptr(plan.workspace), plan.workspace.numel())
+            _ptr(checkpoints), _ptr(o))
+    if noalloc:
+        st = lib().kda_prefill_chunked_noalloc(*args, _opt_ptr(options), _stream(q.device))
+        if st != KDA_OK:
+            raise KdaError(st, "kda_prefill_chunked_noalloc")
+        return o, final_state, checkpoints
+    if plan.workspace is None:
+        raise ValueError("this plan has no workspace (made for the noalloc entry point)")
+    args += (_ptr(plan.workspace), plan.workspace.numel())
     if options is None:
         st = lib().kda_prefill_chunked(*args, _stream(q.device))
     else:

@@ -32,7 +32,8 @@
  *     returns KDA_ERR_UNSUPPORTED.
  *   - All work is enqueued on `stream` (NULL = the default stream) and the
  *     calls are asynchronous. The library allocates nothing and keeps no
- *     global state.
+ *     global state, with one exception: kda_prefill_chunked_noalloc's static
+ *     per-device scratch (see there).
  *   - Arguments are validated before any device work; on an error status no
  *     work has been enqueued. A fault inside a kernel surfaces later, as
  *     KDA_ERR_HIP from a later call or as an error of the caller's sync.
@@ -219,6 +220,31 @@ kda_status kda_prefill_chunked_ex(const void* q, const void* k, const void* v, k
                                   int32_t ckpt_interval, float* checkpoints, void* o,
                                   void* workspace, size_t workspace_bytes,
                                   const kda_options* opt, hipStream_t stream);
+
+/* kda_prefill_chunked_ex for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, results and errors, without the workspace.
+ * The workspace is a static device array of KDA_NOALLOC_SCRATCH_BYTES that
+ * every GPU running this call holds from its first use until the process
+ * ends; the call itself allocates nothing.
+ *   - Calls whose workspace would exceed it (kda_prefill_workspace_size of
+ *     the same shapes > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE
+ *     before any device work.
+ *   - stream must belong to the current device (else KDA_ERR_INVALID_ARG).
+ *   - Every call on one GPU uses the same scratch, and its contents are left
+ *     from the last call (the prefill needs no initialised workspace). Calls
+ *     that overlap on one GPU race: calls from several host threads or on
+ *     several streams of one GPU must be ordered by the caller.
+ * Errors: as kda_prefill_chunked_ex, plus KDA_ERR_HIP when the scratch's
+ * device address cannot be looked up. */
+#define KDA_NOALLOC_SCRATCH_BYTES (256u << 20)
+kda_status kda_prefill_chunked_noalloc(const void* q, const void* k, const void* v, kda_dtype dtype,
+                                       const float* g, const float* beta, const int32_t* cu_seqlens,
+                                       const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t H,
+                                       int32_t Dk, int32_t Dv, float scale, float g_min,
+                                       const float* initial_state, float* final_state,
+                                       int32_t ckpt_interval, float* checkpoints, void* o,
+                                       const kda_options* opt, hipStream_t stream);
 
 /* One recurrent decode step for N independent sequences ([K3-SA] Methods 1)
  * FlashKDA, first bullet: decode runs the state update directly; about 7 D^2

@@ -121,6 +121,34 @@ def test_prefill_argument_errors(L):
     assert _prefill_status(L, N=0, cu_host=ctypes.cast(empty, ctypes.POINTER(ctypes.c_int32))) == E.KDA_OK
 
 
+def test_noalloc_prefill_errors_before_any_device_work(L):
+    """kda_prefill_chunked_noalloc validates like kda_prefill_chunked_ex and
+    refuses shapes whose workspace exceeds its static scratch, all before the
+    scratch is looked up or any work is enqueued (so dummy pointers are safe
+    here). Only failing cases are called."""
+    fake = ctypes.c_void_p(0x1000)
+    small = (ctypes.c_int32 * 3)(*cu(20, 12))
+    big = (ctypes.c_int32 * 2)(*cu(8192))
+    as_p = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_int32))
+
+    def call(**over):
+        a = dict(q=fake, k=fake, v=fake, dtype=kda.KDA_BF16, g=fake, beta=fake, cu=fake, cu_host=as_p(small),
+                 N=2, H=4, Dk=128, Dv=128, scale=1.0, g_min=-0.69, s0=None, fin=None, ckpt=0, ckpts=None,
+                 o=fake, opt=None, stream=None)
+        a.update(over)
+        return L.kda_prefill_chunked_noalloc(*a.values())
+    assert call(Dk=64, Dv=64) == kda.KDA_ERR_UNSUPPORTED
+    assert call(q=None) == kda.KDA_ERR_INVALID_ARG
+    assert call(g_min=0.5) == kda.KDA_ERR_INVALID_ARG
+    assert call(ckpt=24) == kda.KDA_ERR_INVALID_ARG
+    assert call(opt=ctypes.byref(kda.Options(gate=-1))) == kda.KDA_ERR_INVALID_ARG
+    # 8192 tokens x 32 heads need more than the static scratch
+    assert kda.workspace_size(1, 8192, 32, 128) > kda.NOALLOC_SCRATCH_BYTES
+    assert call(cu_host=as_p(big), N=1, H=32) == kda.KDA_ERR_WORKSPACE
+    empty = (ctypes.c_int32 * 1)(0)
+    assert call(N=0, cu_host=as_p(empty)) == kda.KDA_OK
+
+
 def test_decode_argument_errors(L):
     fake = ctypes.c_void_p(0x1000)
     call = lambda **o: L.kda_decode_step(*dict(dict(q=fake, k=fake, v=fake, dtype=0, g=fake, beta=fake,
@@ -181,6 +209,11 @@ def test_segment_limits_match_header():
     for name, value in (("KDA_MAX_SEGMENTS", kda.MAX_SEGMENTS), ("KDA_SEGMENT_SLICE_LIMIT", kda.SEGMENT_SLICE_LIMIT)):
         m = re.search(r"#define\s+%s\s+(\d+)" % name, text)
         assert m and int(m.group(1)) == value, name
+
+
+def test_noalloc_scratch_size_matches_header():
+    m = re.search(r"#define\s+KDA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == kda.NOALLOC_SCRATCH_BYTES
 
 
 def test_prefill_options_argument_errors(L):
