@@ -37,19 +37,30 @@ import sys
 import numpy as np
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-# the kernels of one plain kda_prefill_chunked call on the benchmarked shape
-# (B = 1, H = 32, T = 8192, D = 128, bf16 q/k/v, no front end), with their
-# grids in work-items (the same instantiations also run other shapes in the
-# same program, so a dispatch is selected by kernel and grid)
-PREFILL_KERNELS = (("kda::plan_kernel", 1024),
-                   ("kda::prep_kernel<128, unsigned short, false>", 32 * 256 * 128),
-                   ("kda::chain_kernel<128, unsigned short, false>", 256 * 448))
+def prefill_kernels(heads, blocks, units):
+    """The kernels of one plain kda_prefill_chunked call at D = 128 (bf16 q/k/v,
+    no front end, no segments) with `blocks` 32-token blocks per head and
+    `units` (sequence, head) chain units, with their grids in work-items (the
+    same instantiations also run other shapes in the same program, so a
+    dispatch is selected by kernel and grid)."""
+    groups = (units + 7) // 8                 # 8 units x 8 column slices per group of workgroups
+    return (("kda::plan_kernel", 1024),
+            ("kda::prep_kernel<128, unsigned short, false>", heads * blocks * 128),
+            ("kda::chain_kernel<128, unsigned short>", groups * 8 * 8 * 448))
+
+
+# B = 1, H = 32, T = 131072 (4096 blocks) and T = 8192 (256 blocks)
+PREFILL_LONG = prefill_kernels(32, 4096, 32)
+PREFILL_8K = prefill_kernels(32, 256, 32)
+PREFILL_KERNELS = PREFILL_LONG
 # one kda_decode_step over 256 sequences x 32 heads at D = 128 (one workgroup of
 # 256 threads per head)
 DECODE_KERNELS = (("kda::decode_kernel<128, unsigned short, true, false>", 256 * 32 * 256),)
 WORKLOADS = {
-    "prefill": (PREFILL_KERNELS, "KDA prefill HBM traffic (B=1, H=32, T=8192, D=128, bf16 q/k/v)",
-                "kda_prefill_chunked"),
+    "prefill": (PREFILL_LONG, "KDA prefill HBM traffic (B=1, H=32, T=131072, D=128, checkpoint every 32768, "
+                "bf16 q/k/v)", "kda_prefill_chunked"),
+    "prefill_8k": (PREFILL_8K, "KDA prefill HBM traffic (B=1, H=32, T=8192, D=128, bf16 q/k/v)",
+                   "kda_prefill_chunked"),
     "decode": (DECODE_KERNELS, "KDA decode HBM traffic (256 sequences x 32 heads, D=128, one token, bf16 q/k/v)",
                "kda_decode_step"),
 }
