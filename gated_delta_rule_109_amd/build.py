@@ -55,5 +55,44 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer build of the C ABI
+# (argument validation, sizing, the plan's host arithmetic): kda_api.hip with
+# the host pass instrumented and the device code untouched, linked with the
+# uninstrumented kernel objects of build() into libkda_san.so. Load it with
+# clang's ASan runtime preloaded (SAN_RUNTIME); for CPU tests of the C ABI only.
+SAN_LIB = os.path.join(HERE, "libkda_san.so")
+SAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                  "-Xarch_host", "-fno-sanitize-recover=all", "-g"]
+SAN_RUNTIME = os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib", "clang")
+
+
+def san_runtime() -> str:
+    """clang's shared ASan runtime (the one hipcc's host pass instruments for)."""
+    import glob
+    hits = sorted(glob.glob(os.path.join(SAN_RUNTIME, "*", "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    if not hits:
+        raise FileNotFoundError("libclang_rt.asan-x86_64.so not found under " + SAN_RUNTIME)
+    return hits[-1]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    objs = [os.path.join(BUILD_DIR, s.replace(".hip", ".o")) for s in SOURCES if s != "kda_api.hip"]
+    for o in objs:
+        if not os.path.exists(o):
+            build(verbose)
+            break
+    san_obj = os.path.join(BUILD_DIR, "kda_api_san.o")
+    _run([HIPCC, *CFLAGS, *SAN_HOST_FLAGS, "-c", os.path.join(CSRC, "kda_api.hip"), "-o", san_obj], verbose)
+    clangxx = os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "bin", "clang++")
+    link = [clangxx, "-shared", "-shared-libsan", "-fsanitize=address,undefined", "-o", SAN_LIB + ".tmp",
+            san_obj, *objs, "-L" + os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "lib"), "-lamdhip64"]
+    _run(link, verbose)
+    os.replace(SAN_LIB + ".tmp", SAN_LIB)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -6,12 +6,24 @@
 
 #include <float.h>
 #include <limits.h>
+#include <string.h>
 
 #include <initializer_list>
 
 namespace {
 
 bool supported_dims(int32_t Dk, int32_t Dv) { return Dk == Dv && (Dk == 16 || Dk == 128); }
+
+// An enum argument as the int a C caller passed. A C enum is an int, but in
+// C++ a value outside the enumerators' range may not be read as the enum type,
+// so the argument's bytes are read instead (by reference: no enum-typed load).
+template <typename E>
+int enum_code(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+  int c;
+  memcpy(&c, &e, sizeof c);
+  return c;
+}
 
 // Validates cu_seqlens_host; on success returns total tokens and prefill
 // blocks (kda::kBlockTokens tokens each).
@@ -53,6 +65,13 @@ int32_t gate_of(const kda_options* opt) { return opt ? opt->gate : KDA_GATE_CHAN
 // any finite floor at or below 0 is usable.
 bool decode_floor_ok(float g_min) { return g_min >= -FLT_MAX && g_min <= 0.f; }
 
+kda_status prefill_impl(const void* q, const void* k, const void* v, int dtype, const float* g,
+                        const float* beta, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                        int32_t num_seqs, int32_t H, int32_t Dk, int32_t Dv, float scale, float g_min,
+                        const float* initial_state, float* final_state, int32_t ckpt_interval,
+                        float* checkpoints, void* o, void* workspace, size_t workspace_bytes,
+                        bool use_scratch, const kda_options* opt, hipStream_t stream);
+
 bool aligned16(std::initializer_list<const void*> ps) {
   for (const void* p : ps)
     if ((uintptr_t)p & 15) return false;
@@ -64,7 +83,7 @@ bool aligned16(std::initializer_list<const void*> ps) {
 extern "C" {
 
 const char* kda_status_string(kda_status status) {
-  switch (status) {
+  switch (enum_code(status)) {
     case KDA_OK: return "KDA_OK";
     case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument";
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: unsupported head size or dtype";
@@ -101,9 +120,9 @@ kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_
                                const float* initial_state, float* final_state,
                                int32_t ckpt_interval, float* checkpoints, void* o,
                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return kda_prefill_chunked_ex(q, k, v, dtype, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H,
-                                Dk, Dv, scale, g_min, initial_state, final_state, ckpt_interval,
-                                checkpoints, o, workspace, workspace_bytes, nullptr, stream);
+  return prefill_impl(q, k, v, enum_code(dtype), g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, Dk, Dv,
+                      scale, g_min, initial_state, final_state, ckpt_interval, checkpoints, o, workspace,
+                      workspace_bytes, false, nullptr, stream);
 }
 
 }  // extern "C"
@@ -113,7 +132,7 @@ namespace {
 // The prefill behind both workspace conventions: the caller's workspace, or
 // (use_scratch) the library's static per-device scratch, looked up only after
 // every argument and the size have been checked.
-kda_status prefill_impl(const void* q, const void* k, const void* v, kda_dtype dtype, const float* g,
+kda_status prefill_impl(const void* q, const void* k, const void* v, int dtype, const float* g,
                         const float* beta, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
                         int32_t num_seqs, int32_t H, int32_t Dk, int32_t Dv, float scale, float g_min,
                         const float* initial_state, float* final_state, int32_t ckpt_interval,
@@ -195,7 +214,7 @@ kda_status kda_prefill_chunked_ex(const void* q, const void* k, const void* v, k
                                   int32_t ckpt_interval, float* checkpoints, void* o,
                                   void* workspace, size_t workspace_bytes,
                                   const kda_options* opt, hipStream_t stream) {
-  return prefill_impl(q, k, v, dtype, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, Dk, Dv, scale,
+  return prefill_impl(q, k, v, enum_code(dtype), g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, Dk, Dv, scale,
                       g_min, initial_state, final_state, ckpt_interval, checkpoints, o, workspace,
                       workspace_bytes, false, opt, stream);
 }
@@ -207,7 +226,7 @@ kda_status kda_prefill_chunked_noalloc(const void* q, const void* k, const void*
                                        const float* initial_state, float* final_state,
                                        int32_t ckpt_interval, float* checkpoints, void* o,
                                        const kda_options* opt, hipStream_t stream) {
-  return prefill_impl(q, k, v, dtype, g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, Dk, Dv, scale,
+  return prefill_impl(q, k, v, enum_code(dtype), g, beta, cu_seqlens, cu_seqlens_host, num_seqs, H, Dk, Dv, scale,
                       g_min, initial_state, final_state, ckpt_interval, checkpoints, o, nullptr, 0, true,
                       opt, stream);
 }
@@ -216,7 +235,8 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
                            const float* g, const float* beta, float* state, void* o, int32_t N,
                            int32_t H, int32_t Dk, int32_t Dv, float scale, float g_min,
                            hipStream_t stream) {
-  if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
+  const int dt = enum_code(dtype);
+  if (dt != KDA_BF16 && dt != KDA_F32) return KDA_ERR_UNSUPPORTED;
   if (!supported_dims(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
   if (N < 0 || H <= 0 || (int64_t)N * H > INT32_MAX) return KDA_ERR_INVALID_ARG;
   if (!decode_floor_ok(g_min)) return KDA_ERR_INVALID_ARG;
@@ -228,7 +248,7 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, kda_dtyp
   a.N = N; a.H = H; a.D = Dk;
   a.T = 1; a.accept = nullptr;
   a.scale = scale; a.g_min = g_min;
-  a.bf16 = dtype == KDA_BF16;
+  a.bf16 = dt == KDA_BF16;
   a.stream = stream;
   return from_hip(kda::launch_decode(a));
 }
@@ -238,7 +258,8 @@ kda_status kda_decode_tokens(const void* q, const void* k, const void* v, kda_dt
                              const int32_t* accept, void* o, int32_t N, int32_t T, int32_t H,
                              int32_t Dk, int32_t Dv, float scale, float g_min,
                              const kda_options* opt, hipStream_t stream) {
-  if (dtype != KDA_BF16 && dtype != KDA_F32) return KDA_ERR_UNSUPPORTED;
+  const int dt = enum_code(dtype);
+  if (dt != KDA_BF16 && dt != KDA_F32) return KDA_ERR_UNSUPPORTED;
   if (!options_ok(opt)) return KDA_ERR_INVALID_ARG;
   const bool need_g = gate_of(opt) != KDA_GATE_NONE;
   if (!supported_dims(Dk, Dv)) return KDA_ERR_UNSUPPORTED;
@@ -256,7 +277,7 @@ kda_status kda_decode_tokens(const void* q, const void* k, const void* v, kda_dt
   a.scale = scale; a.g_min = g_min;
   a.fe_flags = opt ? opt->flags : 0u; a.fe_eps = opt ? opt->norm_eps : 0.f;
   a.gate = gate_of(opt);
-  a.bf16 = dtype == KDA_BF16;
+  a.bf16 = dt == KDA_BF16;
   a.stream = stream;
   return from_hip(kda::launch_decode(a));
 }

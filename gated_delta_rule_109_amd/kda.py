@@ -15,7 +15,8 @@ from typing import Optional
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkda.so")
+# the built library (KDA_LIB names another build of it, e.g. the host-sanitizer one)
+LIB_PATH = os.environ.get("KDA_LIB") or os.path.join(HERE, "libkda.so")
 
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 KDA_BF16, KDA_F32 = 0, 1

@@ -21,11 +21,14 @@ _i64 = ctypes.POINTER(ctypes.c_int64)
 
 
 def lib():
+    """The compiled oracle: oracle/liboracle_kda.so, or the library named by
+    KDA_ORACLE_LIB (the sanitizer build)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        path = os.environ.get("KDA_ORACLE_LIB") or _build.LIB
+        if path == _build.LIB and not os.path.exists(path):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        L = ctypes.CDLL(path)
         L.kda_oracle_prefill.restype = ctypes.c_int
         L.kda_oracle_prefill.argtypes = [_f, _f, _f, _f, _f, _i64, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
