@@ -728,6 +728,68 @@ def test_calls_replay_from_a_captured_graph():
             assert torch.equal(a, b), f"replay with inputs {seed} differs from the eager call"
 
 
+# ------------------------------------------- 32 heads, packed and captured
+def test_prefill_varlen_32_heads_every_head():
+    """32 heads (one chain workgroup per compute unit and more), packed
+    sequences including empty ones, cached states and checkpoints every 256
+    tokens; every head against the oracle."""
+    lengths = [1500, 17, 0, 2200, 700, 33, 1600, 0]
+    H, D = 32, 128
+    print(f"case: varlen H={H} lengths={lengths}", flush=True)
+    inp = make_inputs(sum(lengths), H, D, seed=171, lengths=lengths, initial_state=True)
+    o, fin, ck = run_prefill(inp, H, D, ckpt=256)
+    o_ref, f_ref, ck_ref = oracle(inp, ckpt=256)
+    check_outputs(o, o_ref, inp.cu_seqlens, H)
+    check_states(fin, f_ref, "final")
+    assert ck.shape == ck_ref.shape == (sum(L // 256 for L in lengths), H, D, D)
+    check_states(ck, ck_ref, "checkpoint")
+
+
+def test_32_head_call_with_checkpoints_replays_from_a_captured_graph():
+    """A 32-head prefill of two sequences with checkpoints captured in a graph
+    replays to exactly the eager call's results, on new inputs each time."""
+    T, H, D = 4096, 32, 128
+    print(f"case: graph capture T={T} H={H}", flush=True)
+    plan = kda.make_plan([0, 1000, T], H, D, DEV, ckpt_interval=512)
+    bufs = {n: torch.empty(T, H, D, dtype=torch.bfloat16, device=DEV) for n in ("q", "k", "v")}
+    g = torch.empty(T, H, D, device=DEV)
+    beta = torch.empty(T, H, device=DEV)
+    o = torch.empty(T, H, D, dtype=torch.bfloat16, device=DEV)
+    fin = torch.empty(2, H, D, D, device=DEV)
+    ck = torch.empty(plan.num_ckpt, H, D, D, device=DEV)
+
+    def load(seed):
+        q, k, v, gg, bb, _, _ = make_inputs_device(T, H, D, seed=seed, device=DEV, lengths=[1000, T - 1000])
+        for n, x in (("q", q), ("k", k), ("v", v)):
+            bufs[n].copy_(x)
+        g.copy_(gg)
+        beta.copy_(bb)
+
+    def call():
+        kda.prefill(bufs["q"], bufs["k"], bufs["v"], g, beta, plan=plan, o=o, final_state=fin, checkpoints=ck)
+
+    load(600)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for seed in (601, 602, 603):
+        load(seed)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (o.clone(), fin.clone(), ck.clone())
+        _ = torch.randn(1 << 20, device=DEV).sum()          # unrelated eager work
+        call()
+        torch.cuda.synchronize()
+        for x, y in zip(got, (o, fin, ck)):
+            assert torch.equal(x, y), f"replay with inputs {seed} differs from the eager call"
+
+
 # ------------------------------------------- segment-parallel prefill
 @pytest.mark.parametrize("P", [2, 3, 5, 16])
 @pytest.mark.parametrize("D", [128, 16])
