@@ -60,6 +60,7 @@
 #include "kda_plan.h"
 
 #include <atomic>
+#include <type_traits>
 
 namespace kda {
 
@@ -277,6 +278,23 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
   char* rec = records + ((size_t)h * gridDim.y + c) * R::kBytes;   // head-major: a head's blocks are contiguous
   auto row = [&](int t) __attribute__((always_inline)) { return ((size_t)(tok0 + t) * H + h) * D; };
 
+  // The q pieces phase 2 needs (fragment order: token 16u + mm, channels
+  // ch(p, gq, 0..3) and ch(p, gq, 4..7)), loaded now so that they arrive while
+  // phase 1 runs. Every wave loads them (only the wave forming Q~ uses them:
+  // a load under a wave-dependent branch would be waited for at the branch's
+  // end); rows past the end read row cnt - 1 and are selected away later.
+  using QPiece = typename std::conditional<sizeof(TIn) == 2, bf16x4, f32x4>::type;
+  QPiece qraw[2][R::NP][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int p = 0; p < R::NP; ++p)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int c0 = ch_of(p, gq, 4 * e);
+        qraw[u][p][e] = *(const QPiece*)(q + row(min(16 * u + mm, cnt - 1)) + (c0 < D ? c0 : 0));
+      }
+
   if (tid < kBT) {
     float b = beta[(size_t)(tok0 + min(tid, cnt - 1)) * H + h];
     if (kGeneral && (fe_flags & KDA_FE_BETA_LOGITS)) b = beta_logit(b);
@@ -298,6 +316,43 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
     return gsrc[i];
   };
 
+  // ---- staging: the block's k rows and (per-channel gate) g rows into LDS
+  // with 16-byte loads, so that phase 1's per-channel threads read their 32
+  // values from LDS instead of issuing a small load per element. g goes to
+  // sP, which phase 1 overwrites in place with P (each thread only touches
+  // its own channel). Without per-channel g rows the g loads read a valid
+  // dummy address and the values are not used. Rows past the end read row
+  // cnt - 1 (selected away in phase 1).
+  const bool g_rows = !kGeneral || gate == KDA_GATE_CHANNEL;
+  {
+    constexpr int kGQuads = D / 4, kGPieces = kBT * kGQuads;
+    constexpr int kKVec = 16 / (int)sizeof(TIn), kKQuads = D / kKVec, kKPieces = kBT * kKQuads;
+    static_assert(kGPieces % kThreads == 0 && kKPieces % kThreads == 0, "whole staging rounds");
+    f32x4 gv[kGPieces / kThreads];
+    u32x4 kv[kKPieces / kThreads];
+#pragma unroll
+    for (int i = 0; i < kGPieces / kThreads; ++i) {
+      const int e = tid + i * kThreads, t = e / kGQuads, c4 = (e % kGQuads) * 4;
+      gv[i] = *(const f32x4*)(g_rows ? g + row(min(t, cnt - 1)) + c4 : (const float*)k);
+    }
+#pragma unroll
+    for (int i = 0; i < kKPieces / kThreads; ++i) {
+      const int e = tid + i * kThreads, t = e / kKQuads, c = (e % kKQuads) * kKVec;
+      kv[i] = *(const u32x4*)(k + row(min(t, cnt - 1)) + c);
+    }
+#pragma unroll
+    for (int i = 0; i < kGPieces / kThreads; ++i) {
+      const int e = tid + i * kThreads, t = e / kGQuads, c4 = (e % kGQuads) * 4;
+      *(f32x4*)&sP[t][c4] = gv[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kKPieces / kThreads; ++i) {
+      const int e = tid + i * kThreads, t = e / kKQuads, c = (e % kKQuads) * kKVec;
+      *(u32x4*)&sK[t][c] = kv[i];
+    }
+  }
+  __syncthreads();
+
   // ---- phase 0 (front end only): inverse L2 norms of the 32 k and q rows.
   // kThreads / 32 lanes per token, each summing D / (kThreads / 32) channels
   // of both rows, then a butterfly over those lanes.
@@ -313,15 +368,12 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
 #pragma unroll
       for (int c = 0; c < kChPerLane; c += 4) {
         f32x4 xk, xq;
-        // the raw k rows also go to sK, so phase 1 does not read them again
+        // (k from its LDS copy)
         if constexpr (sizeof(TIn) == 2) {
-          const bf16x4 rawk = *(const bf16x4*)(k + off + c);
-          *(bf16x4*)&sK[t][part * kChPerLane + c] = rawk;
-          xk = from_bf16x4(rawk);
+          xk = from_bf16x4(*(const bf16x4*)&sK[t][part * kChPerLane + c]);
           xq = from_bf16x4(*(const bf16x4*)(q + off + c));
         } else {
-          xk = *(const f32x4*)(k + off + c);
-          *(f32x4*)&sK[t][part * kChPerLane + c] = xk;
+          xk = *(const f32x4*)&sK[t][part * kChPerLane + c];
           xq = *(const f32x4*)(q + off + c);
         }
 #pragma unroll
@@ -344,33 +396,19 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
   auto rk = [&](int t) __attribute__((always_inline)) { return kGeneral ? sRk[t] : 1.f; };
   auto rq = [&](int t) __attribute__((always_inline)) { return kGeneral ? sRq[t] : 1.f; };
 
-  // ---- phase 1: one channel per thread (coalesced rows). Rows past the end
-  // of the sequence give alpha = 1 and k = 0. Every load reads a valid row
-  // (clamped) and the padding is selected afterwards: a load under a
-  // condition becomes a branch that waits for it before the next one.
+  // ---- phase 1: one channel per thread, from the staged rows (g from sP
+  // for the per-channel gate, else one load per token for the head gate and
+  // none without a gate). Rows past the end of the sequence give alpha = 1
+  // and k = 0.
   if (tid < D) {
     const int ch = tid;
     float a[kBT], kf[kBT];
-    // with the front end's norms, phase 0 has already staged the k rows
-    const bool k_staged = kGeneral && (fe_flags & KDA_FE_L2NORM_QK);
-    if (k_staged) {
 #pragma unroll
-      for (int t = 0; t < kBT; ++t) {
-        a[t] = g_at(min(t, cnt - 1), ch);
-        const TIn kraw = sK[t][ch];
-        if constexpr (sizeof(TIn) == 2) kf[t] = bf16_to_f32(kraw);
-        else kf[t] = kraw;
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < kBT; ++t) {
-        const int tc = min(t, cnt - 1);
-        a[t] = g_at(tc, ch);
-        const TIn kraw = k[row(tc) + ch];
-        sK[t][ch] = kraw;
-        if constexpr (sizeof(TIn) == 2) kf[t] = bf16_to_f32(kraw);
-        else kf[t] = kraw;
-      }
+    for (int t = 0; t < kBT; ++t) {
+      a[t] = g_rows ? sP[t][ch] : g_at(min(t, cnt - 1), ch);
+      const TIn kraw = sK[t][ch];
+      if constexpr (sizeof(TIn) == 2) kf[t] = bf16_to_f32(kraw);
+      else kf[t] = kraw;
     }
 #pragma unroll
     for (int t = 0; t < kBT; ++t) {
@@ -416,12 +454,11 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
   // [16us + 4gq .. +3]: the (us = 0, us = 1) pair of a token tile is exactly
   // its L fragment. Every wave forms Km.
   {
-    // (clamped loads, padding selected after the loads: see phase 1)
-    auto piece = [&](const TIn* base, int t, int ch0) __attribute__((always_inline)) {
-      const TIn* ptr = base + row(min(t, cnt - 1)) + (ch0 < D ? ch0 : 0);
+    // q from the pieces loaded at the start (padding selected here)
+    auto qpiece = [&](const QPiece& raw, int t, int ch0) __attribute__((always_inline)) {
       f32x4 x;
-      if constexpr (sizeof(TIn) == 2) x = from_bf16x4(*(const bf16x4*)ptr);
-      else x = *(const f32x4*)ptr;
+      if constexpr (sizeof(TIn) == 2) x = from_bf16x4(raw);
+      else x = raw;
       return t < cnt && ch0 < D ? x : f32x4{0.f, 0.f, 0.f, 0.f};
     };
     // k from the LDS copy (rows past the end hold row cnt - 1: selected away)
@@ -445,37 +482,58 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
       // from the inputs: a token's own term then keeps its relative accuracy
       // when q_t . k_t nearly cancels (with a zero start state it is the whole
       // output of a sequence's first token).
-      bf16x8 X[2][R::NP], Xl[2][R::NP], Km[2][R::NP], Kml[2][R::NP];
+      // The products accumulate one 32-deep k block p at a time, so only
+      // block p's fragments are live: acc[ut][us] for the (token tile,
+      // token tile) pairs with us <= ut (the pair (0, 1) stays zero).
+      f32x4 acc[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
       float qk[2] = {0.f, 0.f};          // partial q_t . k_t over this lane's channels
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int p = 0; p < R::NP; ++p) {
+        bf16x8 X[2], Xl[2], Km[2], Kml[2];
 #pragma unroll
-        for (int p = 0; p < R::NP; ++p) {
+        for (int u = 0; u < 2; ++u) {
           const int t = 16 * u + mm, c0 = ch_of(p, gq, 0), c1 = ch_of(p, gq, 4);
           const f32x4 P0 = decay(t, c0), P1 = decay(t, c1);
           const float rs = which ? rq(t) : rk(t);
-          const f32x4 x0 = (which ? piece(q, t, c0) : kpiece(t, c0)) * rs;
-          const f32x4 x1 = (which ? piece(q, t, c1) : kpiece(t, c1)) * rs;
+          const f32x4 x0 = (which ? qpiece(qraw[u][p][0], t, c0) : kpiece(t, c0)) * rs;
+          const f32x4 x1 = (which ? qpiece(qraw[u][p][1], t, c1) : kpiece(t, c1)) * rs;
           const f32x4 k0 = which ? kpiece(t, c0) * rk(t) : x0, k1 = which ? kpiece(t, c1) * rk(t) : x1;
           f32x4 r0, r1;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            r0[i] = k0[i] / P0[i];
-            r1[i] = k1[i] / P1[i];
+            // k / P with the hardware reciprocal (1 ulp; the bf16 hi/lo
+            // split that follows keeps 2^-17)
+            r0[i] = k0[i] * __builtin_amdgcn_rcpf(P0[i]);
+            r1[i] = k1[i] * __builtin_amdgcn_rcpf(P1[i]);
             qk[u] += x0[i] * k0[i] + x1[i] * k1[i];
           }
           bf16x4 h0, l0, h1, l1;
           split_bf16(r0, h0, l0);
           split_bf16(r1, h1, l1);
-          Km[u][p] = cat(h0, h1);
-          Kml[u][p] = cat(l0, l1);
+          Km[u] = cat(h0, h1);
+          Kml[u] = cat(l0, l1);
           split_bf16(x0 * P0, h0, l0);
           split_bf16(x1 * P1, h1, l1);
-          X[u][p] = cat(h0, h1);
-          Xl[u][p] = cat(l0, l1);
-          if (which == 0) *(bf16x8*)(rec + R::kKpl + (u * R::NP + p) * 1024 + lane * 16) = Xl[u][p];
-          *(bf16x8*)(rec + (which ? R::kQt : R::kKp) + (u * R::NP + p) * 1024 + lane * 16) = X[u][p];
+          X[u] = cat(h0, h1);
+          Xl[u] = cat(l0, l1);
+          if (which == 0) *(bf16x8*)(rec + R::kKpl + (u * R::NP + p) * 1024 + lane * 16) = Xl[u];
+          *(bf16x8*)(rec + (which ? R::kQt : R::kKp) + (u * R::NP + p) * 1024 + lane * 16) = X[u];
         }
+#pragma unroll
+        for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+          for (int us = 0; us <= ut; ++us) {
+            if (which) {
+              acc[ut][us] = mfma32(Km[us], X[ut], acc[ut][us]);
+              acc[ut][us] = mfma32(Km[us], Xl[ut], acc[ut][us]);
+              acc[ut][us] = mfma32(Kml[us], X[ut], acc[ut][us]);
+            } else {
+              acc[ut][us] = mfma32(X[ut], Km[us], acc[ut][us]);
+              acc[ut][us] = mfma32(Xl[ut], Km[us], acc[ut][us]);
+              acc[ut][us] = mfma32(X[ut], Kml[us], acc[ut][us]);
+            }
+          }
+      }
       // q_t . k_t of token 16u + mm: the four lanes mm + 16 gq hold its channels
       // (wave-uniform branch: every lane takes part)
 #pragma unroll
@@ -488,33 +546,18 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
         bf16x4 lfrag[2];
 #pragma unroll
         for (int us = 0; us < 2; ++us) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          if (us <= ut) {
-#pragma unroll
-            for (int p = 0; p < R::NP; ++p) {
-              if (which) {
-                acc = mfma32(Km[us][p], X[ut][p], acc);
-                acc = mfma32(Km[us][p], Xl[ut][p], acc);
-                acc = mfma32(Kml[us][p], X[ut][p], acc);
-              } else {
-                acc = mfma32(X[ut][p], Km[us][p], acc);
-                acc = mfma32(Xl[ut][p], Km[us][p], acc);
-                acc = mfma32(X[ut][p], Kml[us][p], acc);
-              }
-            }
-          }
           if (which == 0) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int r = 16 * ut + 4 * gq + i, s = 16 * us + mm;
-              sA[r][s] = s < r ? sBeta[r] * acc[i] : 0.f;
+              sA[r][s] = s < r ? sBeta[r] * acc[ut][us][i] : 0.f;
             }
           } else {
             f32x4 lv;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int sr = 16 * us + 4 * gq + i, tr = 16 * ut + mm;
-              lv[i] = sr < tr ? acc[i] : (sr == tr ? qk[ut] : 0.f);
+              lv[i] = sr < tr ? acc[ut][us][i] : (sr == tr ? qk[ut] : 0.f);
             }
             lfrag[us] = to_bf16x4(lv);
           }
