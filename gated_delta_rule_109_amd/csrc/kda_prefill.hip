@@ -245,21 +245,25 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
   using R = Rec<D>;
   constexpr int kThreads = prep_threads<D>();
   constexpr int kWaves = kThreads / kWave;
-  // P[r][ch] (fp32, rows padded by 16 bytes) during phases 1-2, then the
-  // blocks of T.
+  // One LDS area, used twice: P[r][ch] (fp32, rows padded by 16 bytes) and
+  // the k rows during phases 1-2; then A and the blocks of T. A is written
+  // only after every wave has finished reading P and k, so the two uses never
+  // overlap, and the smaller footprint lets six workgroups share a compute
+  // unit instead of five.
   constexpr int kPBytes = kBT * (D + 4) * 4;
   constexpr int kKPad = 16 / (int)sizeof(TIn);                   // 16-byte row padding
   constexpr int kKBytes = kBT * (D + kKPad) * (int)sizeof(TIn);
-  constexpr int kTBytes = (kBT * (kBT + 4) + 2 * 16 * 20) * 4;
+  constexpr int kSqBytes = kBT * (kBT + 4) * 4;                   // one padded 32 x 32 fp32 matrix
+  constexpr int kTBytes = 2 * kSqBytes + 2 * 16 * 20 * 4;
   __shared__ __attribute__((aligned(16))) char lds_raw[kPBytes + kKBytes > kTBytes ? kPBytes + kKBytes : kTBytes];
   float(*sP)[D + 4] = (float(*)[D + 4])lds_raw;
   // the block's k rows as loaded (phase 1 reads them once from memory; phase 2
   // takes them from here in fragment order instead of reading memory again)
   TIn(*sK)[D + kKPad] = (TIn(*)[D + kKPad])(lds_raw + kPBytes);
-  float(*sT)[kBT + 4] = (float(*)[kBT + 4])lds_raw;
-  float(*sX)[20] = (float(*)[20])(lds_raw + kBT * (kBT + 4) * 4);                  // (I + A_bb)^{-1}
-  float(*sM)[20] = (float(*)[20])(lds_raw + (kBT * (kBT + 4) + 16 * 20) * 4);      // A_ba T_aa
-  __shared__ __attribute__((aligned(16))) float sA[kBT][kBT + 4];
+  float(*sA)[kBT + 4] = (float(*)[kBT + 4])lds_raw;
+  float(*sT)[kBT + 4] = (float(*)[kBT + 4])(lds_raw + kSqBytes);
+  float(*sX)[20] = (float(*)[20])(lds_raw + 2 * kSqBytes);                         // (I + A_bb)^{-1}
+  float(*sM)[20] = (float(*)[20])(lds_raw + 2 * kSqBytes + 16 * 20 * 4);           // A_ba T_aa
   __shared__ float sBeta[kBT];
   __shared__ float sRk[kGeneral ? kBT : 1], sRq[kGeneral ? kBT : 1];   // inverse row norms of k and q
 
@@ -453,6 +457,7 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
   // transposed (Km as the A operand) so that each lane holds L[16ut + mm]
   // [16us + 4gq .. +3]: the (us = 0, us = 1) pair of a token tile is exactly
   // its L fragment. Every wave forms Km.
+  f32x4 accA[2][2];   // A (before diag(beta)), kept until P and k are no longer read
   {
     // q from the pieces loaded at the start (padding selected here)
     auto qpiece = [&](const QPiece& raw, int t, int ch0) __attribute__((always_inline)) {
@@ -547,11 +552,7 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
 #pragma unroll
         for (int us = 0; us < 2; ++us) {
           if (which == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 16 * ut + 4 * gq + i, s = 16 * us + mm;
-              sA[r][s] = s < r ? sBeta[r] * acc[ut][us][i] : 0.f;
-            }
+            accA[ut][us] = acc[ut][us];
           } else {
             f32x4 lv;
 #pragma unroll
@@ -567,12 +568,24 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
     }
   }
   __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int ut = 0; ut < 2; ++ut)
+#pragma unroll
+      for (int us = 0; us < 2; ++us)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * ut + 4 * gq + i, s = 16 * us + mm;
+          sA[r][s] = s < r ? sBeta[r] * accA[ut][us][i] : 0.f;
+        }
+  }
+  __syncthreads();
 
   // ---- T = (I + A)^{-1} diag(beta) by blocks (a = tokens 0-15, b = 16-31):
   //   T_aa = X_a diag(beta_a),  T_bb = X_b diag(beta_b),
   //   T_ba = -X_b (A_ba T_aa),  X = (I + A_diag-block)^{-1},
   // the diagonal blocks by forward substitution (lane j: column j % 16 of
-  // block j / 16), then two 16 x 16 products. T reuses the P storage.
+  // block j / 16), then two 16 x 16 products.
   if (tid < kBT) {
     const int blk = tid / 16, j = tid % 16, off = 16 * blk;
     float x[16];
@@ -671,46 +684,59 @@ constexpr int kInFlight = 4;           // blocks each loader keeps in flight
 constexpr int kTouchAhead = 4;         // blocks beyond the loads that the L2 touches run
 constexpr int kRing = 2;               // LDS slots
 
-template <int D, typename TIn>
+// NSL: 16-column slices per workgroup. With NSL = 2 one stream of record
+// loads serves both slices (two compute waves per slice, three loaders, one
+// output wave): the record traffic per column halves, for calls whose slices
+// outnumber the compute units.
+template <int D, typename TIn, int NSL = 1>
 struct ChainCfg {
   using R = Rec<D>;
-  static constexpr int kHalves = R::NT >= 2 ? 2 : 1;                // compute waves (row split)
+  static_assert(NSL == 1 || (NSL == 2 && D == 128), "two slices per workgroup at D = 128 only");
+  static constexpr int kHalves = R::NT >= 2 ? 2 : 1;                // compute waves per slice (row split)
   static constexpr int kTilesPerWave = R::NT / kHalves;             // 16-row tiles per compute wave
   static constexpr int kBlocksPerWave = (kTilesPerWave + 1) / 2;    // 32-deep k blocks per compute wave
-  static constexpr int kWaves = kHalves + kLoaders + 1;             // + the output wave
+  static constexpr int kLoadersN = NSL == 1 ? kLoaders : 3;
+  static constexpr int kInFlightN = NSL == 1 ? kInFlight : 3;
+  static constexpr int kCompute = NSL * kHalves;
+  static constexpr int kWaves = kCompute + kLoadersN + 1;           // + the output wave
   static constexpr int kThreads = kWave * kWaves;
-  static constexpr int kVBytes = kBT * 16 * (int)sizeof(TIn);       // V columns of the slice, one block
+  static constexpr int kVBytes = kBT * 16 * NSL * (int)sizeof(TIn);  // V columns of the slices, one block
   static constexpr int kVFrags = kVBytes / 1024;
   static constexpr int kFrags = R::kFrags + kVFrags;                 // 1 KiB wave-loads per block
-  static constexpr int kPerLoader = (kFrags + kLoaders - 1) / kLoaders;
+  static constexpr int kPerLoader = (kFrags + kLoadersN - 1) / kLoadersN;
   static constexpr int kSlot = kFrags * 1024;
-  static constexpr int kXBytes = 2 * kHalves * 2 * kWave * 16 + 2 * R::NP * kWave * 16;   // xbuf, sbuf
-  static constexpr int kDBytes = 2 * 2 * kWave * 16;                 // dbuf
+  // xbuf, and sbuf (NSL = 1: bf16 state for the output wave) or qbuf (NSL = 2:
+  // the compute waves' partial (Q~ S)^T)
+  static constexpr int kXBytes = 2 * NSL * kHalves * 2 * kWave * 16 +
+                                 (NSL == 1 ? 2 * R::NP * kWave * 16 : 2 * NSL * kHalves * 2 * kWave * 16);
+  static constexpr int kDBytes = 2 * NSL * 2 * kWave * 16;           // dbuf
   static_assert(kVBytes % 1024 == 0, "whole V fragments");
   static_assert(kRing == 2, "buffer lifetimes");
   static_assert(kRing * kSlot + kXBytes + kDBytes <= 160 * 1024, "LDS");
-  static_assert(kInFlight * (kPerLoader + 1) < 64, "vmcnt field");   // + one L2 touch per block
+  static_assert(kInFlightN * (kPerLoader + 1) < 64, "vmcnt field");   // + one L2 touch per block
 };
 
 // K~+ S takes both the key and the state as bf16 hi / lo pairs (hi hi + hi lo +
 // lo hi): with slow decay K~+ is close to the bf16 key, the state is long
 // lived and K~+ S nearly cancels V, so a single bf16 term of either operand
 // dominates the error of V - K~+ S.
-template <int D, typename TIn>
-__global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
+template <int D, typename TIn, int NSL>
+__global__ __launch_bounds__((ChainCfg<D, TIn, NSL>::kThreads)) void chain_kernel(
     const TIn* __restrict__ v, const int32_t* __restrict__ cu, int64_t total_tokens, int nck,
     const int32_t* __restrict__ seq_blk_off, const int32_t* __restrict__ seq_ck_off,
     const char* __restrict__ records, const float* initial_state, float* final_state,
     float* __restrict__ ckpts, TIn* __restrict__ o, int N, int H, int ckpt_interval,
     float scale, int total_blocks, float* __restrict__ segs, int P, int pass,
     const int32_t* __restrict__ seq_order) {
-  using Cfg = ChainCfg<D, TIn>;
+  using Cfg = ChainCfg<D, TIn, NSL>;
   using R = Rec<D>;
   constexpr int NCW = Cfg::kHalves;
+  constexpr int kLd = Cfg::kLoadersN, kIF = Cfg::kInFlightN;
   __shared__ __attribute__((aligned(1024))) char ring[kRing * Cfg::kSlot];
-  __shared__ f32x4 xbuf[2][NCW][2][kWave];      // [set][wave][token tile]: partial K~+ S
-  __shared__ bf16x8 sbuf[2][R::NP][kWave];      // [set][k block]: bf16 state, B-operand fragments
-  __shared__ bf16x8 dbuf[2][2][kWave];          // [set][hi, lo]: delta of both token tiles
+  __shared__ f32x4 xbuf[2][NSL][NCW][2][kWave];           // [set][slice][wave][token tile]: partial K~+ S
+  __shared__ bf16x8 sbuf[NSL == 1 ? 2 : 1][R::NP][kWave];  // [set][k block]: bf16 state (NSL = 1)
+  __shared__ f32x4 qbuf[NSL == 2 ? 2 : 1][NSL][NCW][2][kWave];   // [set][slice][wave][u]: partial (Q~ S)^T (NSL = 2)
+  __shared__ bf16x8 dbuf[2][NSL][2][kWave];               // [set][slice][hi, lo]: delta of both token tiles
 
   // Work unit: (sequence, head, segment, mode). Without segments (P = 1) a
   // unit is a whole (sequence, head) run. With P segments of whole blocks,
@@ -719,15 +745,17 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   // pass 1 runs segments 1 .. P-1 in full from the scanned start states.
   //
   // Placement: units are ranked with the longest sequences first (seq_order),
-  // and workgroup b takes rank 8 (b / (8 S)) + b % 8 and slice (b / 8) % S of
-  // the S = D / 16 slices. So the slices of a unit run on one XCD (b mod 8),
-  // sharing the records through its L2, and the longest recurrences start
-  // first. Grid slots past the last unit have nothing to do.
-  constexpr int S = D / 16;
+  // and workgroup b takes rank 8 (b / (8 S)) + b % 8 and slice group
+  // (b / 8) % S of the S = D / (16 NSL) groups of NSL slices. So the slice
+  // groups of a unit run on one XCD (b mod 8), sharing the records through its
+  // L2, and the longest recurrences start first. Grid slots past the last unit
+  // have nothing to do.
+  constexpr int S = D / (16 * NSL);
   const int U = P == 1 ? 1 : (pass == 0 ? 2 * P - 3 : P - 1);
   const int NU = N * H * U;
   const int b = blockIdx.x;
   const int s = (b / 8) % S, rank = 8 * (b / (8 * S)) + b % 8;
+  const int cb = 16 * NSL * s;                                // first column of the workgroup
   if (rank >= NU) return;
   const int n = seq_order[rank / (H * U)];
   const int u = (rank / H) % U, h = rank % H;
@@ -754,7 +782,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   const int len = max(0, min(seq_len - seg_off, kBT * (blk1 - blk0)));
   const int nblk = blk1 - blk0;
   const bool write_o = mode == kUnitFull, v_on = mode != kUnitTransition;
-  if (nblk == 0 && wave >= NCW) return;   // only the start -> end state copy remains
+  if (nblk == 0 && wave >= Cfg::kCompute) return;   // only the start -> end state copy remains
   const char* rec0 = records + ((size_t)h * total_blocks + seq_blk_off[n] + blk0) * R::kBytes;
   // segment states, [N][KDA_MAX_SEGMENTS][H][3][D][D]: start, local, transition
   auto seg_state = [&](int p, int kind) __attribute__((always_inline)) {
@@ -762,47 +790,65 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   };
   auto slot_of = [&](int c) __attribute__((always_inline)) { return ring + (c % kRing) * Cfg::kSlot; };
 
-  if (wave == NCW + kLoaders) {
+  if (wave == Cfg::kCompute + kLd) {
     // ---------------- output wave ----------------
     // O^T = (Q~ S)^T + delta^T L^T: with S^T and delta as the A operands
     // the accumulator holds token 16u + mm, columns 4gq .. 4gq + 3 in each
-    // lane. (Q~ S)^T is formed here from the bf16 state the compute waves
-    // publish, off their MFMA pipes.
-    f32x4 P[2];
-    bf16x8 Lf[2], Qn[2][R::NP], Ln[2];
-    // Q~ and L of block c, read between B(c) and B(c + 1), while its slot is valid
+    // lane. With one slice, (Q~ S)^T is formed here from the bf16 state the
+    // compute waves publish, off their MFMA pipes; with two, the compute waves
+    // form it over their rows and this wave adds the two halves.
+    f32x4 P[NSL][2];
+    bf16x8 Lf[2], Qn[NSL == 1 ? 2 : 1][R::NP], Ln[2];
+    // Q~ (one slice) and L of block c, read between B(c) and B(c + 1), while its slot is valid
     auto preload = [&](int c) __attribute__((always_inline)) {
       const char* slot = slot_of(c);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         Ln[u] = *(const bf16x8*)(slot + R::kL + u * 1024 + lane * 16);
+        if constexpr (NSL == 1) {
 #pragma unroll
-        for (int p = 0; p < R::NP; ++p) Qn[u][p] = *(const bf16x8*)(slot + R::kQt + (u * R::NP + p) * 1024 + lane * 16);
+          for (int p = 0; p < R::NP; ++p) Qn[u][p] = *(const bf16x8*)(slot + R::kQt + (u * R::NP + p) * 1024 + lane * 16);
+        }
       }
     };
     auto fetch = [&](int c) __attribute__((always_inline)) {   // between B(c + 1) and B(c + 2)
-      bf16x8 sf[R::NP];
 #pragma unroll
-      for (int p = 0; p < R::NP; ++p) sf[p] = sbuf[c % 2][p][lane];
+      for (int u = 0; u < 2; ++u) Lf[u] = Ln[u];
+      if constexpr (NSL == 1) {
+        bf16x8 sf[R::NP];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        Lf[u] = Ln[u];
-        P[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int p = 0; p < R::NP; ++p) sf[p] = sbuf[c % 2][p][lane];
 #pragma unroll
-        for (int p = 0; p < R::NP; ++p) P[u] = mfma32(sf[p], Qn[u][p], P[u]);
+        for (int u = 0; u < 2; ++u) {
+          P[0][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int p = 0; p < R::NP; ++p) P[0][u] = mfma32(sf[p], Qn[u][p], P[0][u]);
+        }
+      } else {
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            P[sl][u] = qbuf[c % 2][sl][0][u][lane];
+#pragma unroll
+            for (int w = 1; w < NCW; ++w) P[sl][u] += qbuf[c % 2][sl][w][u][lane];
+          }
       }
     };
     auto emit = [&](int c) __attribute__((always_inline)) {    // between B(c + 2) and B(c + 3)
-      const bf16x8 dh = dbuf[c % 2][0][lane], dl = dbuf[c % 2][1][lane];
       const int cnt = min(kBT, len - kBT * c);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const f32x4 out = scale * mfma32(dl, Lf[u], mfma32(dh, Lf[u], P[u]));
-        const int tt = 16 * u + mm;
-        if (tt < cnt && write_o) {
-          TIn* dst = o + ((size_t)(t_begin + kBT * c + tt) * H + h) * D + 16 * s + 4 * gq;
-          if constexpr (sizeof(TIn) == 2) *(bf16x4*)dst = to_bf16x4(out);
-          else *(f32x4*)dst = out;
+      for (int sl = 0; sl < NSL; ++sl) {
+        const bf16x8 dh = dbuf[c % 2][sl][0][lane], dl = dbuf[c % 2][sl][1][lane];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const f32x4 out = scale * mfma32(dl, Lf[u], mfma32(dh, Lf[u], P[sl][u]));
+          const int tt = 16 * u + mm;
+          if (tt < cnt && write_o) {
+            TIn* dst = o + ((size_t)(t_begin + kBT * c + tt) * H + h) * D + cb + 16 * sl + 4 * gq;
+            if constexpr (sizeof(TIn) == 2) *(bf16x4*)dst = to_bf16x4(out);
+            else *(f32x4*)dst = out;
+          }
         }
       }
     };
@@ -819,10 +865,10 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     return;
   }
 
-  if (wave >= NCW) {
+  if (wave >= Cfg::kCompute) {
     // ---------------- loader waves ----------------
-    const int lw = wave - NCW;
-    u32x4 buf[kInFlight][Cfg::kPerLoader];
+    const int lw = wave - Cfg::kCompute;
+    u32x4 buf[kIF][Cfg::kPerLoader];
     // L2 touches: with each block it loads, every loader also reads one dword
     // of the record kTouchAhead blocks further on. The workgroups of the S
     // slices of a head split the record's 128-byte lines between them: lane
@@ -839,7 +885,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     constexpr int kLines = R::kBytes / 128;
     constexpr int kShare = (kLines + S - 1) / S;
     const int tline = min(s * kShare + min(lw * kWave + lane, kShare - 1), kLines - 1);
-    uint32_t touched[kInFlight];
+    uint32_t touched[kIF];
     uint32_t fold = 0;
     auto touch = [&](uint32_t& dst, int j) __attribute__((always_inline)) {
       dst = *(const uint32_t*)(rec0 + (size_t)j * R::kBytes + tline * 128);
@@ -847,28 +893,28 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     // Every loader issues exactly kPerLoader 16-byte loads per block
     // (fragments past the end re-read a valid address and are not stored), so
     // the loads of one block form one contiguous group in the vmcnt order. The
-    // V fragments hold the slice's 16 columns of the block's token rows; lane
-    // l of V fragment f reads bytes 1024f + 16l .. +15 of the row-major
-    // [token][16] tile, and the loader stores them transposed ([column][token])
+    // V fragments hold the workgroup's 16 NSL columns of the block's token rows;
+    // lane l of V fragment f reads bytes 1024f + 16l .. +15 of the row-major
+    // [token][16 NSL] tile, and the loader stores them transposed ([column][token])
     // so that a compute lane finds its four tokens of one column side by side.
     // Rows past the end of the sequence are loaded from a valid row and written
     // as zeros, after the loads have completed (selecting right after the load
     // would force a wait on it).
-    constexpr int kVRow = 16 * (int)sizeof(TIn);
+    constexpr int kVRow = 16 * NSL * (int)sizeof(TIn);
     constexpr int kVec = 16 / (int)sizeof(TIn);
     auto load_block = [&](u32x4 (&dst)[Cfg::kPerLoader], int j) __attribute__((always_inline)) {
       const char* rec = rec0 + (size_t)j * R::kBytes;
       const int cnt = min(kBT, len - kBT * j);
 #pragma unroll
       for (int i = 0; i < Cfg::kPerLoader; ++i) {
-        const int fr = lw + kLoaders * i;
+        const int fr = lw + kLd * i;
         const char* src;
         if (fr < R::kFrags) {
           src = rec + fr * 1024 + lane * 16;
         } else {
           const int e = min(fr - R::kFrags, Cfg::kVFrags - 1) * 1024 + lane * 16;
           const int tt = min(e / kVRow, cnt - 1), c0 = (e % kVRow) / (int)sizeof(TIn);
-          src = (const char*)(v + ((size_t)(t_begin + kBT * j + tt) * H + h) * D + 16 * s + c0);
+          src = (const char*)(v + ((size_t)(t_begin + kBT * j + tt) * H + h) * D + cb + c0);
         }
         dst[i] = *(const u32x4*)src;
       }
@@ -878,7 +924,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       const int cnt = min(kBT, len - kBT * j);
 #pragma unroll
       for (int i = 0; i < Cfg::kPerLoader; ++i) {
-        const int fr = lw + kLoaders * i;
+        const int fr = lw + kLd * i;
         if (fr < R::kFrags) {
           *(u32x4*)(slot + fr * 1024 + lane * 16) = src[i];
         } else if (fr < Cfg::kFrags) {
@@ -896,45 +942,45 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     };
     // The steady-state loop is branch-free (stores past the last block land in
     // a slot nobody reads any more; loads past it re-read the last block), so
-    // the compiler's vmcnt bookkeeping keeps all kInFlight blocks in flight.
+    // the compiler's vmcnt bookkeeping keeps all kIF blocks in flight.
     const int last = nblk - 1;
-    static_for<0, kInFlight>([&](auto A) __attribute__((always_inline)) {
+    static_for<0, kIF>([&](auto A) __attribute__((always_inline)) {
       load_block(buf[A.value], min(A.value, last));
       touch(touched[A.value], min(A.value + kTouchAhead, last));
     });
     store_block(buf[0], 0);
     fold ^= touched[0];
-    load_block(buf[0], min(kInFlight, last));
-    touch(touched[0], min(kInFlight + kTouchAhead, last));
+    load_block(buf[0], min(kIF, last));
+    touch(touched[0], min(kIF + kTouchAhead, last));
     lds_barrier();
     auto step = [&](auto A, int j) __attribute__((always_inline)) {
       // publish block j + 1 before barrier B(j + 1), then refill its registers
-      constexpr int set = (decltype(A)::value + 1) % kInFlight;
+      constexpr int set = (decltype(A)::value + 1) % kIF;
       const int c = j + 1;
       store_block(buf[set], c);
       fold ^= touched[set];
-      load_block(buf[set], min(c + kInFlight, last));
-      touch(touched[set], min(c + kInFlight + kTouchAhead, last));
+      load_block(buf[set], min(c + kIF, last));
+      touch(touched[set], min(c + kIF + kTouchAhead, last));
       lds_barrier();
     };
     int j0 = 0;
-    for (; j0 + kInFlight <= nblk; j0 += kInFlight)
-      static_for<0, kInFlight>([&](auto A) __attribute__((always_inline)) { step(A, j0 + A.value); });
-    static_for<0, kInFlight>([&](auto A) __attribute__((always_inline)) {
+    for (; j0 + kIF <= nblk; j0 += kIF)
+      static_for<0, kIF>([&](auto A) __attribute__((always_inline)) { step(A, j0 + A.value); });
+    static_for<0, kIF>([&](auto A) __attribute__((always_inline)) {
       if (j0 + A.value < nblk) step(A, j0 + A.value);
     });
     lds_barrier();
     // keeps the touches: the condition holds for no call (scale is never this
     // value in practice, and the store would only land in the ring, after
     // every read of it)
-    static_for<0, kInFlight>([&](auto A) __attribute__((always_inline)) { fold ^= touched[A.value]; });
+    static_for<0, kIF>([&](auto A) __attribute__((always_inline)) { fold ^= touched[A.value]; });
     if (fold == 0x9e3779b9u && scale == -1.2345e-30f) *(uint32_t*)ring = fold;
     return;
   }
 
   // ---------------- compute waves ----------------
-  // Compute wave hf holds rows [hf * D/kHalves, (hf + 1) * D/kHalves) of the
-  // slice. Right after the state update it forms the next block's partial
+  // Compute wave hf of slice sl holds rows [hf * D/kHalves, (hf + 1) *
+  // D/kHalves) of its slice. Right after the state update it forms the next block's partial
   // K~+ S over its rows (kept in registers and published to LDS) and
   // publishes its rows of the state in bf16 (for the output wave). After the
   // next barrier each wave adds its partner's K~+ S partial to its own; with
@@ -943,8 +989,8 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
   // all partials in wave order). Each operand group of the next block is read
   // from LDS right after the products of this block have consumed the
   // registers it replaces.
-  const int hf = wave;
-  const int col = 16 * s + mm;
+  const int hf = wave % NCW, sl = wave / NCW;   // row half, and slice within the workgroup
+  const int col = cb + 16 * sl + mm;
   // start and end states of the unit (NULL start: zero, or the identity for
   // a transition; NULL end: not stored)
   const float* init = nullptr;
@@ -996,7 +1042,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       for (int u = 0; u < 2; ++u) {
         th[u] = *(const bf16x8*)(slot + R::kT + u * 2048 + lane * 32);
         tl[u] = *(const bf16x8*)(slot + R::kT + u * 2048 + lane * 32 + 16);
-        const TIn* vt = (const TIn*)(slot + R::kBytes) + mm * kBT + 16 * u + 4 * gq;   // V^T[mm][..]
+        const TIn* vt = (const TIn*)(slot + R::kBytes) + (16 * sl + mm) * kBT + 16 * u + 4 * gq;   // V^T[col][..]
         if constexpr (sizeof(TIn) == 2) vv[u] = from_bf16x4(*(const bf16x4*)vt);
         else vv[u] = *(const f32x4*)vt;
       }
@@ -1017,6 +1063,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
     f32x4 u_own[2];
     auto partials = [&](int c) __attribute__((always_inline)) {
       f32x4 U[2] = {z, z}, UL[2] = {z, z};
+      f32x4 QS[2] = {z, z};          // (Q~ S)^T over this wave's rows (two slices only)
 #pragma unroll
       for (int qq = 0; qq < PW; ++qq) {
         const bf16x4 zero = {};
@@ -1025,7 +1072,14 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
         split_bf16(acc[2 * qq], h0, l0);
         if (two) split_bf16(acc[2 * qq + 1], h1, l1);
         const bf16x8 Bs = cat(h0, h1), Bl = cat(l0, l1);
-        sbuf[c % 2][hf * PW + qq][lane] = Bs;
+        if constexpr (NSL == 1) sbuf[c % 2][hf * PW + qq][lane] = Bs;
+        else {
+          // (Q~ S)^T over this wave's rows (Q~ of block c is in its slot now)
+          const char* qslot = slot_of(c);
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            QS[u] = mfma32(Bs, *(const bf16x8*)(qslot + R::kQt + (u * R::NP + hf * PW + qq) * 1024 + lane * 16), QS[u]);
+        }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           U[u] = mfma32(kp[u][qq], Bs, U[u]);
@@ -1037,7 +1091,8 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       for (int u = 0; u < 2; ++u) {
         U[u] += UL[u];
         u_own[u] = U[u];
-        if (NCW > 1) xbuf[c % 2][hf][u][lane] = U[u];
+        if (NCW > 1) xbuf[c % 2][sl][hf][u][lane] = U[u];
+        if constexpr (NSL == 2) qbuf[c % 2][sl][hf][u][lane] = QS[u];
       }
     };
     auto store_state = [&](const f32x4* st, int idx) __attribute__((always_inline)) {
@@ -1054,15 +1109,15 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       lds_barrier();
       f32x4 U0 = u_own[0], U1 = u_own[1];
       if constexpr (NCW == 2) {
-        U0 += xbuf[j % 2][hf ^ 1][0][lane];
-        U1 += xbuf[j % 2][hf ^ 1][1][lane];
+        U0 += xbuf[j % 2][sl][hf ^ 1][0][lane];
+        U1 += xbuf[j % 2][sl][hf ^ 1][1][lane];
       } else if constexpr (NCW > 2) {   // every wave sums all partials in the same order
-        U0 = xbuf[j % 2][0][0][lane];
-        U1 = xbuf[j % 2][0][1][lane];
+        U0 = xbuf[j % 2][sl][0][0][lane];
+        U1 = xbuf[j % 2][sl][0][1][lane];
 #pragma unroll
         for (int w = 1; w < NCW; ++w) {
-          U0 += xbuf[j % 2][w][0][lane];
-          U1 += xbuf[j % 2][w][1][lane];
+          U0 += xbuf[j % 2][sl][w][0][lane];
+          U1 += xbuf[j % 2][sl][w][1][lane];
         }
       }
       // the partner's partials are read before the next block's operands, so
@@ -1094,8 +1149,8 @@ __global__ __launch_bounds__((ChainCfg<D, TIn>::kThreads)) void chain_kernel(
       split_bf16(dl[1], dh1, dlo1);
       const bf16x8 dh = cat(dh0, dh1), dlw = cat(dlo0, dlo1);
       if (hf == NCW - 1) {
-        dbuf[j % 2][0][lane] = dh;
-        dbuf[j % 2][1][lane] = dlw;
+        dbuf[j % 2][sl][0][lane] = dh;
+        dbuf[j % 2][sl][1][lane] = dlw;
       }
       const int mid = kBT * j + kChunk;   // checkpoint after the block's first 16 tokens
       if (ckpt_interval > 0 && write_o && mid <= len && (seg_off + mid) % ckpt_interval == 0) {
@@ -1218,15 +1273,21 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  using Cfg = ChainCfg<D, TIn>;
+  using Cfg = ChainCfg<D, TIn, 1>;
   const int64_t slices = (int64_t)a.num_seqs * a.H * (D / 16);   // one workgroup per 16-column slice
   const int64_t nh = (int64_t)a.num_seqs * a.H;
   const int P = a.segments;
   float* segs = P > 1 ? (float*)(ws + L.segs) : nullptr;
-  auto chain = chain_kernel<D, TIn>;
+  // Two slices per workgroup where the slice workgroups outnumber the compute
+  // units: the calls that run the chain in several rounds, whose time is then
+  // set by record traffic per column rather than by one recurrence's length.
+  const bool two = D == 128 && P == 1 && slices > kChipCUs;
+  auto chain = two ? chain_kernel<D, TIn, D == 128 ? 2 : 1> : chain_kernel<D, TIn, 1>;
+  const int threads = two ? ChainCfg<D, TIn, D == 128 ? 2 : 1>::kThreads : Cfg::kThreads;
+  const int groups_per_unit = two ? D / 32 : D / 16;
   auto run_chain = [&](int units, int pass) {
-    const int64_t groups = (nh * units + 7) / 8;     // 8 units x D/16 slices per group of workgroups
-    hipLaunchKernelGGL(chain, dim3((unsigned)(groups * 8 * (D / 16))), dim3(Cfg::kThreads), 0, a.stream,
+    const int64_t groups = (nh * units + 7) / 8;     // 8 units x (slice groups) per group of workgroups
+    hipLaunchKernelGGL(chain, dim3((unsigned)(groups * 8 * groups_per_unit)), dim3(threads), 0, a.stream,
                        (const TIn*)a.v, a.cu_seqlens, (int64_t)a.total_tokens, (int)a.num_checkpoints,
                        seq_blk_off, seq_ck_off, records, a.initial_state,
                        a.final_state, a.checkpoints, (TIn*)a.o, a.num_seqs, a.H, a.ckpt_interval,

@@ -745,6 +745,46 @@ def test_prefill_varlen_32_heads_every_head():
     check_states(ck, ck_ref, "checkpoint")
 
 
+@pytest.mark.parametrize("bf16,ckpt,initial", [(True, 48, True), (False, 48, True), (True, 0, False)])
+def test_two_slice_chain_workgroups(bf16, ckpt, initial):
+    """More 16-column slices than compute units (9 sequences x 4 heads x 8
+    slices = 288 > 256), so each chain workgroup runs two slices from one
+    record stream: ragged, one-token and empty sequences, cached or zero
+    states, checkpoints inside blocks (every 48 tokens), bf16 and fp32
+    storage; every sequence and head against the oracle."""
+    lengths = [100, 0, 37, 250, 16, 1, 64, 129, 80]
+    H, D = 4, 128
+    assert len(lengths) * H * (D // 16) > 256
+    print(f"case: two-slice chain bf16={bf16} ckpt={ckpt} initial={initial}", flush=True)
+    inp = make_inputs(sum(lengths), H, D, seed=223 + ckpt, lengths=lengths, initial_state=True, bf16=bf16)
+    o, fin, ck = run_prefill(inp, H, D, bf16=bf16, ckpt=ckpt, initial=initial)
+    o_ref, f_ref, ck_ref = oracle(inp, ckpt=ckpt, initial=initial)
+    check_outputs(o, o_ref, inp.cu_seqlens, H)
+    check_states(fin, f_ref, "final")
+    if ckpt:
+        assert ck.shape == ck_ref.shape == (sum(L // ckpt for L in lengths), H, D, D)
+        check_states(ck, ck_ref, "checkpoint")
+
+
+def test_two_slice_chain_at_the_threshold_matches_one_slice():
+    """33 sequence-head pairs (264 slices: two per workgroup) against 32 pairs
+    (256 slices: one per workgroup) on the same first 32 pairs' data: the
+    shared sequences give identical results either way."""
+    H, D = 1, 128
+    lengths = [96 + 7 * i for i in range(33)]
+    print("case: slice threshold 32 vs 33 sequences", flush=True)
+    inp = make_inputs(sum(lengths), H, D, seed=229, lengths=lengths, initial_state=True)
+    o33, f33, _ = run_prefill(inp, H, D)
+    cut = int(inp.cu_seqlens[32])
+    sub = Inputs(inp.q[:cut], inp.k[:cut], inp.v[:cut], inp.g[:cut], inp.beta[:cut], inp.cu_seqlens[:33],
+                 inp.initial_state[:32])
+    o32, f32, _ = run_prefill(sub, H, D)
+    o_ref, f_ref, _ = oracle(inp)
+    check_outputs(o33, o_ref, inp.cu_seqlens, H)
+    check_states(f33, f_ref, "final")
+    assert rel_err(f33[:32], f32) <= 1e-6 and rel_err(o33[:cut], o32) <= 1e-2
+
+
 def test_32_head_call_with_checkpoints_replays_from_a_captured_graph():
     """A 32-head prefill of two sequences with checkpoints captured in a graph
     replays to exactly the eager call's results, on new inputs each time."""
