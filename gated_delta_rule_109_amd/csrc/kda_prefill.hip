@@ -704,7 +704,12 @@ struct ChainCfg {
   static constexpr int kVFrags = kVBytes / 1024;
   static constexpr int kFrags = R::kFrags + kVFrags;                 // 1 KiB wave-loads per block
   static constexpr int kPerLoader = (kFrags + kLoadersN - 1) / kLoadersN;
-  static constexpr int kSlot = kFrags * 1024;
+  // V sits after the record in each slot, row-major [token][16 NSL columns]
+  // with rows padded by 16 bytes: a loader lane stores its 16 loaded bytes
+  // with one write, and the 16 lanes of a compute-lane group read one token
+  // row each without bank conflicts between groups.
+  static constexpr int kVPitch = 16 * NSL * (int)sizeof(TIn) + 16;
+  static constexpr int kSlot = R::kBytes + (kBT * kVPitch + 255) / 256 * 256;
   // xbuf, and sbuf (NSL = 1: bf16 state for the output wave) or qbuf (NSL = 2:
   // the compute waves' partial (Q~ S)^T)
   static constexpr int kXBytes = 2 * NSL * kHalves * 2 * kWave * 16 +
@@ -895,13 +900,12 @@ __global__ __launch_bounds__((ChainCfg<D, TIn, NSL>::kThreads)) void chain_kerne
     // the loads of one block form one contiguous group in the vmcnt order. The
     // V fragments hold the workgroup's 16 NSL columns of the block's token rows;
     // lane l of V fragment f reads bytes 1024f + 16l .. +15 of the row-major
-    // [token][16 NSL] tile, and the loader stores them transposed ([column][token])
-    // so that a compute lane finds its four tokens of one column side by side.
+    // [token][16 NSL] tile and stores them at the same place of the padded
+    // tile in the slot.
     // Rows past the end of the sequence are loaded from a valid row and written
     // as zeros, after the loads have completed (selecting right after the load
     // would force a wait on it).
     constexpr int kVRow = 16 * NSL * (int)sizeof(TIn);
-    constexpr int kVec = 16 / (int)sizeof(TIn);
     auto load_block = [&](u32x4 (&dst)[Cfg::kPerLoader], int j) __attribute__((always_inline)) {
       const char* rec = rec0 + (size_t)j * R::kBytes;
       const int cnt = min(kBT, len - kBT * j);
@@ -931,12 +935,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn, NSL>::kThreads)) void chain_kerne
           const int e = (fr - R::kFrags) * 1024 + lane * 16;
           const int tt = e / kVRow, c0 = (e % kVRow) / (int)sizeof(TIn);
           const u32x4 zero = {0u, 0u, 0u, 0u};
-          const u32x4 x = tt < cnt && v_on ? src[i] : zero;
-          TIn el[kVec];
-          __builtin_memcpy(el, &x, 16);
-          TIn* vt = (TIn*)(slot + R::kBytes);
-#pragma unroll
-          for (int e2 = 0; e2 < kVec; ++e2) vt[(c0 + e2) * kBT + tt] = el[e2];
+          *(u32x4*)(slot + R::kBytes + tt * Cfg::kVPitch + c0 * (int)sizeof(TIn)) = tt < cnt && v_on ? src[i] : zero;
         }
       }
     };
@@ -1042,9 +1041,10 @@ __global__ __launch_bounds__((ChainCfg<D, TIn, NSL>::kThreads)) void chain_kerne
       for (int u = 0; u < 2; ++u) {
         th[u] = *(const bf16x8*)(slot + R::kT + u * 2048 + lane * 32);
         tl[u] = *(const bf16x8*)(slot + R::kT + u * 2048 + lane * 32 + 16);
-        const TIn* vt = (const TIn*)(slot + R::kBytes) + (16 * sl + mm) * kBT + 16 * u + 4 * gq;   // V^T[col][..]
-        if constexpr (sizeof(TIn) == 2) vv[u] = from_bf16x4(*(const bf16x4*)vt);
-        else vv[u] = *(const f32x4*)vt;
+        // V[16u + 4gq + i][16 sl + mm], i = 0..3
+        const char* vrow = slot + R::kBytes + (16 * u + 4 * gq) * Cfg::kVPitch + (16 * sl + mm) * (int)sizeof(TIn);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vv[u][i] = Elem<TIn>::load((const TIn*)(vrow + i * Cfg::kVPitch));
       }
     };
     auto read_khpc = [&](const char* slot) __attribute__((always_inline)) {
