@@ -37,16 +37,23 @@ import sys
 import numpy as np
 
 PKG = os.path.dirname(os.path.abspath(__file__))
+CHIP_CUS = 256                                # MI355X compute units
+
+
 def prefill_kernels(heads, blocks, units):
     """The kernels of one plain kda_prefill_chunked call at D = 128 (bf16 q/k/v,
     no front end, no segments) with `blocks` 32-token blocks per head and
     `units` (sequence, head) chain units, with their grids in work-items (the
     same instantiations also run other shapes in the same program, so a
     dispatch is selected by kernel and grid)."""
-    groups = (units + 7) // 8                 # 8 units x 8 column slices per group of workgroups
+    groups = (units + 7) // 8                 # 8 units x (slice groups) per group of workgroups
+    if units * 8 > CHIP_CUS:                  # more 16-column slices than CUs: two per workgroup
+        chain = ("kda::chain_kernel<128, unsigned short, 2>", groups * 8 * 4 * 512)
+    else:
+        chain = ("kda::chain_kernel<128, unsigned short, 1>", groups * 8 * 8 * 448)
     return (("kda::plan_kernel", 1024),
             ("kda::prep_kernel<128, unsigned short, false>", heads * blocks * 128),
-            ("kda::chain_kernel<128, unsigned short>", groups * 8 * 8 * 448))
+            chain)
 
 
 # B = 1, H = 32, T = 131072 (4096 blocks) and T = 8192 (256 blocks)

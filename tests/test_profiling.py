@@ -36,7 +36,7 @@ def write_counters(d, rows):
 PLAN = "kda::plan_kernel(int const*, int)"
 PREP = "void kda::prep_kernel<128, unsigned short, false>(unsigned short const*)"
 PREP_GEN = "void kda::prep_kernel<128, unsigned short, true>(unsigned short const*)"
-CHAIN = "void kda::chain_kernel<128, unsigned short>(unsigned short const*)"
+CHAIN = "void kda::chain_kernel<128, unsigned short, 1>(unsigned short const*)"
 ABS = "void at::native::vectorized_elementwise_kernel<4, at::native::AbsFunctor<float>>(int)"
 
 
@@ -87,23 +87,24 @@ def test_mfma_busy_uses_one_xcd_of_active_cycles(tmp_path):
                        ("void (anonymous namespace)::mfma_loop<1>(float*, int)", "SQ_INSTS_VALU_MFMA_MOPS_BF16", 0),
                        ("void (anonymous namespace)::mfma_loop<1>(float*, int)", "GRBM_GUI_ACTIVE", 8000)])
     rows = {r[0]: r for r in P.mfma_summary(d)}
-    assert rows["kda::chain_kernel<128, unsigned short>"][3] == pytest.approx(50.0)
-    assert rows["kda::chain_kernel<128, unsigned short>"][4] == pytest.approx(2e6 * 512 / 1e9)
+    assert rows["kda::chain_kernel<128, unsigned short, 1>"][3] == pytest.approx(50.0)
+    assert rows["kda::chain_kernel<128, unsigned short, 1>"][4] == pytest.approx(2e6 * 512 / 1e9)
     assert rows["mfma_loop<1> (reference loop)"][3] == pytest.approx(100.0)
 
 
 def test_prefill_grids_follow_the_shape():
     long = dict(P.WORKLOADS["prefill"][0])
     assert long["kda::prep_kernel<128, unsigned short, false>"] == 32 * 4096 * 128
-    assert long["kda::chain_kernel<128, unsigned short>"] == 256 * 448
+    assert long["kda::chain_kernel<128, unsigned short, 1>"] == 256 * 448
     short = dict(P.WORKLOADS["prefill_8k"][0])
     assert short["kda::prep_kernel<128, unsigned short, false>"] == 32 * 256 * 128
-    # 16 sequences x 32 heads: 512 units, 64 groups of 8 units x 8 slices
-    assert dict(P.prefill_kernels(32, 2756, 512))["kda::chain_kernel<128, unsigned short>"] == 4096 * 448
+    # 16 sequences x 32 heads: 512 units (4096 slices, more than the CUs), 64
+    # groups of 8 units x 4 two-slice workgroups of 512 threads
+    assert dict(P.prefill_kernels(32, 2756, 512))["kda::chain_kernel<128, unsigned short, 2>"] == 2048 * 512
 
 
 def test_kernel_key_keeps_template_arguments():
-    assert P.kernel_key(CHAIN) == "kda::chain_kernel<128, unsigned short>"
+    assert P.kernel_key(CHAIN) == "kda::chain_kernel<128, unsigned short, 1>"
     assert P.kernel_key(PLAN) == "kda::plan_kernel"
 
 
