@@ -411,14 +411,15 @@ def _fe_oracle_prefill(q, k, v, g, beta, cu, s0, flags, ckpt=0):
     return reference.prefill(q2, k2, v, g2, b2, cu_seqlens=cu, initial_state=s0, ckpt_interval=ckpt)
 
 
-@pytest.mark.parametrize("D", [128, 16])
-@pytest.mark.parametrize("bf16", [True, False])
-def test_prefill_front_end_all_flags(D, bf16):
+@pytest.mark.parametrize("D,bf16,H", [(128, True, 3), (128, False, 3), (16, True, 3), (16, False, 3),
+                                       (128, True, 5)])
+def test_prefill_front_end_all_flags(D, bf16, H):
     """Raw q, k (not normalised), gate and write logits, ragged varlen with
-    initial states and checkpoints; against the fp64 front end + oracle."""
+    initial states and checkpoints; against the fp64 front end + oracle. With
+    5 heads at D = 128 there are 320 slices, so the chain takes two per
+    workgroup."""
     lengths = [37, 0, 16, 1, 100, 64, 15, 17]
-    H = 3
-    print(f"case: prefill front end D={D} bf16={bf16}", flush=True)
+    print(f"case: prefill front end D={D} bf16={bf16} H={H}", flush=True)
     raw = make_inputs(sum(lengths), H, D, seed=61 + D, lengths=lengths, initial_state=True, bf16=bf16,
                       raw=True)
     dt = torch.bfloat16 if bf16 else torch.float32
@@ -531,14 +532,14 @@ def _variant_gate(inp, gate):
 
 
 @pytest.mark.parametrize("gate", [kda.GATE_HEAD, kda.GATE_NONE])
-@pytest.mark.parametrize("D", [128, 16])
-def test_prefill_gate_variants(gate, D):
+@pytest.mark.parametrize("D,H", [(128, 3), (16, 3), (128, 5)])
+def test_prefill_gate_variants(gate, D, H):
     """Gated DeltaNet (one decay per token and head) and DeltaNet (no decay):
     ragged varlen with initial states and checkpoints, against the oracle with
-    the variant's gate spread over the key channels."""
+    the variant's gate spread over the key channels (5 heads at D = 128: two
+    slices per chain workgroup)."""
     lengths = [37, 0, 16, 1, 100, 64, 15, 17]
-    H = 3
-    print(f"case: prefill gate {gate} D={D}", flush=True)
+    print(f"case: prefill gate {gate} D={D} H={H}", flush=True)
     inp = make_inputs(sum(lengths), H, D, seed=131 + gate + D, lengths=lengths, initial_state=True)
     gv = _variant_gate(inp, gate)
     o, fin, ck = kda.prefill(to_dev(inp.q, torch.bfloat16), to_dev(inp.k, torch.bfloat16),
