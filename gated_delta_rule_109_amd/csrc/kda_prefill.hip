@@ -114,11 +114,13 @@ constexpr int kChipCUs = 256;
 
 int32_t auto_segments(int32_t num_seqs, int32_t H, int32_t D, int64_t max_blocks) {
   if (!segments_allowed(num_seqs, H, D)) return 1;
-  const int64_t slices = (int64_t)num_seqs * H * (D / 16);
+  // chain workgroups of a pass: one per 16-column slice and unit, or one per
+  // two slices at D = 128 (the launcher takes two when one would not fit)
+  const int64_t groups = (int64_t)num_seqs * H * (D == 128 ? D / 32 : D / 16);
   int32_t best = 1;
   for (int32_t P = 3; P <= KDA_MAX_SEGMENTS; ++P) {
-    const int64_t units = slices * (2 * P - 3 > P - 1 ? 2 * P - 3 : P - 1);
-    if (units <= kChipCUs && 2 * (int64_t)P <= max_blocks) best = P;
+    const int64_t wgs = groups * (2 * P - 3 > P - 1 ? 2 * P - 3 : P - 1);
+    if (wgs <= kChipCUs && 2 * (int64_t)P <= max_blocks) best = P;
   }
   return best;
 }
@@ -1200,47 +1202,107 @@ __global__ __launch_bounds__((ChainCfg<D, TIn, NSL>::kThreads)) void chain_kerne
 // the identity with zero values) and local the run from a zero state. Columns
 // stay independent, so one workgroup takes one 16-column slice of one
 // (sequence, head): it needs its own columns of S_in and local, and all of M.
-// fp32, one output row and 16 / kPerRow column groups per thread.
+// The product runs on fp32 MFMA (16 x 16 x 4, full fp32 operands): wave w
+// takes row tiles w * kTPW .. of the 16-column result. M and local of the next
+// step are loaded into registers while this step's product runs (two LDS
+// buffers for M), so each step waits only for its own arithmetic.
 template <int D>
 __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ segs, int N, int H, int P) {
-  constexpr int kOut = D * 16 / 256;                 // outputs per thread: 8 at D = 128, 1 at D = 16
-  constexpr int kPerRow = 16 / kOut;                 // threads per state row
+  constexpr int kTiles = D / 16;                     // 16-row tiles of the result
+  constexpr int kTPW = (kTiles + 3) / 4;             // row tiles per wave (4 waves)
+  constexpr int kM4 = (D * D / 4 + 255) / 256;       // float4 pieces of M per thread
   const int NH = N * H;
   const int s = blockIdx.x / NH, nh = blockIdx.x % NH;
   const int n = nh / H, h = nh % H;
-  const int tid = threadIdx.x, r = tid / kPerRow, c0 = (tid % kPerRow) * kOut;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int mm = lane % 16, gq = lane / 16;
   auto seg_state = [&](int p, int kind) __attribute__((always_inline)) {
     return segs + ((((size_t)n * KDA_MAX_SEGMENTS + p) * H + h) * 3 + kind) * D * D;
   };
-  // M of the step, staged with coalesced float4 loads (rows padded by 16
-  // bytes against bank conflicts), and S_in(p - 1) for this slice's columns
-  __shared__ __attribute__((aligned(16))) float sM[D][D + 4];
+  // M of a step, staged with coalesced float4 loads (rows padded by 16 bytes
+  // against bank conflicts), and S_in(p - 1) for this slice's columns
+  __shared__ __attribute__((aligned(16))) float sM[2][D][D + 4];
   __shared__ float X[D][16];
-  for (int e = tid; e < D * 16; e += 256) X[e / 16][e % 16] = seg_state(1, 0)[(size_t)(e / 16) * D + 16 * s + e % 16];
-  for (int p = 2; p < P; ++p) {
+  f32x4 mreg[kM4];
+  f32x4 lreg[kTPW];                                  // local, in the accumulator layout
+  auto tile_ok = [&](int t) __attribute__((always_inline)) { return wave * kTPW + t < kTiles; };
+  // M and local of segment p - 1, the operands of S_in(p)
+  auto load_step = [&](int p) __attribute__((always_inline)) {
     const f32x4* M4 = (const f32x4*)seg_state(p - 1, 2);
-    __syncthreads();                                 // X written, sM free
-    for (int e = tid; e < D * D / 4; e += 256) *(f32x4*)&sM[e / (D / 4)][4 * (e % (D / 4))] = M4[e];
-    const float* Lc = seg_state(p - 1, 1) + (size_t)r * D + 16 * s + c0;
-    float y[kOut];
 #pragma unroll
-    for (int c = 0; c < kOut; ++c) y[c] = Lc[c];
-    __syncthreads();
-#pragma unroll 4
-    for (int k4 = 0; k4 < D; k4 += 4) {
-      const f32x4 m4 = *(const f32x4*)&sM[r][k4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int c = 0; c < kOut; ++c) y[c] += m4[kk] * X[k4 + kk][c0 + c];
+    for (int i = 0; i < kM4; ++i) {
+      const int e = tid + 256 * i;
+      if (e < D * D / 4) mreg[i] = M4[e];
     }
-    __syncthreads();                                 // every read of X done
-    float* out = seg_state(p, 0) + (size_t)r * D + 16 * s + c0;
+    const float* Lc = seg_state(p - 1, 1) + 16 * s + mm;
 #pragma unroll
-    for (int c = 0; c < kOut; ++c) {
-      X[r][c0 + c] = y[c];
-      out[c] = y[c];
+    for (int t = 0; t < kTPW; ++t)
+      if (tile_ok(t)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lreg[t][r] = Lc[(size_t)(16 * (wave * kTPW + t) + 4 * gq + r) * D];
+      }
+  };
+  auto stage = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kM4; ++i) {
+      const int e = tid + 256 * i;
+      if (e < D * D / 4) *(f32x4*)&sM[buf][e / (D / 4)][4 * (e % (D / 4))] = mreg[i];
     }
+  };
+  for (int e = tid; e < D * 16; e += 256) X[e / 16][e % 16] = seg_state(1, 0)[(size_t)(e / 16) * D + 16 * s + e % 16];
+  if (P > 2) {
+    load_step(2);
+    stage(0);
+  }
+  __syncthreads();
+  for (int p = 2; p < P; ++p) {
+    // kChains independent accumulation chains per tile (k steps kk mod
+    // kChains), summed pairwise in a fixed order at the end
+    constexpr int kChains = D / 4 < 4 ? D / 4 : 4;      // (D / 4 k steps in all; 8 chains measured slower)
+    f32x4 acc[kTPW][kChains];
+#pragma unroll
+    for (int t = 0; t < kTPW; ++t) {
+      acc[t][0] = lreg[t];
+#pragma unroll
+      for (int q = 1; q < kChains; ++q) acc[t][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (p + 1 < P) load_step(p + 1);                 // in flight during the product
+    const int buf = p & 1;
+    // Y[16 rt + 4 gq + r][mm] += sum_k M[16 rt + i][k] X[k][mm]: lane l gives
+    // A = M[16 rt + mm][4 kk + gq] and B = X[4 kk + gq][mm]
+#pragma unroll
+    for (int k4 = 0; k4 < D / 4; k4 += kChains) {
+#pragma unroll
+      for (int q = 0; q < kChains; ++q) {
+        const int kk = k4 + q;
+        const float bx = X[4 * kk + gq][mm];
+#pragma unroll
+        for (int t = 0; t < kTPW; ++t)
+          if (tile_ok(t))
+            acc[t][q] = __builtin_amdgcn_mfma_f32_16x16x4f32(sM[buf][16 * (wave * kTPW + t) + mm][4 * kk + gq], bx,
+                                                             acc[t][q], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kTPW; ++t)
+#pragma unroll
+      for (int w = 1; w < kChains; w *= 2)
+#pragma unroll
+        for (int q = 0; q < kChains; q += 2 * w) acc[t][q] += acc[t][q + w];
+    __syncthreads();                                 // every read of X (and of this M) done
+    float* out = seg_state(p, 0) + 16 * s + mm;
+#pragma unroll
+    for (int t = 0; t < kTPW; ++t)
+      if (tile_ok(t)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * (wave * kTPW + t) + 4 * gq + r;
+          X[row][mm] = acc[t][0][r];
+          out[(size_t)row * D] = acc[t][0][r];
+        }
+      }
+    if (p + 1 < P) stage((p + 1) & 1);               // that buffer was last read in step p - 1
+    __syncthreads();                                 // X and the next M visible
   }
 }
 
@@ -1278,14 +1340,15 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   const int64_t nh = (int64_t)a.num_seqs * a.H;
   const int P = a.segments;
   float* segs = P > 1 ? (float*)(ws + L.segs) : nullptr;
-  // Two slices per workgroup where the slice workgroups outnumber the compute
-  // units: the calls that run the chain in several rounds, whose time is then
-  // set by record traffic per column rather than by one recurrence's length.
-  const bool two = D == 128 && P == 1 && slices > kChipCUs;
-  auto chain = two ? chain_kernel<D, TIn, D == 128 ? 2 : 1> : chain_kernel<D, TIn, 1>;
-  const int threads = two ? ChainCfg<D, TIn, D == 128 ? 2 : 1>::kThreads : Cfg::kThreads;
-  const int groups_per_unit = two ? D / 32 : D / 16;
   auto run_chain = [&](int units, int pass) {
+    // Two slices per workgroup where one-slice workgroups would outnumber the
+    // compute units: the chain would then run in several rounds, and its time
+    // is set by the record traffic per column rather than by one recurrence's
+    // length.
+    const bool two = D == 128 && slices * units > kChipCUs;
+    auto chain = two ? chain_kernel<D, TIn, D == 128 ? 2 : 1> : chain_kernel<D, TIn, 1>;
+    const int threads = two ? ChainCfg<D, TIn, D == 128 ? 2 : 1>::kThreads : Cfg::kThreads;
+    const int groups_per_unit = two ? D / 32 : D / 16;
     const int64_t groups = (nh * units + 7) / 8;     // 8 units x (slice groups) per group of workgroups
     hipLaunchKernelGGL(chain, dim3((unsigned)(groups * 8 * groups_per_unit)), dim3(threads), 0, a.stream,
                        (const TIn*)a.v, a.cu_seqlens, (int64_t)a.total_tokens, (int)a.num_checkpoints,
