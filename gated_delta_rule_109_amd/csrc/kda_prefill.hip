@@ -34,16 +34,19 @@
 //                   kernel consumes, lane by lane. A second instantiation takes
 //                   the gate layout and the front end at run time.
 //  3. chain_kernel  (one workgroup per sequence, head and 16-column slice of the
-//                   state): the sequential recurrence over blocks. Columns of S
-//                   evolve independently, so each slice runs on its own. The
-//                   fp32 state slice lives in the MFMA accumulators of two
-//                   compute waves (half the rows each); loader waves stream
-//                   records into an LDS ring several blocks ahead and an
-//                   output wave forms and stores the output tiles.
+//                   state, or per two slices when one-slice workgroups would
+//                   outnumber the compute units): the sequential recurrence
+//                   over blocks. Columns of S evolve independently, so each
+//                   slice runs on its own. The fp32 state slice lives in the
+//                   MFMA accumulators of two compute waves (half the rows
+//                   each); loader waves stream records into an LDS ring
+//                   several blocks ahead and an output wave forms and stores
+//                   the output tiles.
 //  4. scan_kernel   (with segments only): when a sequence is split into
 //                   segments that the chain runs side by side, the start state
 //                   of each segment from the segments' transitions and local
-//                   states; the chain then runs once more from those states.
+//                   states (fp32 MFMA); the chain then runs once more from
+//                   those states.
 //
 // Precision: MFMA operands are bf16 with fp32 accumulation. Every product that
 // feeds the state takes its operands as two-term bf16 splits (x = hi + lo,
@@ -651,20 +654,24 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
 }
 
 // ---- 3. the recurrence over blocks ------------------------------------------------------
-// A workgroup owns one 16-column slice of one (sequence, head) state (columns
-// of S evolve independently, so slices never talk to each other).
-//  - kHalves compute waves split the slice's D rows: each holds D / kHalves
+// A workgroup owns one 16-column slice of one (sequence, head) state, or two
+// adjacent slices (NSL = 2; columns of S evolve independently, so slices never
+// talk to each other, and two slices only share the record stream).
+//  - kHalves compute waves per slice split its D rows: each holds D / kHalves
 //    rows of the fp32 state in MFMA accumulator layout. They exchange only
 //    their partial K~+ S through LDS, once per block.
-//  - kLoaders loader waves stream each block's record plus the slice's V
-//    columns from L2/HBM with 16-byte vector loads, keeping kInFlight blocks
-//    in flight in their registers, and publish block j + 1 into a small LDS
-//    ring before barrier B(j + 1). (Global->LDS DMA was measured to move only
-//    about 16 B per clock per CU on gfx950, too slow for this stream.)
-//  - one output wave forms each block's output tiles from the bf16 state and
-//    delta the compute waves leave in LDS ((Q~ S)^T + delta^T L^T), and stores
+//  - loader waves (kLoaders, or 3 with two slices) stream each block's record
+//    plus the workgroup's V columns from L2/HBM with 16-byte vector loads,
+//    keeping kInFlight blocks (3 with two slices) in flight in their
+//    registers, and publish
+//    block j + 1 into a small LDS ring before barrier B(j + 1). (Global->LDS
+//    DMA was measured to move only about 16 B per clock per CU on gfx950, too
+//    slow for this stream.)
+//  - one output wave forms each block's output tiles ((Q~ S)^T + delta^T L^T)
+//    from the bf16 state and delta the compute waves leave in LDS, and stores
 //    them, so the output products sit off the compute waves' dependent chain
-//    and their MFMA pipes.
+//    and their MFMA pipes. With two slices the compute waves form their rows'
+//    share of (Q~ S)^T themselves and the output wave adds the halves.
 // One barrier per block. Barrier B0 ends the prologue; block j's compute step
 // runs between barriers B(j+1) and B(j+2); a final barrier follows the last.
 //
@@ -673,9 +680,10 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
 //    the compute waves read it (as the next block's operands, its P_16 too)
 //    and the output wave reads its Q~ and L into registers; the loaders
 //    overwrite it only after B(c + 1);
-//  - the K~+ S partials and the bf16 state of block c (xbuf[c % 2],
-//    sbuf[c % 2]) are written before B(c + 1) and read between B(c + 1) and
-//    B(c + 2); they are overwritten after B(c + 2);
+//  - the K~+ S partials and the bf16 state (or the (Q~ S)^T partials) of
+//    block c (xbuf[c % 2], sbuf[c % 2] or qbuf[c % 2]) are written before
+//    B(c + 1) and read between B(c + 1) and B(c + 2); they are overwritten
+//    after B(c + 2);
 //  - delta of block c (dbuf[c % 2]) is written before B(c + 2), read between
 //    B(c + 2) and B(c + 3), and overwritten after B(c + 3).
 constexpr int kUnitFull = 0;           // chain unit modes (see chain_kernel)
