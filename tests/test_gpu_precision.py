@@ -227,12 +227,23 @@ def _sweep_case(i):
     )
 
 
-@pytest.mark.parametrize("i", range(20))
-def test_seeded_sweep(i):
-    c = _sweep_case(i)
-    print(f"case: sweep {i} {c}", flush=True)
+def _sweep_case_many_slices(i):
+    """Many sequence-head pairs at D = 128 (usually more 16-column slices than
+    compute units, so the chain runs two slices per workgroup)."""
+    rng = np.random.default_rng(5000 + i)
+    c = _sweep_case(100 + i)
+    N, H = int(rng.integers(8, 25)), int(rng.integers(4, 9))
+    c["lengths"] = [int(x) for x in rng.choice([0, 1, 15, 16, 17, 31, 32, 33, 64, 95, 130, 257], size=N)]
+    if sum(c["lengths"]) == 0:
+        c["lengths"][0] = 45
+    c.update(H=H, D=128, segments=0)
+    return c
+
+
+def _run_sweep_case(seed, c):
+    """One sweep case through kda_prefill_chunked_ex against the oracle."""
     lengths, H, D = c["lengths"], c["H"], c["D"]
-    inp = make_inputs(sum(lengths), H, D, seed=4000 + i, lengths=lengths, initial_state=c["initial"],
+    inp = make_inputs(sum(lengths), H, D, seed=seed, lengths=lengths, initial_state=c["initial"],
                       bf16=c["bf16"], g_scale=c["g_scale"])
     g = inp.g
     if c["g_min"] < LN_HALF:     # gates reaching the lower floor
@@ -255,3 +266,17 @@ def test_seeded_sweep(i):
         assert ck is None and len(ck_ref) == 0 or ck.shape == ck_ref.shape
         if ck is not None:
             check_states(ck.cpu().numpy(), ck_ref, "checkpoint")
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_seeded_sweep(i):
+    c = _sweep_case(i)
+    print(f"case: sweep {i} {c}", flush=True)
+    _run_sweep_case(4000 + i, c)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_seeded_sweep_many_slices(i):
+    c = _sweep_case_many_slices(i)
+    print(f"case: sweep (many slices) {i} N={len(c['lengths'])} {c}", flush=True)
+    _run_sweep_case(4100 + i, c)
