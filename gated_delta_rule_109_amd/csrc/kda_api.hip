@@ -104,13 +104,21 @@ int64_t kda_prefill_num_checkpoints(const int32_t* cu_seqlens_host, int32_t num_
   return total;
 }
 
-size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t Dk,
-                                  int32_t Dv) {
-  if (num_seqs < 0 || total_tokens < 0 || H <= 0 || !supported_dims(Dk, Dv)) return 0;
+size_t kda_prefill_workspace_size_window(int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t Dk,
+                                         int32_t Dv, int64_t window_blocks) {
+  if (num_seqs < 0 || total_tokens < 0 || H <= 0 || !supported_dims(Dk, Dv) || window_blocks <= 0) return 0;
   // sum_n ceil(L_n / 32) <= sum_n (L_n / 32 + 1) for any lengths with this total
   const int64_t max_blocks = total_tokens / kda::kBlockTokens + num_seqs;
   if (max_blocks > INT32_MAX) return 0;
-  return kda::prefill_layout(num_seqs, max_blocks, H, Dk).total;
+  const bool windowed = window_blocks < max_blocks;
+  return kda::prefill_layout(num_seqs, max_blocks, H, Dk, windowed ? window_blocks : max_blocks, windowed).total;
+}
+
+size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t Dk,
+                                  int32_t Dv) {
+  if (H <= 0 || !supported_dims(Dk, Dv)) return 0;
+  const int64_t cap = (int64_t)((size_t)KDA_PREFILL_RECORD_CAP_BYTES / (kda::record_bytes(Dk) * (size_t)H));
+  return kda_prefill_workspace_size_window(num_seqs, total_tokens, H, Dk, Dv, cap > 1 ? cap : 1);
 }
 
 kda_status kda_prefill_chunked(const void* q, const void* k, const void* v, kda_dtype dtype,
@@ -156,43 +164,47 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, int dtype, 
   if (!aligned16({q, k, v, g, beta, cu_seqlens, initial_state, final_state, checkpoints, o}))
     return KDA_ERR_INVALID_ARG;
   if (num_seqs == 0) return KDA_OK;
-  // segments per sequence: the library's choice, off, or forced (where the
-  // workspace holds the segment states)
-  int32_t P = 1;
+  // segments per sequence: the library's choice (0), off (1), or forced
+  // (where the workspace holds the segment states)
   const int32_t req = opt ? opt->segments : 0;
-  if (req >= 2) {
-    if (!kda::segments_allowed(num_seqs, H, Dk)) return KDA_ERR_INVALID_ARG;
-    P = req;
-  } else if (req == 0) {
-    int64_t max_blocks = 0;
-    for (int32_t n = 0; n < num_seqs; ++n) {
-      const int64_t b = (cu_seqlens_host[n + 1] - cu_seqlens_host[n] + kda::kBlockTokens - 1) / kda::kBlockTokens;
-      max_blocks = b > max_blocks ? b : max_blocks;
-    }
-    P = kda::auto_segments(num_seqs, H, Dk, max_blocks);
+  if (req >= 2 && !kda::segments_allowed(num_seqs, H, Dk)) return KDA_ERR_INVALID_ARG;
+  // Record windows: all of the call's records at once if the workspace holds
+  // them, else windows of as many blocks as it holds, evened out.
+  // A window also keeps the prep grid's second dimension (its blocks) within
+  // kMaxWindowBlocks.
+  constexpr int64_t kMaxWindowBlocks = 65535;
+  if (use_scratch) workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+  int64_t window = blocks > 0 ? blocks : 1;
+  if (blocks > kMaxWindowBlocks ||
+      workspace_bytes < kda::prefill_layout(num_seqs, blocks, H, Dk, window, false).total) {
+    const size_t fixed = kda::prefill_layout(num_seqs, blocks, H, Dk, 0, true).total;
+    if (workspace_bytes < fixed) return KDA_ERR_WORKSPACE;
+    window = (int64_t)((workspace_bytes - fixed) / (kda::record_bytes(Dk) * (size_t)H));
+    if (window < 1) return KDA_ERR_WORKSPACE;
+    window = window < kMaxWindowBlocks ? window : kMaxWindowBlocks;
+    const int64_t nwin = (blocks + window - 1) / window;
+    window = (blocks + nwin - 1) / nwin;
   }
-  const kda::PrefillLayout L = kda::prefill_layout(num_seqs, blocks, H, Dk);
   if (use_scratch) {
-    if (L.total > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
     // the scratch of the device the work runs on: the stream's, which must be
     // the current one (the array's address is looked up with it current)
     int cur = -1, dev = -1;
     if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &dev) != hipSuccess) return KDA_ERR_HIP;
     if (dev != cur) return KDA_ERR_INVALID_ARG;
     if (kda::noalloc_scratch(&workspace) != hipSuccess) return KDA_ERR_HIP;
-    workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
   }
-  if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 255)) return KDA_ERR_WORKSPACE;
+  if (!workspace || ((uintptr_t)workspace & 255)) return KDA_ERR_WORKSPACE;
 
   kda::PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
-  a.cu_seqlens = cu_seqlens;
+  a.cu_seqlens = cu_seqlens; a.cu_seqlens_host = cu_seqlens_host;
   a.num_seqs = num_seqs; a.H = H; a.D = Dk;
-  a.total_tokens = tokens; a.total_blocks = blocks; a.num_checkpoints = nck > 0 ? nck : 0;
+  a.total_tokens = tokens; a.total_blocks = blocks; a.window_blocks = window;
+  a.num_checkpoints = nck > 0 ? nck : 0;
   a.scale = scale; a.g_min = g_min;
   a.fe_flags = opt ? opt->flags : 0u; a.fe_eps = opt ? opt->norm_eps : 0.f;
   a.gate = gate_of(opt);
-  a.segments = P;
+  a.segments = req;
   a.initial_state = initial_state; a.final_state = final_state;
   a.ckpt_interval = nck > 0 ? ckpt_interval : 0;
   a.checkpoints = checkpoints;

@@ -57,19 +57,94 @@ __host__ __device__ inline void block_rows(int s0, int s1, int j, int64_t total,
   cnt = r < 1 ? 1 : (r > kBT ? kBT : r);
 }
 
-// Blocks [blk0, blk1) of segment seg of P of a sequence of seq_nblk blocks
-// whose records start at record blk_off, kept inside total_blocks records.
-__host__ __device__ inline void segment_blocks(int seq_nblk, int seg, int P, int blk_off,
-                                               int total_blocks, int& blk0, int& blk1) {
-  const int bps = (seq_nblk + P - 1) / P;
-  int room = total_blocks - blk_off;
-  room = room < 0 ? 0 : room;
-  int b0 = seg * bps < seq_nblk ? seg * bps : seq_nblk;
-  b0 = b0 < room ? b0 : room;
-  int b1 = b0 + bps < seq_nblk ? b0 + bps : seq_nblk;
-  b1 = b1 < room ? b1 : room;
-  blk0 = b0;
-  blk1 = b1;
+// ---- record windows -----------------------------------------------------------
+// The records of blocks [c0, c1) = [w W, min((w + 1) W, total_blocks)) of the
+// global block list exist during window w of nwin = ceil(total_blocks / W)
+// only. A sequence with records [g0, g1) (g0 = off[n], g1 = off[n + 1]) takes
+// part in windows [win_lo, win_hi]; an empty one (g0 = g1) only in the window
+// holding position g0 (the last window if g0 = total_blocks). Both ends are
+// non-decreasing in n and win_hi(n) <= win_lo(n + 1), so the sequences of a
+// window are a contiguous range and all windows together list at most
+// N + nwin - 1 (sequence, window) pairs.
+__host__ __device__ inline void window_range(int w, int W, int total_blocks, int& c0, int& c1) {
+  const int64_t a = (int64_t)w * W, b = a + W;
+  c0 = (int)(a < total_blocks ? a : total_blocks);
+  c1 = (int)(b < total_blocks ? b : total_blocks);
+}
+__host__ __device__ inline int win_lo_at(int64_t g0, int W, int nwin) {
+  const int64_t w = g0 / W;
+  return (int)(w < nwin - 1 ? w : nwin - 1);
+}
+__host__ __device__ inline int win_hi_at(int64_t g0, int64_t g1, int W, int nwin) {
+  if (g1 <= g0) return win_lo_at(g0, W, nwin);
+  const int64_t w = (g1 - 1) / W;
+  return (int)(w < nwin - 1 ? w : nwin - 1);
+}
+__host__ __device__ inline int win_lo(const int32_t* off, int n, int W, int nwin) {
+  return win_lo_at(off[n], W, nwin);
+}
+__host__ __device__ inline int win_hi(const int32_t* off, int n, int W, int nwin) {
+  return win_hi_at(off[n], off[n + 1], W, nwin);
+}
+
+// First sequence of window w and the number of sequences in it.
+__host__ __device__ inline void window_seqs(const int32_t* off, int N, int W, int nwin, int w, int& first,
+                                            int& count) {
+  int lo = 0, hi = N;   // first n with win_hi(n) >= w
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (win_hi(off, mid, W, nwin) >= w) hi = mid; else lo = mid + 1;
+  }
+  first = lo;
+  lo = 0, hi = N;       // first n with win_lo(n) > w
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (win_lo(off, mid, W, nwin) > w) hi = mid; else lo = mid + 1;
+  }
+  count = lo > first ? lo - first : 0;
+}
+
+// Blocks [p0, p1) of a sequence with records [g0, g1) that lie in the window's
+// records [c0, c1), as indices within the sequence (p0 = p1 if none).
+__host__ __device__ inline void window_part(int g0, int g1, int c0, int c1, int& p0, int& p1) {
+  const int a = g0 > c0 ? g0 : c0, b = g1 < c1 ? g1 : c1;
+  p0 = a < b ? a - g0 : 0;
+  p1 = a < b ? b - g0 : 0;
+}
+
+// Blocks [b0, b1) of segment seg of P of np blocks.
+__host__ __device__ inline void part_segment(int np, int seg, int P, int& b0, int& b1) {
+  const int bps = (np + P - 1) / P;
+  b0 = seg * bps < np ? seg * bps : np;
+  b1 = b0 + bps < np ? b0 + bps : np;
+}
+
+// Host walk over the windows in order, from the host copy of cu_seqlens
+// (exact per-sequence block counts, so the offsets need no table): calls
+// visit(w, c0, c1, first, count, longest) for every window, with the window's
+// first sequence, its number of sequences and its longest part in blocks.
+// The sequences it counts per window are those window_seqs finds for offsets
+// computed from the same copy.
+template <typename Visit>
+inline void walk_windows(const int32_t* cu_host, int N, int total_blocks, int W, int nwin, Visit visit) {
+  auto nb = [&](int n) { return (int64_t)seq_blocks(cu_host[n + 1] - cu_host[n]); };
+  int nf = 0;            // first sequence whose last window is not before w
+  int64_t off_nf = 0;    // its first record
+  for (int w = 0; w < nwin; ++w) {
+    int c0, c1;
+    window_range(w, W, total_blocks, c0, c1);
+    while (nf < N && win_hi_at(off_nf, off_nf + nb(nf), W, nwin) < w) off_nf += nb(nf++);
+    int count = 0;
+    int64_t longest = 0, off = off_nf;
+    for (int n = nf; n < N && win_lo_at(off, W, nwin) <= w; ++n) {
+      const int64_t g1 = off + nb(n);
+      const int64_t part = (g1 < c1 ? g1 : c1) - (off > c0 ? off : c0);
+      longest = part > longest ? part : longest;
+      ++count;
+      off = g1;
+    }
+    visit(w, c0, c1, nf, count, (int)longest);
+  }
 }
 
 }  // namespace plan

@@ -25,8 +25,9 @@
 //
 // Kernels, all on the caller's stream:
 //  1. plan_kernel   (1 workgroup): per-sequence block / checkpoint offsets, a
-//                   block -> (first token, valid tokens) table, and the
-//                   sequences ranked longest first for the chain's placement.
+//                   block -> (first token, valid tokens) table, and for each
+//                   record window (below) its sequences ranked longest part
+//                   first for the chain's placement.
 //  2. prep_kernel   (one workgroup per block and head, fully parallel): gates,
 //                   decayed operands, A and L on MFMA, T by forward
 //                   substitution; writes one "record" per (block, head) whose
@@ -47,6 +48,13 @@
 //                   of each segment from the segments' transitions and local
 //                   states (fp32 MFMA); the chain then runs once more from
 //                   those states.
+// Record windows: when the workspace does not hold every record at once, the
+// global block list is cut into windows of consecutive blocks, and prep and
+// chain (and the scan) run window by window, each window's records replacing
+// the last one's. A chain unit is the part of a sequence inside the window; a
+// part that does not start its sequence starts from the fp32 state the
+// previous window carried out, so every block's arithmetic is the same as in
+// one window.
 //
 // Precision: MFMA operands are bf16 with fp32 accumulation. Every product that
 // feeds the state takes its operands as two-term bf16 splits (x = hi + lo,
@@ -128,21 +136,31 @@ int32_t auto_segments(int32_t num_seqs, int32_t H, int32_t D, int64_t max_blocks
   return best;
 }
 
-PrefillLayout prefill_layout(int32_t num_seqs, int64_t total_blocks, int32_t H, int32_t D) {
+PrefillLayout prefill_layout(int32_t num_seqs, int64_t total_blocks, int32_t H, int32_t D,
+                             int64_t window_blocks, bool windowed) {
   PrefillLayout L;
   size_t off = 0;
   L.seq_blk_off = off; off = align256(off + sizeof(int32_t) * (size_t)(num_seqs + 1));
   L.seq_ck_off = off;  off = align256(off + sizeof(int32_t) * (size_t)(num_seqs + 1));
   L.blk_info = off;    off = align256(off + 2 * sizeof(int32_t) * (size_t)total_blocks);
-  L.seq_order = off;   off = align256(off + sizeof(int32_t) * (size_t)num_seqs);
-  L.records = off;
-  L.record_bytes = record_bytes(D);
-  off = align256(off + L.record_bytes * (size_t)total_blocks * (size_t)H);
+  // window tables, sized for the most windows (one block each)
+  L.win_slots = total_blocks > 1 ? total_blocks : 1;
+  L.win_base = off;    off = align256(off + sizeof(int32_t) * (size_t)(L.win_slots + 1));
+  L.order_cap = num_seqs + L.win_slots;
+  L.win_order = off;   off = align256(off + sizeof(int32_t) * (size_t)L.order_cap);
   L.segs = 0;
   if (segments_allowed(num_seqs, H, D)) {
     L.segs = off;
-    off += sizeof(float) * (size_t)num_seqs * KDA_MAX_SEGMENTS * H * 3 * D * D;
+    off = align256(off + sizeof(float) * (size_t)num_seqs * KDA_MAX_SEGMENTS * H * 3 * D * D);
   }
+  L.carry = 0;
+  if (windowed) {
+    L.carry = off;
+    off = align256(off + 2 * sizeof(float) * (size_t)H * D * D);
+  }
+  L.records = off;
+  L.record_bytes = record_bytes(D);
+  off += L.record_bytes * (size_t)window_blocks * (size_t)H;
   L.total = off;
   return L;
 }
@@ -151,12 +169,15 @@ PrefillLayout prefill_layout(int32_t num_seqs, int64_t total_blocks, int32_t H, 
 constexpr int kMaxSortedSeqs = 1024;   // longest-first chain order up to this many sequences
 
 // Per-sequence block and checkpoint offsets (prefix sums saturated at the host
-// copy's totals), the (first row, valid rows) of every block, and the chain's
-// sequence order. Index arithmetic and its clamping: kda_plan.h.
+// copy's totals), the (first row, valid rows) of every block, and for each
+// record window of W blocks (nwin of them) the chain's sequence order:
+// win_order[win_base[w] ..] lists the window's sequences, longest part first.
+// Index arithmetic and its clamping: kda_plan.h.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ cu, int N, int64_t total_tokens,
                                                     int ckpt_interval, int num_checkpoints,
                                                     int32_t* seq_blk_off, int32_t* seq_ck_off,
-                                                    int2* blk_info, int total_blocks, int32_t* seq_order) {
+                                                    int2* blk_info, int total_blocks, int W, int nwin,
+                                                    int32_t* win_base, int32_t* win_order, int order_cap) {
   __shared__ int s_c[1024], s_k[1024];
   __shared__ int carry_c, carry_k;
   const int tid = threadIdx.x;
@@ -192,6 +213,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (tid == 0) {
     seq_blk_off[N] = carry_c;
     seq_ck_off[N] = carry_k;
+    carry_c = 0;
   }
   __syncthreads();
   for (int c = tid; c < total_blocks; c += 1024) {
@@ -201,24 +223,57 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     plan::block_rows(s0, s1, c - seq_blk_off[n], total_tokens, t0, cnt);
     blk_info[c] = make_int2(t0, cnt);
   }
-  // Chain order: sequences by block count, longest first (ties by index), so
-  // that when the chain's workgroups outnumber the compute units the longest
-  // recurrences start first. Ranked by counting over block counts in LDS for
-  // N <= kMaxSortedSeqs; beyond that, the given order.
-  __shared__ int s_nb[kMaxSortedSeqs];
-  const bool sorted = N <= kMaxSortedSeqs;
-  if (sorted) {
-    for (int n = tid; n < N; n += 1024) s_nb[n] = seq_blk_off[n + 1] - seq_blk_off[n];
+  // Windows: sequences per window, and their prefix sums (saturated at the
+  // order table's size, which the pairs never exceed).
+  for (int base = 0; base < nwin; base += 1024) {
+    const int w = base + tid;
+    int first, count = 0;
+    if (w < nwin) plan::window_seqs(seq_blk_off, N, W, nwin, w, first, count);
+    s_c[tid] = count;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+      const int ac = tid >= d ? s_c[tid - d] : 0;
+      __syncthreads();
+      s_c[tid] = plan::sat_add(s_c[tid], ac, order_cap);
+      __syncthreads();
+    }
+    if (w < nwin) win_base[w] = plan::sat_add(carry_c, tid > 0 ? s_c[tid - 1] : 0, order_cap);
+    __syncthreads();
+    if (tid == 1023) carry_c = plan::sat_add(carry_c, s_c[1023], order_cap);
     __syncthreads();
   }
-  for (int n = tid; n < N; n += 1024) {
-    int rank = n;
+  if (tid == 0) win_base[nwin] = carry_c;
+  // Chain order within each window: sequences by blocks in the window,
+  // longest first (ties by index), so that when the chain's workgroups
+  // outnumber the compute units the longest recurrences start first. Ranked
+  // by counting over the offsets in LDS for N <= kMaxSortedSeqs; beyond that,
+  // the given order.
+  __shared__ int s_off[kMaxSortedSeqs + 1];
+  const bool sorted = N <= kMaxSortedSeqs;
+  if (sorted)
+    for (int n = tid; n <= N; n += 1024) s_off[n] = seq_blk_off[n];
+  __syncthreads();
+  const int pairs = carry_c;
+  for (int e = tid; e < pairs; e += 1024) {
+    const int w = plan::owner_of(win_base, nwin, e);
+    int first, count, c0, c1;
+    plan::window_seqs(seq_blk_off, N, W, nwin, w, first, count);
+    plan::window_range(w, W, total_blocks, c0, c1);
+    const int i = e - win_base[w];
+    if (i >= count) continue;
+    const int n = first + i;
+    int rank = i;
     if (sorted) {
-      const int bn = s_nb[n];
+      int p0, p1;
+      plan::window_part(s_off[n], s_off[n + 1], c0, c1, p0, p1);
+      const int len = p1 - p0;
       rank = 0;
-      for (int m = 0; m < N; ++m) rank += s_nb[m] > bn || (s_nb[m] == bn && m < n);
+      for (int m = first; m < first + count; ++m) {
+        plan::window_part(s_off[m], s_off[m + 1], c0, c1, p0, p1);
+        rank += p1 - p0 > len || (p1 - p0 == len && m < n);
+      }
     }
-    seq_order[rank] = n;
+    if (win_base[w] + rank < order_cap) win_order[win_base[w] + rank] = n;
   }
 }
 
@@ -245,7 +300,7 @@ constexpr int prep_threads() { return D >= 128 ? D : 64; }
 template <int D, typename TIn, bool kGeneral>
 __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ g,
-    const float* __restrict__ beta, const int2* __restrict__ blk_info, int H, float g_min,
+    const float* __restrict__ beta, const int2* __restrict__ blk_info, int c0, int H, float g_min,
     uint32_t fe_flags, float fe_eps, int gate, char* __restrict__ records) {
   using R = Rec<D>;
   constexpr int kThreads = prep_threads<D>();
@@ -277,12 +332,13 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
   // neighbouring memory. Blocks run last to first: the chain starts from block
   // 0, and the records written last are the ones still held in the 256 MB
   // memory-side cache (MALL) when it reads them (measured: 357 -> 341 us per
-  // call on the 8192-token, 32-head prefill).
+  // call on the 8192-token, 32-head prefill). The launch covers the record
+  // window of blocks [c0, c0 + gridDim.y) of the global block list.
   const int h = blockIdx.x, c = gridDim.y - 1 - blockIdx.y;
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int mm = lane % 16, gq = lane / 16;
-  const int2 ci = blk_info[c];
+  const int2 ci = blk_info[c0 + c];
   const int tok0 = ci.x, cnt = ci.y;
   char* rec = records + ((size_t)h * gridDim.y + c) * R::kBytes;   // head-major: a head's blocks are contiguous
   auto row = [&](int t) __attribute__((always_inline)) { return ((size_t)(tok0 + t) * H + h) * D; };
@@ -741,8 +797,9 @@ __global__ __launch_bounds__((ChainCfg<D, TIn, NSL>::kThreads)) void chain_kerne
     const int32_t* __restrict__ seq_blk_off, const int32_t* __restrict__ seq_ck_off,
     const char* __restrict__ records, const float* initial_state, float* final_state,
     float* __restrict__ ckpts, TIn* __restrict__ o, int N, int H, int ckpt_interval,
-    float scale, int total_blocks, float* __restrict__ segs, int P, int pass,
-    const int32_t* __restrict__ seq_order) {
+    float scale, float* __restrict__ segs, int P, int pass, int win, int c0, int c1,
+    const int32_t* __restrict__ win_base, const int32_t* __restrict__ win_order, int order_cap,
+    const float* carry_in, float* carry_out) {
   using Cfg = ChainCfg<D, TIn, NSL>;
   using R = Rec<D>;
   constexpr int NCW = Cfg::kHalves;
@@ -759,20 +816,29 @@ __global__ __launch_bounds__((ChainCfg<D, TIn, NSL>::kThreads)) void chain_kerne
   // state (zero start) and its transition (identity start, zero values);
   // pass 1 runs segments 1 .. P-1 in full from the scanned start states.
   //
-  // Placement: units are ranked with the longest sequences first (seq_order),
-  // and workgroup b takes rank 8 (b / (8 S)) + b % 8 and slice group
-  // (b / 8) % S of the S = D / (16 NSL) groups of NSL slices. So the slice
-  // groups of a unit run on one XCD (b mod 8), sharing the records through its
-  // L2, and the longest recurrences start first. Grid slots past the last unit
-  // have nothing to do.
+  // Record window: the launch sees the records of blocks [c0, c1) of the
+  // global block list (record h (c1 - c0) + c - c0 for block c) and runs the
+  // part of every sequence that lies in it. A part that does not start its
+  // sequence starts from carry_in, one that does not end it stores its end
+  // state to carry_out ([H][D][D] each; two buffers used alternately by
+  // consecutive windows, as at most one sequence crosses each window edge).
+  //
+  // Placement: the window's sequences are ranked with the longest parts first
+  // (win_order[win_base[win] ..]), and workgroup b takes rank
+  // 8 (b / (8 S)) + b % 8 and slice group (b / 8) % S of the S = D / (16 NSL)
+  // groups of NSL slices. So the slice groups of a unit run on one XCD
+  // (b mod 8), sharing the records through its L2, and the longest
+  // recurrences start first. Grid slots past the last unit have nothing to do.
   constexpr int S = D / (16 * NSL);
   const int U = P == 1 ? 1 : (pass == 0 ? 2 * P - 3 : P - 1);
-  const int NU = N * H * U;
+  const int base = win_base[win];
+  const int NU = max(0, min(win_base[win + 1], order_cap) - base) * H * U;
   const int b = blockIdx.x;
   const int s = (b / 8) % S, rank = 8 * (b / (8 * S)) + b % 8;
   const int cb = 16 * NSL * s;                                // first column of the workgroup
   if (rank >= NU) return;
-  const int n = seq_order[rank / (H * U)];
+  const int n = win_order[base + rank / (H * U)];
+  if (n < 0 || n >= N) return;
   const int u = (rank / H) % U, h = rank % H;
   const int nh = n * H + h;
   int seg = 0, mode = kUnitFull;
@@ -788,17 +854,25 @@ __global__ __launch_bounds__((ChainCfg<D, TIn, NSL>::kThreads)) void chain_kerne
   }
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int mm = lane % 16, gq = lane / 16;
-  int seq_t0, seq_t1, blk0, blk1;
+  int seq_t0, seq_t1;
   plan::clamp_seq(cu, n, total_tokens, seq_t0, seq_t1);
   const int seq_len = seq_t1 - seq_t0;
-  plan::segment_blocks(plan::seq_blocks(seq_len), seg, P, seq_blk_off[n], total_blocks, blk0, blk1);
+  // the sequence's records [g0, g1), its blocks [p0, p1) in this window, and
+  // the segment's blocks [blk0, blk1) of the sequence
+  const int g0 = seq_blk_off[n], g1 = seq_blk_off[n + 1];
+  int p0, p1, b0, b1;
+  plan::window_part(g0, g1, c0, c1, p0, p1);
+  if (p0 == p1 && g0 != g1) return;   // not in this window (only if the cu_seqlens copies differ)
+  plan::part_segment(p1 - p0, seg, P, b0, b1);
+  const int blk0 = p0 + b0, blk1 = p0 + b1;
+  const bool seq_first = p0 == 0, seq_last = g0 + p1 == g1;   // the part starts / ends the sequence
   const int seg_off = kBT * blk0;                             // tokens of the sequence before it
   const int t_begin = seq_t0 + seg_off;
   const int len = max(0, min(seq_len - seg_off, kBT * (blk1 - blk0)));
   const int nblk = blk1 - blk0;
   const bool write_o = mode == kUnitFull, v_on = mode != kUnitTransition;
   if (nblk == 0 && wave >= Cfg::kCompute) return;   // only the start -> end state copy remains
-  const char* rec0 = records + ((size_t)h * total_blocks + seq_blk_off[n] + blk0) * R::kBytes;
+  const char* rec0 = records + ((size_t)h * (c1 - c0) + (nblk > 0 ? g0 + blk0 - c0 : 0)) * R::kBytes;
   // segment states, [N][KDA_MAX_SEGMENTS][H][3][D][D]: start, local, transition
   auto seg_state = [&](int p, int kind) __attribute__((always_inline)) {
     return segs + ((((size_t)n * KDA_MAX_SEGMENTS + p) * H + h) * 3 + kind) * D * D;
@@ -1005,9 +1079,15 @@ __global__ __launch_bounds__((ChainCfg<D, TIn, NSL>::kThreads)) void chain_kerne
   const float* init = nullptr;
   float* fin = nullptr;
   if (mode == kUnitFull) {
-    init = seg == 0 ? (initial_state ? initial_state + (size_t)nh * D * D : nullptr) : seg_state(seg, 0);
-    if (seg == P - 1) fin = final_state ? final_state + (size_t)nh * D * D : nullptr;
-    else if (pass == 0) fin = seg_state(1, 0);
+    if (seg > 0) init = seg_state(seg, 0);
+    else if (!seq_first) init = carry_in ? carry_in + (size_t)h * D * D : nullptr;
+    else init = initial_state ? initial_state + (size_t)nh * D * D : nullptr;
+    if (seg == P - 1) {
+      if (!seq_last) fin = carry_out ? carry_out + (size_t)h * D * D : nullptr;
+      else fin = final_state ? final_state + (size_t)nh * D * D : nullptr;
+    } else if (pass == 0) {
+      fin = seg_state(1, 0);
+    }
   } else {
     fin = seg_state(seg, mode == kUnitLocal ? 1 : 2);
   }
@@ -1316,62 +1396,84 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ segs, int
 
 template <int D, typename TIn>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
-  const PrefillLayout L = prefill_layout(a.num_seqs, a.total_blocks, a.H, D);
+  const int total_blocks = (int)a.total_blocks;
+  const int W = (int)(a.window_blocks > 0 ? a.window_blocks : 1);
+  const int nwin = total_blocks > 0 ? (total_blocks + W - 1) / W : 1;
+  const PrefillLayout L = prefill_layout(a.num_seqs, a.total_blocks, a.H, D, W, nwin > 1);
   char* ws = (char*)a.workspace;
   int32_t* seq_blk_off = (int32_t*)(ws + L.seq_blk_off);
   int32_t* seq_ck_off = (int32_t*)(ws + L.seq_ck_off);
   int2* blk_info = (int2*)(ws + L.blk_info);
+  int32_t* win_base = (int32_t*)(ws + L.win_base);
+  int32_t* win_order = (int32_t*)(ws + L.win_order);
   char* records = ws + L.records;
+  float* carry = nwin > 1 ? (float*)(ws + L.carry) : nullptr;
+  const int order_cap = (int)L.order_cap;
 
-  int32_t* seq_order = (int32_t*)(ws + L.seq_order);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, a.stream, a.cu_seqlens, a.num_seqs,
                      (int64_t)a.total_tokens, a.ckpt_interval, (int)a.num_checkpoints, seq_blk_off,
-                     seq_ck_off, blk_info, (int)a.total_blocks, seq_order);
+                     seq_ck_off, blk_info, total_blocks, W, nwin, win_base, win_order, order_cap);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.total_blocks > 0) {
-    if (a.fe_flags || a.gate != KDA_GATE_CHANNEL)
-      hipLaunchKernelGGL((prep_kernel<D, TIn, true>), dim3((unsigned)a.H, (unsigned)a.total_blocks),
-                         dim3(prep_threads<D>()), 0, a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g,
-                         a.beta, (const int2*)blk_info, a.H, a.g_min, a.fe_flags, a.fe_eps, (int)a.gate,
-                         records);
-    else
-      hipLaunchKernelGGL((prep_kernel<D, TIn, false>), dim3((unsigned)a.H, (unsigned)a.total_blocks),
-                         dim3(prep_threads<D>()), 0, a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g,
-                         a.beta, (const int2*)blk_info, a.H, a.g_min, 0u, 0.f, (int)KDA_GATE_CHANNEL,
-                         records);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   using Cfg = ChainCfg<D, TIn, 1>;
-  const int64_t slices = (int64_t)a.num_seqs * a.H * (D / 16);   // one workgroup per 16-column slice
-  const int64_t nh = (int64_t)a.num_seqs * a.H;
-  const int P = a.segments;
-  float* segs = P > 1 ? (float*)(ws + L.segs) : nullptr;
-  auto run_chain = [&](int units, int pass) {
-    // Two slices per workgroup where one-slice workgroups would outnumber the
-    // compute units: the chain would then run in several rounds, and its time
-    // is set by the record traffic per column rather than by one recurrence's
-    // length.
-    const bool two = D == 128 && slices * units > kChipCUs;
-    auto chain = two ? chain_kernel<D, TIn, D == 128 ? 2 : 1> : chain_kernel<D, TIn, 1>;
-    const int threads = two ? ChainCfg<D, TIn, D == 128 ? 2 : 1>::kThreads : Cfg::kThreads;
-    const int groups_per_unit = two ? D / 32 : D / 16;
-    const int64_t groups = (nh * units + 7) / 8;     // 8 units x (slice groups) per group of workgroups
-    hipLaunchKernelGGL(chain, dim3((unsigned)(groups * 8 * groups_per_unit)), dim3(threads), 0, a.stream,
-                       (const TIn*)a.v, a.cu_seqlens, (int64_t)a.total_tokens, (int)a.num_checkpoints,
-                       seq_blk_off, seq_ck_off, records, a.initial_state,
-                       a.final_state, a.checkpoints, (TIn*)a.o, a.num_seqs, a.H, a.ckpt_interval,
-                       a.scale, (int)a.total_blocks, segs, P, pass, seq_order);
-    return hipGetLastError();
-  };
-  if (P == 1) return run_chain(1, 0);
-  if ((e = run_chain(2 * P - 3, 0)) != hipSuccess) return e;
-  if (P > 2) {
-    hipLaunchKernelGGL(scan_kernel<D>, dim3((unsigned)slices), dim3(256), 0, a.stream, segs, a.num_seqs, a.H, P);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  return run_chain(P - 1, 1);
+  const bool seg_ok = segments_allowed(a.num_seqs, a.H, D);
+  float* segs = seg_ok ? (float*)(ws + L.segs) : nullptr;
+  plan::walk_windows(a.cu_seqlens_host, a.num_seqs, total_blocks, W, nwin,
+                     [&](int w, int c0, int c1, int, int count, int longest) {
+    if (e != hipSuccess) return;
+    const int nw = c1 - c0;
+    if (nw > 0) {
+      if (a.fe_flags || a.gate != KDA_GATE_CHANNEL)
+        hipLaunchKernelGGL((prep_kernel<D, TIn, true>), dim3((unsigned)a.H, (unsigned)nw),
+                           dim3(prep_threads<D>()), 0, a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g,
+                           a.beta, (const int2*)blk_info, c0, a.H, a.g_min, a.fe_flags, a.fe_eps, (int)a.gate,
+                           records);
+      else
+        hipLaunchKernelGGL((prep_kernel<D, TIn, false>), dim3((unsigned)a.H, (unsigned)nw),
+                           dim3(prep_threads<D>()), 0, a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g,
+                           a.beta, (const int2*)blk_info, c0, a.H, a.g_min, 0u, 0.f, (int)KDA_GATE_CHANNEL,
+                           records);
+      if ((e = hipGetLastError()) != hipSuccess) return;
+    }
+    if (count == 0) return;
+    // segments of this window's parts: forced, off, or the library's choice
+    // for its sequences and longest part
+    const int P = a.segments >= 2 ? a.segments
+                  : (a.segments == 1 || !seg_ok ? 1 : auto_segments(count, a.H, D, longest));
+    const int64_t slices = (int64_t)count * a.H * (D / 16);   // one workgroup per 16-column slice
+    const int64_t nh = (int64_t)count * a.H;
+    const float* carry_in = w > 0 ? carry + (size_t)(w % 2) * a.H * D * D : nullptr;
+    float* carry_out = w + 1 < nwin ? carry + (size_t)((w + 1) % 2) * a.H * D * D : nullptr;
+    auto run_chain = [&](int units, int pass) {
+      // Two slices per workgroup where one-slice workgroups would outnumber the
+      // compute units: the chain would then run in several rounds, and its time
+      // is set by the record traffic per column rather than by one recurrence's
+      // length.
+      const bool two = D == 128 && slices * units > kChipCUs;
+      auto chain = two ? chain_kernel<D, TIn, D == 128 ? 2 : 1> : chain_kernel<D, TIn, 1>;
+      const int threads = two ? ChainCfg<D, TIn, D == 128 ? 2 : 1>::kThreads : Cfg::kThreads;
+      const int groups_per_unit = two ? D / 32 : D / 16;
+      const int64_t groups = (nh * units + 7) / 8;     // 8 units x (slice groups) per group of workgroups
+      hipLaunchKernelGGL(chain, dim3((unsigned)(groups * 8 * groups_per_unit)), dim3(threads), 0, a.stream,
+                         (const TIn*)a.v, a.cu_seqlens, (int64_t)a.total_tokens, (int)a.num_checkpoints,
+                         seq_blk_off, seq_ck_off, records, a.initial_state, a.final_state, a.checkpoints,
+                         (TIn*)a.o, a.num_seqs, a.H, a.ckpt_interval, a.scale, segs, P, pass, w, c0, c1,
+                         win_base, win_order, order_cap, carry_in, carry_out);
+      return hipGetLastError();
+    };
+    if (P == 1) {
+      e = run_chain(1, 0);
+      return;
+    }
+    if ((e = run_chain(2 * P - 3, 0)) != hipSuccess) return;
+    if (P > 2) {
+      hipLaunchKernelGGL(scan_kernel<D>, dim3((unsigned)(a.num_seqs * a.H * (D / 16))), dim3(256), 0, a.stream,
+                         segs, a.num_seqs, a.H, P);
+      if ((e = hipGetLastError()) != hipSuccess) return;
+    }
+    e = run_chain(P - 1, 1);
+  });
+  return e;
 }
 
 // ---- static scratch of kda_prefill_chunked_noalloc ----------------------------------

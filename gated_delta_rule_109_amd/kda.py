@@ -24,7 +24,7 @@ CHUNK = 16
 LN_HALF = math.log(0.5)
 
 EXPORTED = ("kda_status_string", "kda_prefill_num_checkpoints", "kda_prefill_workspace_size",
-            "kda_prefill_chunked", "kda_prefill_chunked_ex", "kda_prefill_chunked_noalloc",
+            "kda_prefill_workspace_size_window", "kda_prefill_chunked", "kda_prefill_chunked_ex", "kda_prefill_chunked_noalloc",
             "kda_decode_step", "kda_decode_tokens")
 DECODE_MAX_TOKENS = 16
 FE_L2NORM_QK, FE_GATE_LOGITS, FE_BETA_LOGITS = 1, 2, 4
@@ -73,6 +73,8 @@ def lib():
         L.kda_prefill_num_checkpoints.argtypes = [_i32p, _i32, _i32]
         L.kda_prefill_workspace_size.restype = ctypes.c_size_t
         L.kda_prefill_workspace_size.argtypes = [_i32, ctypes.c_int64, _i32, _i32, _i32]
+        L.kda_prefill_workspace_size_window.restype = ctypes.c_size_t
+        L.kda_prefill_workspace_size_window.argtypes = [_i32, ctypes.c_int64, _i32, _i32, _i32, ctypes.c_int64]
         L.kda_prefill_chunked.restype = ctypes.c_int
         L.kda_prefill_chunked.argtypes = [_vp, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i32p, _i32,
                                           _i32, _i32, _i32, ctypes.c_float, ctypes.c_float, _vp,
@@ -169,10 +171,16 @@ def kda_check_cu(cu_host) -> int:
     return lib().kda_prefill_num_checkpoints(cu_host.numpy().ctypes.data_as(_i32p), len(cu_host) - 1, 0)
 
 
-def workspace_size(num_seqs: int, total_tokens: int, H: int, D: int) -> int:
+def workspace_size(num_seqs: int, total_tokens: int, H: int, D: int,
+                   window_blocks: Optional[int] = None) -> int:
     """kda_prefill_workspace_size: bytes of device workspace for num_seqs
-    sequences of total_tokens packed tokens (independent of the lengths)."""
-    return int(lib().kda_prefill_workspace_size(int(num_seqs), int(total_tokens), H, D, D))
+    sequences of total_tokens packed tokens (independent of the lengths);
+    with window_blocks, kda_prefill_workspace_size_window: the bytes that run
+    the call with the records of at most that many 32-token blocks at a time."""
+    if window_blocks is None:
+        return int(lib().kda_prefill_workspace_size(int(num_seqs), int(total_tokens), H, D, D))
+    return int(lib().kda_prefill_workspace_size_window(int(num_seqs), int(total_tokens), H, D, D,
+                                                       int(window_blocks)))
 
 
 @dataclass
@@ -188,12 +196,16 @@ class PrefillPlan:
 
 
 def make_plan(cu_seqlens, H: int, D: int, device, ckpt_interval: int = 0,
-              workspace: bool = True) -> PrefillPlan:
+              workspace: bool = True, window_blocks: Optional[int] = None) -> PrefillPlan:
+    """window_blocks: size the workspace for record windows of at most that
+    many blocks (None: the library's default size)."""
     cu_host, p = _host_cu(cu_seqlens)
     if int(kda_check_cu(cu_host)) < 0:
         raise KdaError(KDA_ERR_INVALID_ARG, "cu_seqlens")
     if workspace:
-        ws = workspace_size(len(cu_host) - 1, int(cu_host[-1]), H, D)
+        ws = workspace_size(len(cu_host) - 1, int(cu_host[-1]), H, D, window_blocks)
+        if ws == 0:
+            raise KdaError(KDA_ERR_INVALID_ARG, "kda_prefill_workspace_size")
         workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=device)
     else:
         workspace = None

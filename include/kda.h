@@ -140,18 +140,37 @@ const char* kda_status_string(kda_status status);
 int64_t kda_prefill_num_checkpoints(const int32_t* cu_seqlens_host, int32_t num_seqs,
                                     int32_t ckpt_interval);
 
-/* Bytes of device workspace kda_prefill_chunked needs for num_seqs sequences
- * of total_tokens packed tokens with H heads (0 if the arguments are
- * invalid). The workspace holds per-sequence and per-block tables and the
- * per-block decayed operands of the chunked form: 47 KiB per 32-token block
- * and head at D = 128 (about 1.5 KiB per token and head), sized for the most
- * blocks any split of total_tokens into num_seqs sequences can have,
- * total_tokens / 32 + num_seqs. Where segments may be used
+/* Bytes of device workspace for kda_prefill_chunked on num_seqs sequences of
+ * total_tokens packed tokens with H heads (0 if the arguments are invalid).
+ * The workspace holds per-sequence and per-block tables (16 bytes per
+ * 32-token block) and the per-block decayed operands of the chunked form
+ * ("records": 47 KiB per 32-token block and head at D = 128, about 1.5 KiB per
+ * token and head), sized for the most blocks any split of total_tokens into
+ * num_seqs sequences can have, total_tokens / 32 + num_seqs. The record space
+ * is capped at KDA_PREFILL_RECORD_CAP_BYTES: a call with more records runs in
+ * windows of consecutive blocks, preparing and consuming one window's records
+ * at a time, so the workspace stops growing with T there (the tables still
+ * grow by 16 bytes per block). Where segments may be used
  * (num_seqs * H * (Dv / 16) <= KDA_SEGMENT_SLICE_LIMIT) it also holds three
- * fp32 Dk x Dv states per sequence, head and segment. Its contents are
- * scratch and need no initialisation. */
+ * fp32 Dk x Dv states per sequence, head and segment; with windows, two fp32
+ * Dk x Dv states per head carry the sequence that crosses a window edge. Its
+ * contents are scratch and need no initialisation. */
+#define KDA_PREFILL_RECORD_CAP_BYTES (8ull << 30)
 size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t Dk,
                                   int32_t Dv);
+
+/* Bytes of device workspace that runs the same prefill with records for at
+ * most window_blocks blocks (of every head) at a time (0 if the arguments are
+ * invalid or window_blocks < 1). A window of at least total_tokens / 32 +
+ * num_seqs blocks is one window (no carry states). The prefill accepts any
+ * workspace of at least this size for window_blocks = 1 and chooses its
+ * windows from the bytes it is given: all records at once if they fit, else
+ * windows of as many blocks as fit, evened out over the call. Results do not
+ * depend on the windows (each block's arithmetic is the same), except that
+ * the segment-parallel scan, when used, splits each window's part of a
+ * sequence instead of the whole sequence. */
+size_t kda_prefill_workspace_size_window(int32_t num_seqs, int64_t total_tokens, int32_t H,
+                                         int32_t Dk, int32_t Dv, int64_t window_blocks);
 
 /* Chunked prefill over packed variable-length sequences.
  *
@@ -188,9 +207,11 @@ size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_
  *                  recurrent state is kept only at sparse token intervals).
  *                  Ignored when ckpt_interval == 0.
  *   ckpt_interval  0 (no checkpoints) or a positive multiple of KDA_CHUNK.
- *   workspace      device scratch of at least
- *                  kda_prefill_workspace_size(num_seqs, T, H, Dk, Dv) bytes,
- *                  256-byte aligned.
+ *   workspace      device scratch, 256-byte aligned, of workspace_bytes >=
+ *                  kda_prefill_workspace_size_window(num_seqs, T, H, Dk, Dv, 1)
+ *                  bytes; kda_prefill_workspace_size(num_seqs, T, H, Dk, Dv)
+ *                  bytes run the call in the fewest windows up to the record
+ *                  cap (one window below it).
  * initial_state may alias final_state (the state is read before it is written).
  * Errors: KDA_ERR_INVALID_ARG (null required pointer, negative sizes,
  * malformed cu_seqlens_host, bad ckpt_interval, g_min outside
@@ -227,9 +248,11 @@ kda_status kda_prefill_chunked_ex(const void* q, const void* k, const void* v, k
  * The workspace is a static device array of KDA_NOALLOC_SCRATCH_BYTES that
  * every GPU running this call holds from its first use until the process
  * ends; the call itself allocates nothing.
- *   - Calls whose workspace would exceed it (kda_prefill_workspace_size of
- *     the same shapes > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE
- *     before any device work.
+ *   - The call runs in record windows of as many blocks as the scratch holds
+ *     (see kda_prefill_workspace_size_window), so any length fits; only calls
+ *     whose tables and one block per head exceed it
+ *     (kda_prefill_workspace_size_window(..., 1) > KDA_NOALLOC_SCRATCH_BYTES)
+ *     return KDA_ERR_WORKSPACE, before any device work.
  *   - stream must belong to the current device (else KDA_ERR_INVALID_ARG).
  *   - Every call on one GPU uses the same scratch, and its contents are left
  *     from the last call (the prefill needs no initialised workspace). Calls

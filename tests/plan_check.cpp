@@ -1,12 +1,17 @@
 // Host check of the prefill plan's index arithmetic (csrc/kda_plan.h), run by
 // tests/test_plan.py on the CPU. It evaluates what the plan and chain kernels
-// compute from a device cu_seqlens copy, for seeded host / device pairs, and
-// checks that
+// compute from a device cu_seqlens copy, for seeded host / device pairs and
+// record windows of one block, a few blocks and the whole call, and checks
+// that
 //   - with equal copies the tables are the exact per-sequence blocks, rows
-//     and checkpoint offsets, and
+//     and checkpoint offsets; the windows' parts cover every sequence once,
+//     each sequence starts and ends in exactly one window, the state one
+//     window carries out is the one the next carries in, and the host's
+//     window walk (which sizes the grids) agrees with the plan's tables;
 //   - with copies that differ (shifted, shuffled, negative, past the total,
-//     decreasing) every record, row and checkpoint slot touched stays inside
-//     what the host copy sized.
+//     decreasing) every record, row, checkpoint slot and order-table entry
+//     touched stays inside what the host copy sized, and at most one
+//     sequence crosses each window edge.
 // The plan kernel's scan is a parallel prefix sum with plan::sat_add, which is
 // associative on nonnegative values, so the sequential prefix here is what it
 // computes.
@@ -99,34 +104,141 @@ static long run_case(const std::vector<int32_t>& host, const std::vector<int32_t
     }
     checks += 2;
   }
-  // chain units: records, rows and checkpoint slots of every (sequence, segment)
-  for (int n = 0; n < N; ++n) {
-    int s0, s1;
-    clamp_seq(dev.data(), n, T, s0, s1);
-    const int seq_len = s1 - s0, nb = seq_blocks(seq_len);
-    for (int P = 1; P <= 16; P += (P == 1 ? 2 : 1)) {
-      int covered = 0;
-      for (int seg = 0; seg < P; ++seg) {
-        int b0, b1;
-        segment_blocks(nb, seg, P, blk_off[n], total_blocks, b0, b1);
-        CHECK(0 <= b0 && b0 <= b1 && blk_off[n] + b1 <= total_blocks, "records of seq %d seg %d/%d", n, seg, P);
-        const int seg_off = kBT * b0;
-        const int len_raw = seq_len - seg_off < kBT * (b1 - b0) ? seq_len - seg_off : kBT * (b1 - b0);
-        const int len = len_raw > 0 ? len_raw : 0;
-        if (len > 0) CHECK(s0 + seg_off >= 0 && s0 + seg_off + len <= T, "rows of seq %d seg %d/%d", n, seg, P);
-        // checkpoints after token ends e of this segment (multiples of 16)
-        if (interval > 0)
-          for (int e = 16; e <= len; e += 16)
-            if ((seg_off + e) % interval == 0) {
-              const int idx = (seg_off + e) / interval - 1;
-              CHECK(idx >= 0 && ck_off[n] >= 0, "checkpoint index of seq %d", n);
-              if (same) CHECK(ck_off[n] + idx < nck, "exact checkpoint slot of seq %d", n);
-            }
-        covered += b1 - b0;
-        checks += 3;
-      }
-      if (same) CHECK(covered == nb, "segments of seq %d cover its %d blocks (P = %d)", n, nb, P);
+  // Record windows of W blocks: the plan's per-window tables and the chain's
+  // units, for a single window (W >= total_blocks) and for several.
+  const int Ws[3] = {total_blocks > 0 ? total_blocks : 1, rint_in(1, 4), rint_in(1, 40)};
+  for (int W : Ws) {
+    const int nwin = total_blocks > 0 ? (total_blocks + W - 1) / W : 1;
+    const int order_cap = N + (total_blocks > 1 ? total_blocks : 1);
+    // plan: sequences per window, saturated prefix sums, longest-first order
+    std::vector<int32_t> win_base(nwin + 1), order(order_cap, -1);
+    int acc = 0;
+    for (int w = 0; w < nwin; ++w) {
+      int first, count;
+      window_seqs(blk_off.data(), N, W, nwin, w, first, count);
+      CHECK(0 <= first && first + count <= N, "window %d sequences [%d, +%d)", w, first, count);
+      win_base[w] = acc;
+      acc = sat_add(acc, count, order_cap);
+      ++checks;
     }
+    win_base[nwin] = acc;
+    CHECK(acc <= N + nwin - 1, "window pairs %d > N + nwin - 1 = %d", acc, N + nwin - 1);
+    for (int e = 0; e < acc; ++e) {
+      const int w = owner_of(win_base.data(), nwin, e);
+      int first, count, c0, c1;
+      window_seqs(blk_off.data(), N, W, nwin, w, first, count);
+      window_range(w, W, total_blocks, c0, c1);
+      const int i = e - win_base[w];
+      CHECK(0 <= i && i < count, "entry %d of window %d", i, w);
+      const int n = first + i;
+      int p0, p1;
+      window_part(blk_off[n], blk_off[n + 1], c0, c1, p0, p1);
+      int rank = 0;
+      for (int m = first; m < first + count; ++m) {
+        int q0, q1;
+        window_part(blk_off[m], blk_off[m + 1], c0, c1, q0, q1);
+        rank += q1 - q0 > p1 - p0 || (q1 - q0 == p1 - p0 && m < n);
+      }
+      CHECK(win_base[w] + rank < order_cap && order[win_base[w] + rank] == -1, "order slot of window %d", w);
+      order[win_base[w] + rank] = n;
+      checks += 2;
+    }
+    // host walk (launch grids) against the plan's windows
+    walk_windows(host.data(), N, total_blocks, W, nwin, [&](int w, int c0, int c1, int first, int count, int longest) {
+      int f2, n2, a0, a1;
+      window_range(w, W, total_blocks, a0, a1);
+      CHECK(a0 == c0 && a1 == c1, "window %d range", w);
+      // the window's records fit the W blocks per head the workspace holds,
+      // and the windows tile the block list
+      CHECK(0 <= c0 && c0 <= c1 && c1 <= total_blocks && c1 - c0 <= W && c0 == w * W, "window %d: [%d, %d)", w,
+            c0, c1);
+      CHECK(w + 1 < nwin || c1 == total_blocks, "last window ends at %d of %d", c1, total_blocks);
+      if (same) {
+        window_seqs(blk_off.data(), N, W, nwin, w, f2, n2);
+        CHECK(f2 == first && n2 == count, "host walk of window %d: %d +%d, plan %d +%d", w, first, count, f2, n2);
+        int lg = 0;
+        for (int m = first; m < first + count; ++m) {
+          int q0, q1;
+          window_part(blk_off[m], blk_off[m + 1], c0, c1, q0, q1);
+          lg = q1 - q0 > lg ? q1 - q0 : lg;
+        }
+        CHECK(lg == longest, "longest part of window %d", w);
+      }
+      checks += 2;
+    });
+    // chain units of every window and segment count
+    std::vector<int> covered(N, 0), starts(N, 0), ends(N, 0), listed(N, 0);
+    int prev_out_seq = -1;   // the sequence the previous window carried out
+    for (int w = 0; w < nwin; ++w) {
+      int c0, c1;
+      window_range(w, W, total_blocks, c0, c1);
+      const int cnt = win_base[w + 1] - win_base[w];
+      int carry_in = 0, carry_out = 0, in_seq = -1, out_seq = -1;
+      for (int r = 0; r < cnt; ++r) {
+        const int n = order[win_base[w] + r];
+        CHECK(0 <= n && n < N, "unit %d of window %d", r, w);
+        if (n < 0 || n >= N) continue;
+        int s0, s1;
+        clamp_seq(dev.data(), n, T, s0, s1);
+        const int seq_len = s1 - s0, g0 = blk_off[n], g1 = blk_off[n + 1];
+        int p0, p1;
+        window_part(g0, g1, c0, c1, p0, p1);
+        // every listed sequence has blocks in the window, or is an empty one
+        // listed in this window only
+        if (same) CHECK(p1 > p0 || g0 == g1, "seq %d listed in window %d without blocks there", n, w);
+        if (p0 == p1 && g0 != g1) continue;   // not in this window (differing copies only)
+        if (same) {
+          listed[n] += g0 == g1;
+          covered[n] += p1 - p0;
+          starts[n] += p0 == 0;
+          ends[n] += g0 + p1 == g1;
+        }
+        if (p0 != 0) ++carry_in, in_seq = n;
+        if (g0 + p1 != g1) ++carry_out, out_seq = n;
+        for (int P = 1; P <= 16; P += (P == 1 ? 2 : 5)) {
+          int segcov = 0;
+          for (int seg = 0; seg < P; ++seg) {
+            int b0, b1;
+            part_segment(p1 - p0, seg, P, b0, b1);
+            const int blk0 = p0 + b0, blk1 = p0 + b1, nblk = blk1 - blk0;
+            segcov += nblk;
+            if (nblk > 0) {
+              // records of the unit inside the window's records of its head
+              CHECK(g0 + blk0 - c0 >= 0 && g0 + blk1 - c0 <= c1 - c0, "records of seq %d window %d seg %d/%d", n,
+                    w, seg, P);
+              const int seg_off = kBT * blk0;
+              const int len_raw = seq_len - seg_off < kBT * nblk ? seq_len - seg_off : kBT * nblk;
+              const int len = len_raw > 0 ? len_raw : 0;
+              if (len > 0) CHECK(s0 + seg_off >= 0 && s0 + seg_off + len <= T, "rows of seq %d window %d", n, w);
+              if (interval > 0)
+                for (int e = 16; e <= len; e += 16)
+                  if ((seg_off + e) % interval == 0) {
+                    const int idx = (seg_off + e) / interval - 1;
+                    CHECK(idx >= 0 && ck_off[n] >= 0, "checkpoint index of seq %d", n);
+                    if (same) CHECK(ck_off[n] + idx < nck, "exact checkpoint slot of seq %d", n);
+                  }
+              if (same && len_raw <= 0) CHECK(false, "empty rows in a nonempty segment of seq %d", n);
+            }
+            checks += 2;
+          }
+          CHECK(segcov == p1 - p0, "segments of seq %d cover its part in window %d", n, w);
+        }
+      }
+      // at most one sequence crosses each window edge
+      CHECK(carry_in <= 1 && carry_out <= 1, "window %d: %d carried in, %d out", w, carry_in, carry_out);
+      // the state a window carries out is the one the next window carries in
+      if (same) CHECK(in_seq == prev_out_seq, "window %d carries in seq %d, window before out %d", w, in_seq,
+                      prev_out_seq);
+      prev_out_seq = out_seq;
+      checks += 2;
+    }
+    if (same)
+      for (int n = 0; n < N; ++n) {
+        CHECK(covered[n] == seq_blocks(host[n + 1] - host[n]), "windows cover seq %d: %d blocks", n, covered[n]);
+        CHECK(starts[n] == 1 && ends[n] == 1, "seq %d starts %d times, ends %d times", n, starts[n], ends[n]);
+        if (host[n + 1] == host[n]) CHECK(listed[n] == 1, "empty seq %d listed %d times", n, listed[n]);
+        checks += 2;
+      }
   }
   return checks;
 }

@@ -67,7 +67,7 @@ def test_workspace_size(L):
     assert 257 * 32 * rec128 <= w < 257 * 32 * rec128 + 8192
     # the size depends on the total only, not on how it is split
     w4 = kda.workspace_size(1, 8192, 4, 128)             # 4 x 8 slices <= 80: segment states
-    assert 257 * 4 * rec128 + seg(1, 4, 128) <= w4 < 257 * 4 * rec128 + seg(1, 4, 128) + 4096
+    assert 257 * 4 * rec128 + seg(1, 4, 128) <= w4 < 257 * 4 * rec128 + seg(1, 4, 128) + 8192
     w16 = kda.workspace_size(1, 64, 2, 16)
     assert 3 * 2 * rec16 + seg(1, 2, 16) <= w16 < 3 * 2 * rec16 + seg(1, 2, 16) + 2048
     # ragged lengths never need more than T / 32 + num_seqs blocks
@@ -81,6 +81,38 @@ def test_workspace_size(L):
     assert kda.workspace_size(1, -1, 2, 128) == 0
     assert kda.workspace_size(1, 10, 0, 128) == 0
     assert kda.workspace_size(1, 2 ** 40, 1, 128) == 0    # too many blocks
+
+
+def test_workspace_size_windows(L):
+    """Record windows: the default size caps the records at
+    KDA_PREFILL_RECORD_CAP_BYTES (8 GiB), so it stops growing with T there
+    (the tables still grow by 16 bytes per 32-token block); a size for windows
+    of W blocks holds W blocks of records per head plus two carry states per
+    head."""
+    rec128, cap = 47 * 1024, 8 << 30
+    state = lambda H, D: H * D * D * 4
+    # one window below the cap: the same bytes as a window of every block
+    w = kda.workspace_size(1, 131072, 32, 128)
+    assert w == kda.workspace_size(1, 131072, 32, 128, window_blocks=4097)
+    assert w == kda.workspace_size(1, 131072, 32, 128, window_blocks=10 ** 9)
+    assert 4097 * 32 * rec128 <= w < 4097 * 32 * rec128 + 16 * 4097 + 4096
+    # beyond the cap: records of cap / (H x 47 KiB) blocks, plus the carry
+    blocks_cap = cap // (32 * rec128)
+    for T in (1 << 20, 1 << 22, 1 << 24):
+        wt = kda.workspace_size(1, T, 32, 128)
+        tables = 16 * (T // 32 + 1) + 4096
+        assert blocks_cap * 32 * rec128 + 2 * state(32, 128) <= wt
+        assert wt < blocks_cap * 32 * rec128 + 2 * state(32, 128) + tables
+    # growth from 1M to 16M tokens: the tables only
+    assert kda.workspace_size(1, 1 << 24, 32, 128) - kda.workspace_size(1, 1 << 20, 32, 128) < 16 * (1 << 19) + 4096
+    # explicit windows: W blocks of records per head and two carry states
+    for W in (1, 2, 7, 64):
+        ww = kda.workspace_size(3, 8192, 4, 128, window_blocks=W)
+        base = kda.workspace_size(3, 8192, 4, 128, window_blocks=10 ** 6)   # one window
+        assert ww == base - (8192 // 32 + 3 - W) * 4 * rec128 + 2 * state(4, 128)
+    assert kda.workspace_size(1, 64, 2, 16, window_blocks=1) < kda.workspace_size(1, 64, 2, 16)
+    assert kda.workspace_size(1, 64, 2, 128, window_blocks=0) == 0
+    assert kda.workspace_size(1, 64, 2, 128, window_blocks=-3) == 0
 
 
 def _prefill_status(L, **over):
@@ -142,9 +174,12 @@ def test_noalloc_prefill_errors_before_any_device_work(L):
     assert call(g_min=0.5) == kda.KDA_ERR_INVALID_ARG
     assert call(ckpt=24) == kda.KDA_ERR_INVALID_ARG
     assert call(opt=ctypes.byref(kda.Options(gate=-1))) == kda.KDA_ERR_INVALID_ARG
-    # 8192 tokens x 32 heads need more than the static scratch
+    # long calls run in record windows; only a shape whose tables and one block
+    # per head exceed the scratch is refused (8192 heads: 376 MiB per block)
     assert kda.workspace_size(1, 8192, 32, 128) > kda.NOALLOC_SCRATCH_BYTES
-    assert call(cu_host=as_p(big), N=1, H=32) == kda.KDA_ERR_WORKSPACE
+    assert kda.workspace_size(1, 8192, 32, 128, window_blocks=1) < kda.NOALLOC_SCRATCH_BYTES
+    assert kda.workspace_size(1, 8192, 8192, 128, window_blocks=1) > kda.NOALLOC_SCRATCH_BYTES
+    assert call(cu_host=as_p(big), N=1, H=8192) == kda.KDA_ERR_WORKSPACE
     empty = (ctypes.c_int32 * 1)(0)
     assert call(N=0, cu_host=as_p(empty)) == kda.KDA_OK
 

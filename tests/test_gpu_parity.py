@@ -903,3 +903,97 @@ def test_prefill_segments_chosen_by_the_library_full_size():
     check_states(fin[:, heads].cpu().numpy(), f_ref, "final")
     assert rel_err(fin.cpu().numpy(), fin1.cpu().numpy()) <= 1e-3
     assert rel_err(o.float().cpu().numpy(), o1.float().cpu().numpy()) <= 2e-2
+
+
+# ------------------------------------------------------------- record windows
+# A workspace smaller than all of a call's records runs the call in windows of
+# consecutive blocks: prep and chain per window, with the state of the one
+# sequence that crosses each window edge carried in fp32. Every block's
+# arithmetic is unchanged, so without segments the results are bit-identical
+# to one window.
+def _windowed_pair(q, k, v, g, beta, cu, s0, ckpt, W, options=None):
+    H, D = q.shape[1], q.shape[2]
+    plan = kda.make_plan(cu, H, D, q.device, ckpt, window_blocks=W)
+    one = kda.prefill(q, k, v, g, beta, cu_seqlens=cu, initial_state=s0, ckpt_interval=ckpt, options=options)
+    win = kda.prefill(q, k, v, g, beta, initial_state=s0, plan=plan, options=options)
+    torch.cuda.synchronize()
+    return one, win
+
+
+def _assert_identical(one, win, what):
+    for x, y, name in zip(one, win, ("o", "final state", "checkpoints")):
+        if x is None or y is None:
+            assert x is None and y is None, f"{what}: {name}"
+        else:
+            assert torch.equal(x, y), f"{what}: {name} differs"
+
+
+@pytest.mark.parametrize("W", [1, 3, 8])
+@pytest.mark.parametrize("D", [128, 16])
+def test_windowed_prefill_equals_one_window(D, W):
+    """Ragged batch (empty sequences, sequences shorter than a block, one
+    spanning many windows), checkpoints every 16 tokens, cached initial
+    states, segments off: windows of W blocks give bit-identical outputs,
+    final states and checkpoints, which also match the oracle."""
+    lengths = [0, 37, 200, 1, 64, 0, 513, 100, 32]
+    H = 3
+    print(f"case: windows of {W} blocks D={D} lengths={lengths}", flush=True)
+    inp = make_inputs(sum(lengths), H, D, seed=401 + W + D, lengths=lengths, initial_state=True)
+    q, k, v = (to_dev(x, torch.bfloat16) for x in (inp.q, inp.k, inp.v))
+    one, win = _windowed_pair(q, k, v, to_dev(inp.g), to_dev(inp.beta), inp.cu_seqlens,
+                              to_dev(inp.initial_state), 16, W, kda.Options(segments=1))
+    _assert_identical(one, win, f"W={W}")
+    o_ref, f_ref, ck_ref = oracle(inp, ckpt=16)
+    check_outputs(win[0].float().cpu().numpy(), o_ref, inp.cu_seqlens, H)
+    check_states(win[1].cpu().numpy(), f_ref, "final")
+    check_states(win[2].cpu().numpy(), ck_ref, "checkpoint")
+
+
+@pytest.mark.parametrize("segments", [0, 3])
+def test_windowed_prefill_with_segments_fp32_and_aliased_state(segments):
+    """Windows with the segment-parallel chain inside each window (the
+    library's choice, or 3 forced), fp32 storage, the initial state updated in
+    place (initial_state aliases final_state): against the oracle."""
+    lengths = [900, 0, 130, 415]
+    H, D, W = 2, 128, 12   # 47 blocks: 4 windows; the library takes 6 segments in the first
+    print(f"case: windows of {W} blocks with segments={segments}, fp32, aliased state", flush=True)
+    inp = make_inputs(sum(lengths), H, D, seed=421 + segments, lengths=lengths, initial_state=True, bf16=False)
+    plan = kda.make_plan(inp.cu_seqlens, H, D, DEV, 48, window_blocks=W)
+    state = to_dev(inp.initial_state)
+    o, fin, ck = kda.prefill(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), to_dev(inp.g), to_dev(inp.beta),
+                             initial_state=state, final_state=state, plan=plan,
+                             options=kda.Options(segments=segments))
+    torch.cuda.synchronize()
+    assert fin is state
+    o_ref, f_ref, ck_ref = oracle(inp, ckpt=48)
+    check_outputs(o.float().cpu().numpy(), o_ref, inp.cu_seqlens, H)
+    check_states(fin.cpu().numpy(), f_ref, "final")
+    check_states(ck.cpu().numpy(), ck_ref, "checkpoint")
+
+
+def test_windowed_prefill_gate_variants():
+    """Gated DeltaNet and DeltaNet layouts through windows of 2 blocks: bit
+    for bit the one-window results."""
+    lengths = [70, 0, 190, 33]
+    H, D = 2, 128
+    inp = make_inputs(sum(lengths), H, D, seed=431, lengths=lengths, initial_state=True)
+    q, k, v = (to_dev(x, torch.bfloat16) for x in (inp.q, inp.k, inp.v))
+    for gate in (kda.GATE_HEAD, kda.GATE_NONE):
+        print(f"case: windows of 2 blocks gate={gate}", flush=True)
+        g = to_dev(np.ascontiguousarray(inp.g[..., 0])) if gate == kda.GATE_HEAD else None
+        one, win = _windowed_pair(q, k, v, g, to_dev(inp.beta), inp.cu_seqlens, to_dev(inp.initial_state), 32, 2,
+                                  kda.Options(gate=gate, segments=1))
+        _assert_identical(one, win, f"gate={gate}")
+
+
+def test_windowed_long_prefill_full_size():
+    """B=1, H=32, T=131072, checkpoint every 32768, in four windows of 1024
+    blocks (1.5 GiB of records instead of 6.2 GiB): bit-identical to the
+    one-window call."""
+    T, H, D, I = 131072, 32, 128, 32768
+    print("case: B=1 H=32 T=131072 in 4 windows", flush=True)
+    q, k, v, g, beta, cu, _ = make_inputs_device(T, H, D, seed=441, device=DEV)
+    one, win = _windowed_pair(q, k, v, g, beta, cu, None, I, 1024)
+    plan = kda.make_plan(cu, H, D, DEV, I, window_blocks=1024)
+    assert plan.workspace.numel() < kda.workspace_size(1, T, H, D) // 3
+    _assert_identical(one, win, "4 windows")

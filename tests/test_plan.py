@@ -2,9 +2,11 @@
 
 The plan and chain kernels derive every table from the device copy of
 cu_seqlens; the launches are sized from the host copy. plan_check.cpp runs the
-same header functions on the CPU over seeded host / device pairs and checks
-that equal copies give the exact tables and that copies that differ never
-reach a record, row or checkpoint slot outside what the host copy sized.
+same header functions on the CPU over seeded host / device pairs and record
+windows, and checks that equal copies give the exact tables (and windows that
+cover every sequence once, with one carried state per window edge) and that
+copies that differ never reach a record, row, checkpoint slot or table entry
+outside what the host copy sized.
 """
 import os
 import shutil

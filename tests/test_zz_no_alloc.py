@@ -3,7 +3,8 @@ argument) against kda_prefill_chunked_ex (caller's workspace) on the same
 inputs, through the C ABI: calls in a row, each smaller than the one before,
 every output, final state and checkpoint bit-identical (both run the same
 kernels; the scratch keeps the previous call's contents, which the prefill
-must not depend on)."""
+must not depend on). Calls whose records exceed the scratch run in record
+windows."""
 import numpy as np
 import pytest
 import torch
@@ -63,11 +64,32 @@ def test_noalloc_equals_workspace_entry_point_on_shrinking_calls():
     _same(a, b, "call 3")
 
 
-def test_noalloc_refuses_shapes_beyond_the_scratch():
+def test_noalloc_runs_long_calls_in_record_windows():
+    """8192 tokens x 32 heads: 386 MB of records do not fit the 256 MiB
+    scratch at once, so the call runs in record windows; bit-identical to the
+    one-window call with a workspace. Then a smaller call in a row."""
     T, H, D = 8192, 32, 128
     assert kda.workspace_size(1, T, H, D) > kda.NOALLOC_SCRATCH_BYTES
-    print(f"case: noalloc beyond the scratch: T={T} H={H}", flush=True)
+    print(f"case: noalloc in windows: T={T} H={H} checkpoints every 1024", flush=True)
     q, k, v, g, beta, cu, _ = make_inputs_device(T, H, D, seed=304, device=DEV)
+    a, b = _both(q, k, v, g, beta, cu, None, 1024, None)
+    _same(a, b, "windowed call")
+    lengths = [33, 0, 500]
+    print(f"case: noalloc after the windowed call: lengths={lengths} H=3", flush=True)
+    inp = make_inputs(sum(lengths), 3, 128, seed=305, lengths=lengths, initial_state=True)
+    a, b = _both(to_dev(inp.q, torch.bfloat16), to_dev(inp.k, torch.bfloat16), to_dev(inp.v, torch.bfloat16),
+                 to_dev(inp.g), to_dev(inp.beta), inp.cu_seqlens, to_dev(inp.initial_state), 16, None)
+    _same(a, b, "call after the windowed call")
+
+
+def test_noalloc_refuses_shapes_beyond_the_scratch():
+    """Only a shape whose tables and one block of records per head exceed the
+    scratch is refused (8192 heads: 376 MiB per block), before any device
+    work."""
+    T, H, D = 32, 8192, 128
+    assert kda.workspace_size(1, T, H, D, window_blocks=1) > kda.NOALLOC_SCRATCH_BYTES
+    print(f"case: noalloc beyond the scratch: T={T} H={H}", flush=True)
+    q, k, v, g, beta, cu, _ = make_inputs_device(T, H, D, seed=306, device=DEV)
     with pytest.raises(kda.KdaError) as e:
         kda.prefill(q, k, v, g, beta, cu_seqlens=cu, noalloc=True)
     assert e.value.status == kda.KDA_ERR_WORKSPACE
