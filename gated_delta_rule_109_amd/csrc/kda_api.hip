@@ -117,7 +117,9 @@ size_t kda_prefill_workspace_size_window(int32_t num_seqs, int64_t total_tokens,
 size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t Dk,
                                   int32_t Dv) {
   if (H <= 0 || !supported_dims(Dk, Dv)) return 0;
-  const int64_t cap = (int64_t)((size_t)KDA_PREFILL_RECORD_CAP_BYTES / (kda::record_bytes(Dk) * (size_t)H));
+  const size_t cap_bytes = num_seqs == 1 ? (size_t)KDA_PREFILL_SINGLE_SEQ_WINDOW_BYTES
+                                         : (size_t)KDA_PREFILL_RECORD_CAP_BYTES;
+  const int64_t cap = (int64_t)(cap_bytes / (kda::record_bytes(Dk) * (size_t)H));
   return kda_prefill_workspace_size_window(num_seqs, total_tokens, H, Dk, Dv, cap > 1 ? cap : 1);
 }
 
@@ -173,15 +175,26 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, int dtype, 
   // A window also keeps the prep grid's second dimension (its blocks) within
   // kMaxWindowBlocks.
   constexpr int64_t kMaxWindowBlocks = 65535;
+  // A single sequence runs in windows of about
+  // KDA_PREFILL_SINGLE_SEQ_WINDOW_BYTES of records even when the workspace
+  // holds more: every window then still holds all of its (sequence, head)
+  // pairs, and part of each window's records is still in the memory-side
+  // cache when the chain reads them.
+  const size_t rec_bytes = kda::record_bytes(Dk) * (size_t)H;
+  int64_t max_window = kMaxWindowBlocks;
+  if (num_seqs == 1) {
+    const int64_t w1 = (int64_t)((size_t)KDA_PREFILL_SINGLE_SEQ_WINDOW_BYTES / rec_bytes);
+    max_window = w1 < 1 ? 1 : (w1 < max_window ? w1 : max_window);
+  }
   if (use_scratch) workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
   int64_t window = blocks > 0 ? blocks : 1;
-  if (blocks > kMaxWindowBlocks ||
+  if (blocks > max_window ||
       workspace_bytes < kda::prefill_layout(num_seqs, blocks, H, Dk, window, false).total) {
     const size_t fixed = kda::prefill_layout(num_seqs, blocks, H, Dk, 0, true).total;
     if (workspace_bytes < fixed) return KDA_ERR_WORKSPACE;
-    window = (int64_t)((workspace_bytes - fixed) / (kda::record_bytes(Dk) * (size_t)H));
+    window = (int64_t)((workspace_bytes - fixed) / rec_bytes);
     if (window < 1) return KDA_ERR_WORKSPACE;
-    window = window < kMaxWindowBlocks ? window : kMaxWindowBlocks;
+    window = window < max_window ? window : max_window;
     const int64_t nwin = (blocks + window - 1) / window;
     window = (blocks + nwin - 1) / nwin;
   }

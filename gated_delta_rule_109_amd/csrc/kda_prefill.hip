@@ -213,57 +213,74 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (tid == 0) {
     seq_blk_off[N] = carry_c;
     seq_ck_off[N] = carry_k;
-    carry_c = 0;
   }
+  // The offsets in LDS for N <= kMaxSortedSeqs (the searches below then take
+  // no dependent global loads); beyond that they are read from memory.
+  __shared__ int s_off[kMaxSortedSeqs + 1];
+  const bool in_lds = N <= kMaxSortedSeqs;
   __syncthreads();
+  if (in_lds)
+    for (int n = tid; n <= N; n += 1024) s_off[n] = seq_blk_off[n];
+  __syncthreads();
+  const int32_t* off = in_lds ? s_off : seq_blk_off;
   for (int c = tid; c < total_blocks; c += 1024) {
-    const int n = plan::owner_of(seq_blk_off, N, c);
+    const int n = plan::owner_of(off, N, c);
     int s0, s1, t0, cnt;
     plan::clamp_seq(cu, n, total_tokens, s0, s1);
-    plan::block_rows(s0, s1, c - seq_blk_off[n], total_tokens, t0, cnt);
+    plan::block_rows(s0, s1, c - off[n], total_tokens, t0, cnt);
     blk_info[c] = make_int2(t0, cnt);
   }
   // Windows: sequences per window, and their prefix sums (saturated at the
-  // order table's size, which the pairs never exceed).
-  for (int base = 0; base < nwin; base += 1024) {
-    const int w = base + tid;
-    int first, count = 0;
-    if (w < nwin) plan::window_seqs(seq_blk_off, N, W, nwin, w, first, count);
-    s_c[tid] = count;
-    __syncthreads();
-    for (int d = 1; d < 1024; d <<= 1) {
-      const int ac = tid >= d ? s_c[tid - d] : 0;
+  // order table's size, which the pairs never exceed). One window holds every
+  // sequence.
+  if (tid == 0) carry_c = 0;
+  __syncthreads();
+  if (nwin == 1) {
+    if (tid == 0) {
+      win_base[0] = 0;
+      carry_c = plan::sat_add(0, N, order_cap);
+    }
+  } else {
+    for (int base = 0; base < nwin; base += 1024) {
+      const int w = base + tid;
+      int first, count = 0;
+      if (w < nwin) plan::window_seqs(off, N, W, nwin, w, first, count);
+      s_c[tid] = count;
       __syncthreads();
-      s_c[tid] = plan::sat_add(s_c[tid], ac, order_cap);
+      for (int d = 1; d < 1024; d <<= 1) {
+        const int ac = tid >= d ? s_c[tid - d] : 0;
+        __syncthreads();
+        s_c[tid] = plan::sat_add(s_c[tid], ac, order_cap);
+        __syncthreads();
+      }
+      if (w < nwin) win_base[w] = plan::sat_add(carry_c, tid > 0 ? s_c[tid - 1] : 0, order_cap);
+      __syncthreads();
+      if (tid == 1023) carry_c = plan::sat_add(carry_c, s_c[1023], order_cap);
       __syncthreads();
     }
-    if (w < nwin) win_base[w] = plan::sat_add(carry_c, tid > 0 ? s_c[tid - 1] : 0, order_cap);
-    __syncthreads();
-    if (tid == 1023) carry_c = plan::sat_add(carry_c, s_c[1023], order_cap);
-    __syncthreads();
   }
+  __syncthreads();
   if (tid == 0) win_base[nwin] = carry_c;
   // Chain order within each window: sequences by blocks in the window,
   // longest first (ties by index), so that when the chain's workgroups
   // outnumber the compute units the longest recurrences start first. Ranked
   // by counting over the offsets in LDS for N <= kMaxSortedSeqs; beyond that,
   // the given order.
-  __shared__ int s_off[kMaxSortedSeqs + 1];
-  const bool sorted = N <= kMaxSortedSeqs;
-  if (sorted)
-    for (int n = tid; n <= N; n += 1024) s_off[n] = seq_blk_off[n];
-  __syncthreads();
   const int pairs = carry_c;
   for (int e = tid; e < pairs; e += 1024) {
-    const int w = plan::owner_of(win_base, nwin, e);
-    int first, count, c0, c1;
-    plan::window_seqs(seq_blk_off, N, W, nwin, w, first, count);
+    int w = 0, first = 0, count = N, base = 0;
+    if (nwin > 1) {
+      w = plan::owner_of(win_base, nwin, e);
+      base = win_base[w];
+      plan::window_seqs(off, N, W, nwin, w, first, count);
+    }
+    int c0, c1;
     plan::window_range(w, W, total_blocks, c0, c1);
-    const int i = e - win_base[w];
+    const int i = e - base;
     if (i >= count) continue;
     const int n = first + i;
     int rank = i;
-    if (sorted) {
+    if (in_lds) {
       int p0, p1;
       plan::window_part(s_off[n], s_off[n + 1], c0, c1, p0, p1);
       const int len = p1 - p0;
@@ -273,7 +290,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
         rank += p1 - p0 > len || (p1 - p0 == len && m < n);
       }
     }
-    if (win_base[w] + rank < order_cap) win_order[win_base[w] + rank] = n;
+    if (base + rank < order_cap) win_order[base + rank] = n;
   }
 }
 

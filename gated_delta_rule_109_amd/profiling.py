@@ -40,20 +40,45 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CHIP_CUS = 256                                # MI355X compute units
 
 
-def prefill_kernels(heads, blocks, units):
+RECORD_BYTES = 47 * 1024                      # one block record at D = 128
+SINGLE_SEQ_WINDOW_BYTES = 1 << 30             # records per window of a one-sequence call
+
+
+def prefill_windows(num_seqs, heads, blocks):
+    """Blocks per record window of a call whose workspace holds all of its
+    records (kda_prefill_workspace_size's): one window, except that a single
+    sequence takes windows of about 1 GiB of records, evened out."""
+    if num_seqs != 1:
+        return [blocks]
+    w = max(1, min(SINGLE_SEQ_WINDOW_BYTES // (heads * RECORD_BYTES), 65535))
+    if blocks <= w:
+        return [blocks]
+    nwin = -(-blocks // w)
+    w = -(-blocks // nwin)
+    return [w] * (nwin - 1) + [blocks - w * (nwin - 1)]
+
+
+def prefill_kernels(heads, blocks, units, num_seqs=None):
     """The kernels of one plain kda_prefill_chunked call at D = 128 (bf16 q/k/v,
     no front end, no segments) with `blocks` 32-token blocks per head and
-    `units` (sequence, head) chain units, with their grids in work-items (the
-    same instantiations also run other shapes in the same program, so a
-    dispatch is selected by kernel and grid)."""
+    `units` (sequence, head) chain units, as ((kernel, grid in work-items),
+    dispatches per call) (the same instantiations also run other shapes in
+    the same program, so a dispatch is selected by kernel and grid). Every
+    record window runs one prep and one chain dispatch; windows of a single
+    sequence hold all of its units."""
+    num_seqs = units // heads if num_seqs is None else num_seqs
     groups = (units + 7) // 8                 # 8 units x (slice groups) per group of workgroups
     if units * 8 > CHIP_CUS:                  # more 16-column slices than CUs: two per workgroup
         chain = ("kda::chain_kernel<128, unsigned short, 2>", groups * 8 * 4 * 512)
     else:
         chain = ("kda::chain_kernel<128, unsigned short, 1>", groups * 8 * 8 * 448)
-    return (("kda::plan_kernel", 1024),
-            ("kda::prep_kernel<128, unsigned short, false>", heads * blocks * 128),
-            chain)
+    windows = prefill_windows(num_seqs, heads, blocks)
+    out = {("kda::plan_kernel", 1024): 1}
+    for w in windows:
+        key = ("kda::prep_kernel<128, unsigned short, false>", heads * w * 128)
+        out[key] = out.get(key, 0) + 1
+    out[chain] = len(windows)
+    return tuple(out.items())
 
 
 # B = 1, H = 32, T = 131072 (4096 blocks) and T = 8192 (256 blocks)
@@ -62,7 +87,7 @@ PREFILL_8K = prefill_kernels(32, 256, 32)
 PREFILL_KERNELS = PREFILL_LONG
 # one kda_decode_step over 256 sequences x 32 heads at D = 128 (one workgroup of
 # 256 threads per head)
-DECODE_KERNELS = (("kda::decode_kernel<128, unsigned short, true, false>", 256 * 32 * 256),)
+DECODE_KERNELS = ((("kda::decode_kernel<128, unsigned short, true, false>", 256 * 32 * 256), 1),)
 WORKLOADS = {
     "prefill": (PREFILL_LONG, "KDA prefill HBM traffic (B=1, H=32, T=131072, D=128, checkpoint every 32768, "
                 "bf16 q/k/v)", "kda_prefill_chunked"),
@@ -138,15 +163,16 @@ def summarize(fetch_dir, write_dir, calib_mib, kernels=PREFILL_KERNELS):
     fw = calib_kib / w[cal][1]
     rows = []
     total = 0.0
-    for k in kernels:
+    mine = dict(kernels)
+    for k, per_call in kernels:
         if k not in f or k not in w:
             raise RuntimeError(f"{k} missing from the counter runs")
         fb = f[k][1] * ff * 1024
         wb = w[k][1] * fw * 1024
-        total += fb + wb
-        rows.append((k, f[k][0], f[k][1], w[k][1], fb, wb))
+        total += (fb + wb) * per_call
+        rows.append((k, f[k][0], f[k][1], w[k][1], fb, wb, per_call))
     others = [(k, f[k][0], f[k][1], w[k][1], f[k][1] * ff * 1024, w[k][1] * fw * 1024)
-              for k in sorted(f) if k in w and k not in kernels and k != cal]
+              for k in sorted(f) if k in w and k not in mine and k != cal]
     return {"fetch_factor": ff, "write_factor": fw, "rows": rows, "others": others,
             "bytes_per_call": total, "calib": (f[cal][1], w[cal][1])}
 
@@ -161,10 +187,12 @@ def render(res, calib_mib, command, algorithmic_bytes, title=WORKLOADS["prefill"
             f"{calib_mib} MiB; the counters read {res['calib'][0]:.4g} KiB (FETCH_SIZE) and "
             f"{res['calib'][1]:.4g} KiB (WRITE_SIZE), so FETCH_SIZE is scaled by {res['fetch_factor']:.3f} "
             f"and WRITE_SIZE by {res['write_factor']:.3f}.", "",
-            "| kernel | grid (work-items) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB (scaled) |",
-            "|---|---|---|---|---|---|---|"]
-    for (k, grid), n, fk, wk, fb, wb in res["rows"]:
-        out.append(f"| `{k}` | {grid} | {n} | {fk:.4g} | {wk:.4g} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
+            "Per dispatch of each kernel and grid (a call runs one prep and one chain dispatch per record "
+            "window):", "",
+            "| kernel | grid (work-items) | dispatches | per call | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB (scaled) | written MB (scaled) |",
+            "|---|---|---|---|---|---|---|---|"]
+    for (k, grid), n, fk, wk, fb, wb, per_call in res["rows"]:
+        out.append(f"| `{k}` | {grid} | {n} | {per_call} | {fk:.4g} | {wk:.4g} | {fb / 1e6:.1f} | {wb / 1e6:.1f} |")
     tot = res["bytes_per_call"]
     if res.get("others"):
         out += ["", "Other kda kernels in the same run (not part of the call above; per dispatch):", "",

@@ -154,8 +154,15 @@ int64_t kda_prefill_num_checkpoints(const int32_t* cu_seqlens_host, int32_t num_
  * (num_seqs * H * (Dv / 16) <= KDA_SEGMENT_SLICE_LIMIT) it also holds three
  * fp32 Dk x Dv states per sequence, head and segment; with windows, two fp32
  * Dk x Dv states per head carry the sequence that crosses a window edge. Its
- * contents are scratch and need no initialisation. */
+ * contents are scratch and need no initialisation.
+ * A single sequence (num_seqs == 1) runs in windows of about
+ * KDA_PREFILL_SINGLE_SEQ_WINDOW_BYTES of records whatever the workspace
+ * holds: each window still holds all of its heads, and part of its records is
+ * still in the 256 MB memory-side cache when they are read. With several
+ * sequences a window can hold only some of the (sequence, head) pairs, so
+ * they run in one window up to the cap. */
 #define KDA_PREFILL_RECORD_CAP_BYTES (8ull << 30)
+#define KDA_PREFILL_SINGLE_SEQ_WINDOW_BYTES (1ull << 30)
 size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t Dk,
                                   int32_t Dv);
 

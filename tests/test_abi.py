@@ -86,25 +86,33 @@ def test_workspace_size(L):
 def test_workspace_size_windows(L):
     """Record windows: the default size caps the records at
     KDA_PREFILL_RECORD_CAP_BYTES (8 GiB), so it stops growing with T there
-    (the tables still grow by 16 bytes per 32-token block); a size for windows
-    of W blocks holds W blocks of records per head plus two carry states per
-    head."""
+    (the tables still grow by 16 bytes per 32-token block); a single sequence
+    takes windows of about KDA_PREFILL_SINGLE_SEQ_WINDOW_BYTES (1 GiB); a size
+    for windows of W blocks holds W blocks of records per head plus two carry
+    states per head."""
     rec128, cap = 47 * 1024, 8 << 30
     state = lambda H, D: H * D * D * 4
-    # one window below the cap: the same bytes as a window of every block
-    w = kda.workspace_size(1, 131072, 32, 128)
-    assert w == kda.workspace_size(1, 131072, 32, 128, window_blocks=4097)
-    assert w == kda.workspace_size(1, 131072, 32, 128, window_blocks=10 ** 9)
-    assert 4097 * 32 * rec128 <= w < 4097 * 32 * rec128 + 16 * 4097 + 4096
+    # several sequences, below the cap: one window, the same bytes as a window
+    # of every block (131072 / 32 + 2 blocks at most)
+    w = kda.workspace_size(2, 131072, 32, 128)
+    assert w == kda.workspace_size(2, 131072, 32, 128, window_blocks=4098)
+    assert w == kda.workspace_size(2, 131072, 32, 128, window_blocks=10 ** 9)
+    assert 4098 * 32 * rec128 <= w < 4098 * 32 * rec128 + 16 * 4098 + 4096
     # beyond the cap: records of cap / (H x 47 KiB) blocks, plus the carry
     blocks_cap = cap // (32 * rec128)
     for T in (1 << 20, 1 << 22, 1 << 24):
-        wt = kda.workspace_size(1, T, 32, 128)
-        tables = 16 * (T // 32 + 1) + 4096
+        wt = kda.workspace_size(2, T, 32, 128)
+        tables = 16 * (T // 32 + 2) + 4096
         assert blocks_cap * 32 * rec128 + 2 * state(32, 128) <= wt
         assert wt < blocks_cap * 32 * rec128 + 2 * state(32, 128) + tables
     # growth from 1M to 16M tokens: the tables only
-    assert kda.workspace_size(1, 1 << 24, 32, 128) - kda.workspace_size(1, 1 << 20, 32, 128) < 16 * (1 << 19) + 4096
+    assert kda.workspace_size(2, 1 << 24, 32, 128) - kda.workspace_size(2, 1 << 20, 32, 128) < 16 * (1 << 19) + 4096
+    # one sequence: windows of 1 GiB of records (697 blocks at 32 heads)
+    w1 = (1 << 30) // (32 * rec128)
+    assert w1 == 697
+    assert kda.workspace_size(1, 131072, 32, 128) == kda.workspace_size(1, 131072, 32, 128, window_blocks=w1)
+    assert kda.workspace_size(1, 131072, 32, 128) < (1 << 30) + 2 * state(32, 128) + 16 * 4097 + 4096
+    assert kda.workspace_size(1, 8192, 32, 128) == kda.workspace_size(1, 8192, 32, 128, window_blocks=257)
     # explicit windows: W blocks of records per head and two carry states
     for W in (1, 2, 7, 64):
         ww = kda.workspace_size(3, 8192, 4, 128, window_blocks=W)

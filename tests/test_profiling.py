@@ -42,29 +42,37 @@ ABS = "void at::native::vectorized_elementwise_kernel<4, at::native::AbsFunctor<
 
 def test_traffic_summary_scales_by_the_calibration_kernel(tmp_path):
     f, w = str(tmp_path / "f"), str(tmp_path / "w")
+    # a call of two record windows: plan once, prep on two grids, chain twice
+    P1, P2, C = 32 * 683 * 128, 32 * 681 * 128, 256 * 448
+    kernels = ((("kda::plan_kernel", 1024), 1), (("kda::prep_kernel<128, unsigned short, false>", P1), 1),
+               (("kda::prep_kernel<128, unsigned short, false>", P2), 1),
+               (("kda::chain_kernel<128, unsigned short, 1>", C), 2))
     # the calibration kernel reads and writes 256 MiB; the counters read half
     # of that for FETCH_SIZE and all of it for WRITE_SIZE
-    write_counters(f, [(ABS, "FETCH_SIZE", 128 * 1024), (PLAN, "FETCH_SIZE", 1), (PREP, "FETCH_SIZE", 1000),
-                       (PREP_GEN, "FETCH_SIZE", 5000), (CHAIN, "FETCH_SIZE", 2000), (CHAIN, "FETCH_SIZE", 4000),
+    write_counters(f, [(ABS, "FETCH_SIZE", 128 * 1024), (PLAN, "FETCH_SIZE", 1, 1024), (PREP, "FETCH_SIZE", 1000, P1),
+                       (PREP, "FETCH_SIZE", 900, P2), (PREP_GEN, "FETCH_SIZE", 5000, P1),
+                       (CHAIN, "FETCH_SIZE", 2000, C), (CHAIN, "FETCH_SIZE", 4000, C),
                        (CHAIN, "FETCH_SIZE", 99999, 4 * 8 * 448)])      # a smaller call: not counted
-    write_counters(w, [(ABS, "WRITE_SIZE", 256 * 1024), (PLAN, "WRITE_SIZE", 1), (PREP, "WRITE_SIZE", 300),
-                       (PREP_GEN, "WRITE_SIZE", 9), (CHAIN, "WRITE_SIZE", 100)])
-    res = P.summarize(f, w, 256)
+    write_counters(w, [(ABS, "WRITE_SIZE", 256 * 1024), (PLAN, "WRITE_SIZE", 1, 1024), (PREP, "WRITE_SIZE", 300, P1),
+                       (PREP, "WRITE_SIZE", 200, P2), (PREP_GEN, "WRITE_SIZE", 9, P1), (CHAIN, "WRITE_SIZE", 100, C)])
+    res = P.summarize(f, w, 256, kernels)
     assert res["fetch_factor"] == pytest.approx(2.0) and res["write_factor"] == pytest.approx(1.0)
     # plain call only (the front-end prep is listed apart): fetch x2, write x1,
-    # chain fetch averaged over its two dispatches
-    want = (2 * (1 + 1000 + 3000) + (1 + 300 + 100)) * 1024
+    # each chain dispatch the mean of its two samples, two chain dispatches per call
+    want = (2 * (1 + 1000 + 900 + 2 * 3000) + (1 + 300 + 200 + 2 * 100)) * 1024
     assert res["bytes_per_call"] == pytest.approx(want)
     assert [r[0][0] for r in res["others"]] == ["kda::prep_kernel<128, unsigned short, true>"]
+    text = P.render(res, 256, ["cmd"], 1000)
+    assert "| 2 | " in text   # the chain's dispatches per call
 
 
 def test_traffic_record_follows_the_sources(tmp_path):
     f, w = str(tmp_path / "f"), str(tmp_path / "w")
-    write_counters(f, [(ABS, "FETCH_SIZE", 1024), (PLAN, "FETCH_SIZE", 1), (PREP, "FETCH_SIZE", 1),
+    write_counters(f, [(ABS, "FETCH_SIZE", 1024), (PLAN, "FETCH_SIZE", 1), (PREP, "FETCH_SIZE", 1, 32 * 256 * 128),
                        (CHAIN, "FETCH_SIZE", 1)])
-    write_counters(w, [(ABS, "WRITE_SIZE", 1024), (PLAN, "WRITE_SIZE", 1), (PREP, "WRITE_SIZE", 1),
+    write_counters(w, [(ABS, "WRITE_SIZE", 1024), (PLAN, "WRITE_SIZE", 1), (PREP, "WRITE_SIZE", 1, 32 * 256 * 128),
                        (CHAIN, "WRITE_SIZE", 1)])
-    text = P.render(P.summarize(f, w, 1), 1, ["cmd"], 1000)
+    text = P.render(P.summarize(f, w, 1, P.PREFILL_8K), 1, ["cmd"], 1000)
     out = tmp_path / "t.md"
     out.write_text(text)
     rec = P.read_record(str(out))
@@ -93,14 +101,22 @@ def test_mfma_busy_uses_one_xcd_of_active_cycles(tmp_path):
 
 
 def test_prefill_grids_follow_the_shape():
+    # one sequence of 4096 blocks at 32 heads: windows of about 1 GiB of
+    # records (697 blocks at most), evened out: 5 x 683 + 681
+    assert P.prefill_windows(1, 32, 4096) == [683] * 5 + [681]
+    assert P.prefill_windows(1, 32, 256) == [256]
+    assert P.prefill_windows(16, 32, 2756) == [2756]
     long = dict(P.WORKLOADS["prefill"][0])
-    assert long["kda::prep_kernel<128, unsigned short, false>"] == 32 * 4096 * 128
-    assert long["kda::chain_kernel<128, unsigned short, 1>"] == 256 * 448
+    assert long[("kda::prep_kernel<128, unsigned short, false>", 32 * 683 * 128)] == 5
+    assert long[("kda::prep_kernel<128, unsigned short, false>", 32 * 681 * 128)] == 1
+    assert long[("kda::chain_kernel<128, unsigned short, 1>", 256 * 448)] == 6
+    assert long[("kda::plan_kernel", 1024)] == 1
     short = dict(P.WORKLOADS["prefill_8k"][0])
-    assert short["kda::prep_kernel<128, unsigned short, false>"] == 32 * 256 * 128
+    assert short[("kda::prep_kernel<128, unsigned short, false>", 32 * 256 * 128)] == 1
+    assert short[("kda::chain_kernel<128, unsigned short, 1>", 256 * 448)] == 1
     # 16 sequences x 32 heads: 512 units (4096 slices, more than the CUs), 64
     # groups of 8 units x 4 two-slice workgroups of 512 threads
-    assert dict(P.prefill_kernels(32, 2756, 512))["kda::chain_kernel<128, unsigned short, 2>"] == 2048 * 512
+    assert dict(P.prefill_kernels(32, 2756, 512))[("kda::chain_kernel<128, unsigned short, 2>", 2048 * 512)] == 1
 
 
 def test_kernel_key_keeps_template_arguments():
