@@ -41,12 +41,13 @@ bool scan_lengths(const int32_t* cu, int32_t num_seqs, int64_t* tokens, int64_t*
 
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
-// Lowest decay floor the prefill accepts: a block's decayed keys span a
-// factor of up to exp(-32 g_min) (k / P_r with P_r >= exp(32 g_min)), which
-// must stay inside the fp32 / bf16 normal range (2^126) with margin.
+// Lowest decay floor the prefill accepts: a chunk's decayed keys span a
+// factor of up to exp(-16 g_min) (k / P_r with P_r >= exp(16 g_min) inside
+// each 16-token chunk), which must stay inside the fp32 / bf16 normal range
+// (2^126) with margin.
 constexpr float kMinGateFloor = KDA_PREFILL_MIN_G_FLOOR;
-static_assert(kda::kBlockTokens * -KDA_PREFILL_MIN_G_FLOOR * 1.4426950408889634f < 120.f,
-              "decay span of a block");
+static_assert(KDA_CHUNK * -KDA_PREFILL_MIN_G_FLOOR * 1.4426950408889634f < 120.f,
+              "decay span of a chunk");
 
 // Every tensor pointer must be 16-byte aligned (NULL passes).
 // Options: NULL, or known flag bits, a known gate layout and a usable epsilon.

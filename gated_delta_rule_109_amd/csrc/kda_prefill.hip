@@ -21,7 +21,12 @@
 // of a chunk. A tail block is padded with k = q = 0, alpha = 1, beta = 0,
 // which leaves the state and the valid outputs unchanged. The state after the
 // first 16 tokens of a block (a checkpoint position when the interval is an
-// odd multiple of 16) is Diag(P_16) S + Diag(P_16 / Pc) Kh[<16]^T delta[<16].
+// odd multiple of 16) is Diag(P_16) S + Diag(P_16 / Pc) Kh[<16]^T delta[<16],
+// with P_16 / Pc = 1 / Pb, Pb the decay over the block's second 16 tokens.
+// For floors below -2.5, Km = k / P is formed inside each 16-token chunk
+// relative to the chunk's own start (the A and L tiles between the two
+// chunks take k e_15 / e_j), so no factor exceeds exp(-16 g_min), and the
+// records carry Pb, which stays in range where Pc may not.
 //
 // Kernels, all on the caller's stream:
 //  1. plan_kernel   (1 workgroup): per-sequence block / checkpoint offsets, a
@@ -98,7 +103,8 @@ static_assert(plan::kBT == kBlockTokens, "one block size");
 //   T   [u]  (2 KiB, 32 bytes per lane):   T[16u + mm][tok(8g + j)]     hi x 8, lo x 8
 //   L   [u]:                               L[16u + mm][tok(8g + j)]     bf16 x 8
 //   Pc  : Pc[0..D) then P_16[0..D), fp32 (decay over the whole block and over
-//         its first 16 tokens, per channel).
+//         its first 16 tokens, per channel); in records for floors below
+//         -2.5, Pb (the decay over its last 16 tokens) in place of Pc.
 __device__ __forceinline__ int ch_of(int p, int g, int j) { return j < 4 ? 32 * p + 4 * g + j : 32 * p + 16 + 4 * g + j - 4; }
 
 template <int D>
@@ -296,9 +302,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
 
 // ---- 2. per-block preparation ------------------------------------------------------
 // Two phases per (block, head):
-//  1. one thread per key channel: gates, the in-block cumulative decay P_r
-//     (kept in LDS), Pc and P_16, and the Kh fragments (Kh needs every token
-//     of one channel, which this mapping holds);
+//  1. one thread per key channel: gates, the cumulative decay within each
+//     16-token chunk (kept in LDS), the chunks' decays P_16 and Pb (Pc =
+//     P_16 Pb), and the Kh fragments (Kh needs every token of one channel,
+//     which this mapping holds);
 //  2. one lane per (token, 8 channels) in exactly the fragment layout: each
 //     lane loads its q / k pieces, scales them by P (Kp, Qt) and 1 / P (Km),
 //     stores the Kp / Qt fragments and keeps all three in registers for the
@@ -314,7 +321,7 @@ constexpr int prep_threads() { return D >= 128 ? D : 64; }
 // their inverse L2 norms (phase 0 computes them per token), and g and beta
 // may be logits: alpha = max(1 / (1 + e^a), e^{g_min}), beta = sigmoid(b).
 // The plain KDA call uses kGeneral = false, which has none of this code.
-template <int D, typename TIn, bool kGeneral>
+template <int D, typename TIn, bool kGeneral, bool kRebase = false>
 __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const int2* __restrict__ blk_info, int c0, int H, float g_min,
@@ -497,21 +504,31 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
       a[t] = t < cnt ? alpha_of(a[t]) : 1.f;
       kf[t] = t < cnt ? kf[t] * rk(t) : 0.f;
     }
+    // In-block decay sP[t] = prod_{s <= t} alpha_s. With kRebase it restarts
+    // at the second chunk (prod_{16 <= s <= t} alpha_s for t >= 16), so that
+    // no factor falls below exp(16 g_min): the A and L products below then
+    // take each chunk relative to its own start. P16: the first chunk's decay.
     float P = 1.f, P16 = 1.f;
 #pragma unroll
     for (int t = 0; t < kBT; ++t) {
+      if (kRebase && t == kChunk) {
+        P16 = P;
+        P = 1.f;
+      }
       P *= a[t];
       sP[t][ch] = P;
-      if (t == kChunk - 1) P16 = P;
+      if (!kRebase && t == kChunk - 1) P16 = P;
     }
     // Kh_t = k_t * prod_{s > t} alpha_s (in place of k), token groups
-    // g = 0..3 of this channel
+    // g = 0..3 of this channel (with kRebase, Pb = prod_{s >= 16} alpha_s,
+    // the second chunk's decay, on the way)
     float* kh = kf;
-    float Bk = 1.f;
+    float Bk = 1.f, Pb = 1.f;
 #pragma unroll
     for (int t = kBT - 1; t >= 0; --t) {
       kh[t] = kf[t] * Bk;
       Bk *= a[t];
+      if (kRebase && t == kChunk) Pb = Bk;
     }
     const int rt = ch / 16, cm = ch % 16;
 #pragma unroll
@@ -524,7 +541,9 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
       *(bf16x8*)(rec + R::kKh + (2 * rt) * 1024 + (16 * g4 + cm) * 16) = cat(hi0, hi1);
       *(bf16x8*)(rec + R::kKh + (2 * rt + 1) * 1024 + (16 * g4 + cm) * 16) = cat(lo0, lo1);
     }
-    ((float*)(rec + R::kPc))[ch] = P;
+    // the block's decay, or with kRebase the second chunk's (the block's is
+    // then P16 Pb, which may fall below the fp32 range where 1 / Pb does not)
+    ((float*)(rec + R::kPc))[ch] = kRebase ? Pb : P;
     ((float*)(rec + R::kPc))[D + ch] = P16;
   }
   __syncthreads();
@@ -570,12 +589,24 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
       // token tile) pairs with us <= ut (the pair (0, 1) stays zero).
       f32x4 acc[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
       float qk[2] = {0.f, 0.f};          // partial q_t . k_t over this lane's channels
+      // With kRebase each chunk is taken relative to its own start (sP
+      // restarts at token 16): with e = e^{Gamma}, the (row chunk, column
+      // chunk) tiles are
+      //   (0, 0): (x e_i)(k_j / e_j),  (1, 1): (x e'_i)(k_j / e'_j),
+      //   (1, 0): (x e'_i)(k_j e_15 / e_j),
+      // e' the second chunk's own decay, so every factor lies within
+      // exp(16 g_min) of 1. The records keep K~+ and Q~ relative to the
+      // block start (x e'_i e_15 in the second chunk). Without it every tile
+      // is (x e_i)(k_j / e_j), factors within exp(32 g_min) of 1.
 #pragma unroll
       for (int p = 0; p < R::NP; ++p) {
-        bf16x8 X[2], Xl[2], Km[2], Kml[2];
+        bf16x8 X[2], Xl[2], Km[2], Kml[2], Km2, Km2l;
+        const int c0 = ch_of(p, gq, 0), c1 = ch_of(p, gq, 4);
+        f32x4 E0, E1;   // e_15 of the lane's channels
+        if (kRebase) E0 = decay(kChunk - 1, c0), E1 = decay(kChunk - 1, c1);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int t = 16 * u + mm, c0 = ch_of(p, gq, 0), c1 = ch_of(p, gq, 4);
+          const int t = 16 * u + mm;
           const f32x4 P0 = decay(t, c0), P1 = decay(t, c1);
           const float rs = which ? rq(t) : rk(t);
           const f32x4 x0 = (which ? qpiece(qraw[u][p][0], t, c0) : kpiece(t, c0)) * rs;
@@ -595,25 +626,39 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
           split_bf16(r1, h1, l1);
           Km[u] = cat(h0, h1);
           Kml[u] = cat(l0, l1);
+          if (kRebase && u == 0) {   // the first chunk's columns against the second chunk's rows
+            split_bf16(r0 * E0, h0, l0);
+            split_bf16(r1 * E1, h1, l1);
+            Km2 = cat(h0, h1);
+            Km2l = cat(l0, l1);
+          }
           split_bf16(x0 * P0, h0, l0);
           split_bf16(x1 * P1, h1, l1);
           X[u] = cat(h0, h1);
           Xl[u] = cat(l0, l1);
-          if (which == 0) *(bf16x8*)(rec + R::kKpl + (u * R::NP + p) * 1024 + lane * 16) = Xl[u];
-          *(bf16x8*)(rec + (which ? R::kQt : R::kKp) + (u * R::NP + p) * 1024 + lane * 16) = X[u];
+          bf16x8 Xr = X[u], Xrl = Xl[u];   // record: relative to the block start
+          if (kRebase && u == 1) {
+            split_bf16((x0 * P0) * E0, h0, l0);
+            split_bf16((x1 * P1) * E1, h1, l1);
+            Xr = cat(h0, h1);
+            Xrl = cat(l0, l1);
+          }
+          if (which == 0) *(bf16x8*)(rec + R::kKpl + (u * R::NP + p) * 1024 + lane * 16) = Xrl;
+          *(bf16x8*)(rec + (which ? R::kQt : R::kKp) + (u * R::NP + p) * 1024 + lane * 16) = Xr;
         }
 #pragma unroll
         for (int ut = 0; ut < 2; ++ut)
 #pragma unroll
           for (int us = 0; us <= ut; ++us) {
+            const bf16x8 kh = kRebase && ut > us ? Km2 : Km[us], kl = kRebase && ut > us ? Km2l : Kml[us];
             if (which) {
-              acc[ut][us] = mfma32(Km[us], X[ut], acc[ut][us]);
-              acc[ut][us] = mfma32(Km[us], Xl[ut], acc[ut][us]);
-              acc[ut][us] = mfma32(Kml[us], X[ut], acc[ut][us]);
+              acc[ut][us] = mfma32(kh, X[ut], acc[ut][us]);
+              acc[ut][us] = mfma32(kh, Xl[ut], acc[ut][us]);
+              acc[ut][us] = mfma32(kl, X[ut], acc[ut][us]);
             } else {
-              acc[ut][us] = mfma32(X[ut], Km[us], acc[ut][us]);
-              acc[ut][us] = mfma32(Xl[ut], Km[us], acc[ut][us]);
-              acc[ut][us] = mfma32(X[ut], Kml[us], acc[ut][us]);
+              acc[ut][us] = mfma32(X[ut], kh, acc[ut][us]);
+              acc[ut][us] = mfma32(Xl[ut], kh, acc[ut][us]);
+              acc[ut][us] = mfma32(X[ut], kl, acc[ut][us]);
             }
           }
       }
@@ -808,7 +853,9 @@ struct ChainCfg {
 // lo hi): with slow decay K~+ is close to the bf16 key, the state is long
 // lived and K~+ S nearly cancels V, so a single bf16 term of either operand
 // dominates the error of V - K~+ S.
-template <int D, typename TIn, int NSL>
+// kRebase: records of floors below -2.5 (decay over the block's second chunk
+// in place of the block's decay).
+template <int D, typename TIn, int NSL, bool kRebase>
 __global__ __launch_bounds__((ChainCfg<D, TIn, NSL>::kThreads)) void chain_kernel(
     const TIn* __restrict__ v, const int32_t* __restrict__ cu, int64_t total_tokens, int nck,
     const int32_t* __restrict__ seq_blk_off, const int32_t* __restrict__ seq_ck_off,
@@ -1133,6 +1180,7 @@ __global__ __launch_bounds__((ChainCfg<D, TIn, NSL>::kThreads)) void chain_kerne
     f32x4 vv[2];                       // V[16u + 4gq .. +3][mm]
     bf16x8 khh[TW], khl[TW];           // Kh hi / lo per row tile
     f32x4 pc[TW], p16[TW];             // Pc and P_16 of rows 16rt + 4gq .. +3
+    f32x4 pb[kRebase ? TW : 1];        // with kRebase: the second chunk's decay (Pc = P_16 Pb)
     auto read_kp = [&](const char* slot) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -1162,6 +1210,10 @@ __global__ __launch_bounds__((ChainCfg<D, TIn, NSL>::kThreads)) void chain_kerne
         khl[t] = *(const bf16x8*)(slot + R::kKh + (2 * rt + 1) * 1024 + lane * 16);
         pc[t] = *(const f32x4*)(slot + R::kPc + (16 * rt + 4 * gq) * 4);
         p16[t] = *(const f32x4*)(slot + R::kPc + (D + 16 * rt + 4 * gq) * 4);
+        if constexpr (kRebase) {
+          pb[t] = pc[t];
+          pc[t] = p16[t] * pb[t];
+        }
       }
     };
     // partial K~+ S of a block over this wave's rows: it stays in u_own and
@@ -1267,7 +1319,8 @@ __global__ __launch_bounds__((ChainCfg<D, TIn, NSL>::kThreads)) void chain_kerne
 #pragma unroll
         for (int t = 0; t < TW; ++t) {
           const f32x4 upd = mfma32(khl[t], dh_m, mfma32(khh[t], dl_m, mfma32(khh[t], dh_m, z)));
-          sm[t] = p16[t] * acc[t] + (p16[t] / pc[t]) * upd;
+          if constexpr (kRebase) sm[t] = p16[t] * acc[t] + upd / pb[t];
+          else sm[t] = p16[t] * acc[t] + (p16[t] / pc[t]) * upd;
         }
         store_state(sm, (seg_off + mid) / ckpt_interval - 1);
       }
@@ -1411,6 +1464,11 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ segs, int
   }
 }
 
+// Lowest floor for which prep takes the A and L products relative to the
+// block start: k / P_r with P_r >= exp(32 g_min) stays within exp(80). Lower
+// floors take them relative to each 16-token chunk's start.
+constexpr float kRebaseBelow = -2.5f;
+
 template <int D, typename TIn>
 static hipError_t launch_prefill_t(const PrefillArgs& a) {
   const int total_blocks = (int)a.total_blocks;
@@ -1434,13 +1492,20 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
   if (e != hipSuccess) return e;
   using Cfg = ChainCfg<D, TIn, 1>;
   const bool seg_ok = segments_allowed(a.num_seqs, a.H, D);
+  const bool rebase = a.g_min < kRebaseBelow;
   float* segs = seg_ok ? (float*)(ws + L.segs) : nullptr;
   plan::walk_windows(a.cu_seqlens_host, a.num_seqs, total_blocks, W, nwin,
                      [&](int w, int c0, int c1, int, int count, int longest) {
     if (e != hipSuccess) return;
     const int nw = c1 - c0;
     if (nw > 0) {
-      if (a.fe_flags || a.gate != KDA_GATE_CHANNEL)
+      // floors below kRebaseBelow: the chunk-relative A and L products
+      if (rebase)
+        hipLaunchKernelGGL((prep_kernel<D, TIn, true, true>), dim3((unsigned)a.H, (unsigned)nw),
+                           dim3(prep_threads<D>()), 0, a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g,
+                           a.beta, (const int2*)blk_info, c0, a.H, a.g_min, a.fe_flags, a.fe_eps, (int)a.gate,
+                           records);
+      else if (a.fe_flags || a.gate != KDA_GATE_CHANNEL)
         hipLaunchKernelGGL((prep_kernel<D, TIn, true>), dim3((unsigned)a.H, (unsigned)nw),
                            dim3(prep_threads<D>()), 0, a.stream, (const TIn*)a.q, (const TIn*)a.k, a.g,
                            a.beta, (const int2*)blk_info, c0, a.H, a.g_min, a.fe_flags, a.fe_eps, (int)a.gate,
@@ -1467,7 +1532,9 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
       // is set by the record traffic per column rather than by one recurrence's
       // length.
       const bool two = D == 128 && slices * units > kChipCUs;
-      auto chain = two ? chain_kernel<D, TIn, D == 128 ? 2 : 1> : chain_kernel<D, TIn, 1>;
+      constexpr int kTwo = D == 128 ? 2 : 1;
+      auto chain = rebase ? (two ? chain_kernel<D, TIn, kTwo, true> : chain_kernel<D, TIn, 1, true>)
+                          : (two ? chain_kernel<D, TIn, kTwo, false> : chain_kernel<D, TIn, 1, false>);
       const int threads = two ? ChainCfg<D, TIn, D == 128 ? 2 : 1>::kThreads : Cfg::kThreads;
       const int groups_per_unit = two ? D / 32 : D / 16;
       const int64_t groups = (nh * units + 7) / 8;     // 8 units x (slice groups) per group of workgroups

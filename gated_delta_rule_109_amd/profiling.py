@@ -69,13 +69,13 @@ def prefill_kernels(heads, blocks, units, num_seqs=None):
     num_seqs = units // heads if num_seqs is None else num_seqs
     groups = (units + 7) // 8                 # 8 units x (slice groups) per group of workgroups
     if units * 8 > CHIP_CUS:                  # more 16-column slices than CUs: two per workgroup
-        chain = ("kda::chain_kernel<128, unsigned short, 2>", groups * 8 * 4 * 512)
+        chain = ("kda::chain_kernel<128, unsigned short, 2, false>", groups * 8 * 4 * 512)
     else:
-        chain = ("kda::chain_kernel<128, unsigned short, 1>", groups * 8 * 8 * 448)
+        chain = ("kda::chain_kernel<128, unsigned short, 1, false>", groups * 8 * 8 * 448)
     windows = prefill_windows(num_seqs, heads, blocks)
     out = {("kda::plan_kernel", 1024): 1}
     for w in windows:
-        key = ("kda::prep_kernel<128, unsigned short, false>", heads * w * 128)
+        key = ("kda::prep_kernel<128, unsigned short, false, false>", heads * w * 128)
         out[key] = out.get(key, 0) + 1
     out[chain] = len(windows)
     return tuple(out.items())

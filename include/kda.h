@@ -68,10 +68,12 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
  * rounding.) */
 #define KDA_CHUNK 16
 
-/* Lowest decay floor (g_min) the prefill accepts: inside a 32-token block the
- * decayed keys span a factor up to exp(-32 g_min), which must stay well inside
- * the fp32 / bf16 range. ln 0.5 (the configurations here) is far above it. */
-#define KDA_PREFILL_MIN_G_FLOOR (-2.5f)
+/* Lowest decay floor (g_min) the prefill accepts: inside each 16-token chunk
+ * the decayed keys span a factor up to exp(-16 g_min), which must stay inside
+ * the fp32 / bf16 normal range with margin (exp(80) at -5; alpha >= 0.0067).
+ * ln 0.5 (the configurations here) is far above it. Decode has no such
+ * limit. */
+#define KDA_PREFILL_MIN_G_FLOOR (-5.0f)
 
 /* Options of the extended entry points (kda_prefill_chunked_ex,
  * kda_decode_tokens). A NULL pointer means all defaults: the KDA gate and no

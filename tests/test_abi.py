@@ -154,7 +154,7 @@ def test_prefill_argument_errors(L):
     assert _prefill_status(L, ws=None, ws_bytes=1 << 30) == E.KDA_ERR_WORKSPACE
     assert _prefill_status(L, ws=ctypes.c_void_p(0x1010), ws_bytes=1 << 30) == E.KDA_ERR_WORKSPACE
     assert _prefill_status(L, v=ctypes.c_void_p(0x1002)) == E.KDA_ERR_INVALID_ARG   # misaligned
-    assert _prefill_status(L, g_min=-3.0) == E.KDA_ERR_INVALID_ARG     # decay floor below the supported range
+    assert _prefill_status(L, g_min=-5.5) == E.KDA_ERR_INVALID_ARG     # decay floor below the supported range
     assert _prefill_status(L, g_min=0.5) == E.KDA_ERR_INVALID_ARG
     assert _prefill_status(L, g_min=float("nan")) == E.KDA_ERR_INVALID_ARG
     empty = (ctypes.c_int32 * 1)(0)

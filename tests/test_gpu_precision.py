@@ -106,7 +106,7 @@ def _wild_gates(shape, seed):
 
 
 @pytest.mark.parametrize("D", [128, 16])
-@pytest.mark.parametrize("g_min", [LN_HALF, -2.5])
+@pytest.mark.parametrize("g_min", [LN_HALF, -2.5, -5.0])
 def test_prefill_unclamped_gates(D, g_min):
     """g drawn from {-5, -1, -0.3, 0, 0.375}: the kernel clamps to [g_min, 0]
     on load, as the oracle does."""
@@ -177,7 +177,7 @@ def test_decode_tokens_unclamped_gates(D, g_min):
 
 # ------------------------------------------------------------ decay floors below ln 1/2
 @pytest.mark.parametrize("D", [128, 16])
-@pytest.mark.parametrize("g_min", [-2.5, -1.5])
+@pytest.mark.parametrize("g_min", [-5.0, -4.0, -2.5, -1.5])
 def test_prefill_low_decay_floor(D, g_min):
     """Half the key channels sit on the floor g_min (alpha = e^g_min every
     token), the others draw -softplus(N(0, 1)) down to g_min: varlen, cached
@@ -196,6 +196,38 @@ def test_prefill_low_decay_floor(D, g_min):
     torch.cuda.synchronize()
     o_ref, f_ref, ck_ref = reference.prefill(inp.q, inp.k, inp.v, g, inp.beta, cu_seqlens=inp.cu_seqlens,
                                              initial_state=inp.initial_state, g_min=g_min, ckpt_interval=48)
+    check_outputs(_host(o), o_ref, inp.cu_seqlens, H)
+    check_states(fin.cpu().numpy(), f_ref, "final")
+    check_states(ck.cpu().numpy(), ck_ref, "checkpoint")
+
+
+@pytest.mark.parametrize("D", [128, 16])
+@pytest.mark.parametrize("g_min", [-5.0, -2.5])
+def test_prefill_floor_in_one_chunk_only(D, g_min):
+    """Decay at the floor in one 16-token chunk of every block and none in the
+    other (per channel, both orders), so the two chunks' decays differ by up
+    to exp(16 g_min): the A and L tiles between the chunks and the checkpoints
+    after a block's first chunk. Varlen with cached states and a checkpoint
+    every 16 tokens."""
+    lengths = [96, 45, 0, 130]
+    H = 2
+    print(f"case: prefill floor in one chunk g_min={g_min} D={D}", flush=True)
+    inp = make_inputs(sum(lengths), H, D, seed=261 + D, lengths=lengths, initial_state=True)
+    g = np.zeros_like(inp.g)
+    cu = inp.cu_seqlens
+    for n in range(len(lengths)):
+        t = np.arange(cu[n + 1] - cu[n])
+        first = (t % 32) < 16            # a block's first chunk (blocks start at each sequence's start)
+        g[cu[n]:cu[n + 1], :, 0::2] = np.where(first, g_min, 0.0)[:, None, None]
+        g[cu[n]:cu[n + 1], :, 1::2] = np.where(first, 0.0, g_min)[:, None, None]
+    g = g.astype(np.float32)
+    o, fin, ck = kda.prefill(to_dev(inp.q, torch.bfloat16), to_dev(inp.k, torch.bfloat16),
+                             to_dev(inp.v, torch.bfloat16), to_dev(g), to_dev(inp.beta),
+                             cu_seqlens=inp.cu_seqlens, initial_state=to_dev(inp.initial_state),
+                             g_min=g_min, ckpt_interval=16)
+    torch.cuda.synchronize()
+    o_ref, f_ref, ck_ref = reference.prefill(inp.q, inp.k, inp.v, g, inp.beta, cu_seqlens=inp.cu_seqlens,
+                                             initial_state=inp.initial_state, g_min=g_min, ckpt_interval=16)
     check_outputs(_host(o), o_ref, inp.cu_seqlens, H)
     check_states(fin.cpu().numpy(), f_ref, "final")
     check_states(ck.cpu().numpy(), ck_ref, "checkpoint")
@@ -221,7 +253,7 @@ def _sweep_case(i):
         ckpt=int(rng.choice([0, 16, 32, 48, 64, 96])),
         initial=bool(rng.integers(0, 2)),
         g_scale=float(rng.choice([1.0, 1.0 / 16, 1.0 / 256])),
-        g_min=float(rng.choice([LN_HALF, LN_HALF, -1.5, -2.5])),
+        g_min=float(rng.choice([LN_HALF, LN_HALF, -1.5, -2.5, -5.0])),
         segments=segments,
         scale=float(rng.choice([1.0, 0.5])),
     )
@@ -240,8 +272,22 @@ def _sweep_case_many_slices(i):
     return c
 
 
+def _sweep_case_windows(i):
+    """Record windows of 1 to 8 blocks (a workspace sized for them), with
+    sequences long enough to span several windows."""
+    rng = np.random.default_rng(7000 + i)
+    c = _sweep_case(200 + i)
+    N = int(rng.integers(1, 5))
+    c["lengths"] = [int(x) for x in rng.choice([0, 1, 17, 33, 95, 130, 257, 400, 700], size=N)]
+    if sum(c["lengths"]) == 0:
+        c["lengths"][0] = 300
+    c["window"] = int(rng.choice([1, 2, 3, 5, 8]))
+    return c
+
+
 def _run_sweep_case(seed, c):
-    """One sweep case through kda_prefill_chunked_ex against the oracle."""
+    """One sweep case through kda_prefill_chunked_ex against the oracle (with
+    a workspace for record windows of c["window"] blocks, if given)."""
     lengths, H, D = c["lengths"], c["H"], c["D"]
     inp = make_inputs(sum(lengths), H, D, seed=seed, lengths=lengths, initial_state=c["initial"],
                       bf16=c["bf16"], g_scale=c["g_scale"])
@@ -251,10 +297,13 @@ def _run_sweep_case(seed, c):
     gv = _gate_arg(g, c["gate"])
     dt = torch.bfloat16 if c["bf16"] else torch.float32
     opt = kda.Options(gate=c["gate"], segments=c["segments"])
+    plan = None
+    if c.get("window"):
+        plan = kda.make_plan(inp.cu_seqlens, H, D, DEV, c["ckpt"], window_blocks=c["window"])
     o, fin, ck = kda.prefill(to_dev(inp.q, dt), to_dev(inp.k, dt), to_dev(inp.v, dt),
                              None if gv is None else to_dev(gv), to_dev(inp.beta), cu_seqlens=inp.cu_seqlens,
                              initial_state=None if inp.initial_state is None else to_dev(inp.initial_state),
-                             scale=c["scale"], g_min=c["g_min"], ckpt_interval=c["ckpt"], options=opt)
+                             scale=c["scale"], g_min=c["g_min"], ckpt_interval=c["ckpt"], options=opt, plan=plan)
     torch.cuda.synchronize()
     gc = var_oracle.gate_per_channel(gv, c["gate"], inp.q.shape)
     o_ref, f_ref, ck_ref = reference.prefill(inp.q, inp.k, inp.v, gc, inp.beta, cu_seqlens=inp.cu_seqlens,
@@ -280,3 +329,10 @@ def test_seeded_sweep_many_slices(i):
     c = _sweep_case_many_slices(i)
     print(f"case: sweep (many slices) {i} N={len(c['lengths'])} {c}", flush=True)
     _run_sweep_case(4100 + i, c)
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_seeded_sweep_record_windows(i):
+    c = _sweep_case_windows(i)
+    print(f"case: sweep (record windows) {i} {c}", flush=True)
+    _run_sweep_case(4200 + i, c)

@@ -34,9 +34,9 @@ def write_counters(d, rows):
 
 
 PLAN = "kda::plan_kernel(int const*, int)"
-PREP = "void kda::prep_kernel<128, unsigned short, false>(unsigned short const*)"
-PREP_GEN = "void kda::prep_kernel<128, unsigned short, true>(unsigned short const*)"
-CHAIN = "void kda::chain_kernel<128, unsigned short, 1>(unsigned short const*)"
+PREP = "void kda::prep_kernel<128, unsigned short, false, false>(unsigned short const*)"
+PREP_GEN = "void kda::prep_kernel<128, unsigned short, true, false>(unsigned short const*)"
+CHAIN = "void kda::chain_kernel<128, unsigned short, 1, false>(unsigned short const*)"
 ABS = "void at::native::vectorized_elementwise_kernel<4, at::native::AbsFunctor<float>>(int)"
 
 
@@ -44,9 +44,9 @@ def test_traffic_summary_scales_by_the_calibration_kernel(tmp_path):
     f, w = str(tmp_path / "f"), str(tmp_path / "w")
     # a call of two record windows: plan once, prep on two grids, chain twice
     P1, P2, C = 32 * 683 * 128, 32 * 681 * 128, 256 * 448
-    kernels = ((("kda::plan_kernel", 1024), 1), (("kda::prep_kernel<128, unsigned short, false>", P1), 1),
-               (("kda::prep_kernel<128, unsigned short, false>", P2), 1),
-               (("kda::chain_kernel<128, unsigned short, 1>", C), 2))
+    kernels = ((("kda::plan_kernel", 1024), 1), (("kda::prep_kernel<128, unsigned short, false, false>", P1), 1),
+               (("kda::prep_kernel<128, unsigned short, false, false>", P2), 1),
+               (("kda::chain_kernel<128, unsigned short, 1, false>", C), 2))
     # the calibration kernel reads and writes 256 MiB; the counters read half
     # of that for FETCH_SIZE and all of it for WRITE_SIZE
     write_counters(f, [(ABS, "FETCH_SIZE", 128 * 1024), (PLAN, "FETCH_SIZE", 1, 1024), (PREP, "FETCH_SIZE", 1000, P1),
@@ -61,7 +61,7 @@ def test_traffic_summary_scales_by_the_calibration_kernel(tmp_path):
     # each chain dispatch the mean of its two samples, two chain dispatches per call
     want = (2 * (1 + 1000 + 900 + 2 * 3000) + (1 + 300 + 200 + 2 * 100)) * 1024
     assert res["bytes_per_call"] == pytest.approx(want)
-    assert [r[0][0] for r in res["others"]] == ["kda::prep_kernel<128, unsigned short, true>"]
+    assert [r[0][0] for r in res["others"]] == ["kda::prep_kernel<128, unsigned short, true, false>"]
     text = P.render(res, 256, ["cmd"], 1000)
     assert "| 2 | " in text   # the chain's dispatches per call
 
@@ -95,8 +95,8 @@ def test_mfma_busy_uses_one_xcd_of_active_cycles(tmp_path):
                        ("void (anonymous namespace)::mfma_loop<1>(float*, int)", "SQ_INSTS_VALU_MFMA_MOPS_BF16", 0),
                        ("void (anonymous namespace)::mfma_loop<1>(float*, int)", "GRBM_GUI_ACTIVE", 8000)])
     rows = {r[0]: r for r in P.mfma_summary(d)}
-    assert rows["kda::chain_kernel<128, unsigned short, 1>"][3] == pytest.approx(50.0)
-    assert rows["kda::chain_kernel<128, unsigned short, 1>"][4] == pytest.approx(2e6 * 512 / 1e9)
+    assert rows["kda::chain_kernel<128, unsigned short, 1, false>"][3] == pytest.approx(50.0)
+    assert rows["kda::chain_kernel<128, unsigned short, 1, false>"][4] == pytest.approx(2e6 * 512 / 1e9)
     assert rows["mfma_loop<1> (reference loop)"][3] == pytest.approx(100.0)
 
 
@@ -107,20 +107,20 @@ def test_prefill_grids_follow_the_shape():
     assert P.prefill_windows(1, 32, 256) == [256]
     assert P.prefill_windows(16, 32, 2756) == [2756]
     long = dict(P.WORKLOADS["prefill"][0])
-    assert long[("kda::prep_kernel<128, unsigned short, false>", 32 * 683 * 128)] == 5
-    assert long[("kda::prep_kernel<128, unsigned short, false>", 32 * 681 * 128)] == 1
-    assert long[("kda::chain_kernel<128, unsigned short, 1>", 256 * 448)] == 6
+    assert long[("kda::prep_kernel<128, unsigned short, false, false>", 32 * 683 * 128)] == 5
+    assert long[("kda::prep_kernel<128, unsigned short, false, false>", 32 * 681 * 128)] == 1
+    assert long[("kda::chain_kernel<128, unsigned short, 1, false>", 256 * 448)] == 6
     assert long[("kda::plan_kernel", 1024)] == 1
     short = dict(P.WORKLOADS["prefill_8k"][0])
-    assert short[("kda::prep_kernel<128, unsigned short, false>", 32 * 256 * 128)] == 1
-    assert short[("kda::chain_kernel<128, unsigned short, 1>", 256 * 448)] == 1
+    assert short[("kda::prep_kernel<128, unsigned short, false, false>", 32 * 256 * 128)] == 1
+    assert short[("kda::chain_kernel<128, unsigned short, 1, false>", 256 * 448)] == 1
     # 16 sequences x 32 heads: 512 units (4096 slices, more than the CUs), 64
     # groups of 8 units x 4 two-slice workgroups of 512 threads
-    assert dict(P.prefill_kernels(32, 2756, 512))[("kda::chain_kernel<128, unsigned short, 2>", 2048 * 512)] == 1
+    assert dict(P.prefill_kernels(32, 2756, 512))[("kda::chain_kernel<128, unsigned short, 2, false>", 2048 * 512)] == 1
 
 
 def test_kernel_key_keeps_template_arguments():
-    assert P.kernel_key(CHAIN) == "kda::chain_kernel<128, unsigned short, 1>"
+    assert P.kernel_key(CHAIN) == "kda::chain_kernel<128, unsigned short, 1, false>"
     assert P.kernel_key(PLAN) == "kda::plan_kernel"
 
 
