@@ -1001,3 +1001,56 @@ def test_windowed_long_prefill_full_size():
     del win
     _, win2 = _windowed_pair(q, k, v, g, beta, cu, None, I, 2048)
     _assert_identical(one, win2, "2 windows")
+
+
+def test_windowed_call_replays_from_a_captured_graph():
+    """A call in record windows of 5 blocks (several prep and chain launches,
+    carried states) captured in a graph replays to exactly the eager call's
+    results on new inputs each time."""
+    lengths = [300, 0, 530, 77]
+    T, H, D = sum(lengths), 3, 128
+    cu = [0]
+    for x in lengths:
+        cu.append(cu[-1] + x)
+    print(f"case: graph capture of a windowed call lengths={lengths}", flush=True)
+    plan = kda.make_plan(cu, H, D, DEV, ckpt_interval=48, window_blocks=5)
+    bufs = {n: torch.empty(T, H, D, dtype=torch.bfloat16, device=DEV) for n in ("q", "k", "v")}
+    g = torch.empty(T, H, D, device=DEV)
+    beta = torch.empty(T, H, device=DEV)
+    s0 = torch.empty(len(lengths), H, D, D, device=DEV)
+    o = torch.empty(T, H, D, dtype=torch.bfloat16, device=DEV)
+    fin = torch.empty(len(lengths), H, D, D, device=DEV)
+    ck = torch.empty(plan.num_ckpt, H, D, D, device=DEV)
+
+    def load(seed):
+        inp = make_inputs(T, H, D, seed=seed, lengths=lengths, initial_state=True)
+        for n, x in (("q", inp.q), ("k", inp.k), ("v", inp.v)):
+            bufs[n].copy_(to_dev(x, torch.bfloat16))
+        g.copy_(to_dev(inp.g))
+        beta.copy_(to_dev(inp.beta))
+        s0.copy_(to_dev(inp.initial_state))
+
+    def call():
+        kda.prefill(bufs["q"], bufs["k"], bufs["v"], g, beta, initial_state=s0, plan=plan, o=o, final_state=fin,
+                    checkpoints=ck)
+
+    load(700)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for seed in (701, 702, 703):
+        load(seed)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (o.clone(), fin.clone(), ck.clone())
+        _ = torch.randn(1 << 20, device=DEV).sum()          # unrelated eager work
+        call()
+        torch.cuda.synchronize()
+        for x, y in zip(got, (o, fin, ck)):
+            assert torch.equal(x, y), f"replay with inputs {seed} differs from the eager call"

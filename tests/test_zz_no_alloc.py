@@ -93,3 +93,50 @@ def test_noalloc_refuses_shapes_beyond_the_scratch():
     with pytest.raises(kda.KdaError) as e:
         kda.prefill(q, k, v, g, beta, cu_seqlens=cu, noalloc=True)
     assert e.value.status == kda.KDA_ERR_WORKSPACE
+
+
+def test_noalloc_windowed_call_replays_from_a_captured_graph():
+    """The allocation-free entry point captured in a graph, on a shape whose
+    records exceed the scratch (8192 tokens x 32 heads: record windows):
+    every replay equals the eager call on the same inputs bit for bit."""
+    T, H, D = 8192, 32, 128
+    print(f"case: noalloc graph capture T={T} H={H}", flush=True)
+    plan = kda.make_plan([0, T], H, D, DEV, ckpt_interval=1024, workspace=False)
+    bufs = {n: torch.empty(T, H, D, dtype=torch.bfloat16, device=DEV) for n in ("q", "k", "v")}
+    g = torch.empty(T, H, D, device=DEV)
+    beta = torch.empty(T, H, device=DEV)
+    o = torch.empty(T, H, D, dtype=torch.bfloat16, device=DEV)
+    fin = torch.empty(1, H, D, D, device=DEV)
+    ck = torch.empty(plan.num_ckpt, H, D, D, device=DEV)
+
+    def load(seed):
+        q, k, v, gg, bb, _, _ = make_inputs_device(T, H, D, seed=seed, device=DEV)
+        for n, x in (("q", q), ("k", k), ("v", v)):
+            bufs[n].copy_(x)
+        g.copy_(gg)
+        beta.copy_(bb)
+
+    def call():
+        kda.prefill(bufs["q"], bufs["k"], bufs["v"], g, beta, plan=plan, o=o, final_state=fin, checkpoints=ck,
+                    noalloc=True)
+
+    load(310)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for seed in (311, 312):
+        load(seed)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (o.clone(), fin.clone(), ck.clone())
+        _ = torch.randn(1 << 20, device=DEV).sum()          # unrelated eager work
+        call()
+        torch.cuda.synchronize()
+        for x, y in zip(got, (o, fin, ck)):
+            assert torch.equal(x, y), f"replay with inputs {seed} differs from the eager call"
