@@ -234,6 +234,10 @@ def bench_prefill_long(args, dev, flush):
         "wall_s_timed_steps": round(wall, 4),
         "prefill_tflops": round(flops / (ev_ms * 1e-3) / 1e12, 2),
         "prefill_mfma_frac_of_peak": round(flops / (ev_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        "prefill_workspace": {"bytes": plan.workspace.numel(),
+                              "record_windows": len(profiling.prefill_windows(1, H, T // 32)),
+                              "note": "kda_prefill_workspace_size: one sequence runs in record windows "
+                                      "of about 1 GiB"},
     }
     return rec, (q, k, v, g, beta)
 
