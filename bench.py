@@ -307,6 +307,26 @@ def bench_varlen(args, dev, flush):
         sum(vl), H, D, vts, n_seqs=len(vl), init=True)}
 
 
+def bench_prefill_1m(args, dev, flush):
+    """B=1, H=32, T=1,048,576 (the pages' 1M-token context), D=128, a
+    checkpoint every 262,144 tokens, with the library's default workspace:
+    the records run in windows of about 1 GiB, so the workspace stays near
+    1.1 GB where all records at once would take 50 GB."""
+    T, H, D, CK = 1 << 20, 32, 128, 1 << 18
+    q, k, v, g, beta, cu, _ = make_inputs_device(T, H, D, seed=8, device=dev)
+    plan = kda.make_plan(cu, H, D, dev, ckpt_interval=CK)
+    o = torch.empty_like(v)
+    fin = torch.empty(1, H, D, D, dtype=torch.float32, device=dev)
+    ck = torch.empty(T // CK, H, D, D, dtype=torch.float32, device=dev)
+    _, ts = time_events(lambda: kda.prefill(q, k, v, g, beta, plan=plan, o=o, final_state=fin, checkpoints=ck),
+                        3, 1, flush)
+    rec = prefill_record(f"B=1, H=32, T={T}, D=128, checkpoint every {CK} (1M-token context)", T, H, D, ts,
+                         n_ckpt=T // CK)
+    rec["workspace_bytes"] = plan.workspace.numel()
+    rec["record_windows"] = len(profiling.prefill_windows(1, H, T // 32))
+    return {"prefill_1m": rec}
+
+
 def bench_decode(args, dev, flush):
     """256 sequences x 32 heads, D=128: one token per call, and 4 per call."""
     N, H, D = 256, 32, 128
@@ -362,10 +382,11 @@ def main():
     ap.add_argument("--calibrate", type=int, default=0, metavar="MIB",
                     help="before timing, run torch.abs over a float32 tensor of MIB MiB (a kernel of known "
                          "size for calibrating rocprofv3 byte counters)")
-    ap.add_argument("--only", choices=("all", "prefill", "prefill_8k", "varlen", "decode"), default="all",
+    ap.add_argument("--only", choices=("all", "prefill", "prefill_8k", "varlen", "decode", "prefill_1m"),
+                    default="all",
                     help="run only the benchmarked long prefill (and the measured peaks), only the "
-                         "8192-token prefill, only the varlen append-prefill, or only decode (for "
-                         "counter passes that must see one workload)")
+                         "8192-token prefill, only the varlen append-prefill, only decode, or only the "
+                         "1M-token prefill (for counter passes that must see one workload)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -403,6 +424,11 @@ def main():
     if args.only in ("all", "decode"):
         rec.update(bench_decode(args, dev, flush))
         print("bench: decode done", file=sys.stderr, flush=True)
+    torch.cuda.empty_cache()
+    if args.only in ("all", "prefill_1m"):
+        rec.update(bench_prefill_1m(args, dev, flush))
+        torch.cuda.empty_cache()
+        print("bench: 1M-token prefill done", file=sys.stderr, flush=True)
     if args.only in ("all", "prefill"):
         rec["measured_peaks"] = measured_peaks(dev, flush)
     print(json.dumps(rec), flush=True)

@@ -1054,3 +1054,27 @@ def test_windowed_call_replays_from_a_captured_graph():
         torch.cuda.synchronize()
         for x, y in zip(got, (o, fin, ck)):
             assert torch.equal(x, y), f"replay with inputs {seed} differs from the eager call"
+
+
+@pytest.mark.timeout(400)
+def test_million_token_prefill_sampled_heads():
+    """The pages' 1M-token context: B=1, H=32, T=1,048,576, D=128, a
+    checkpoint every 262,144 tokens, with the library's default workspace
+    (records in windows of about 1 GiB: 48 windows, 1.1 GB instead of 50 GB).
+    Heads 0, 13 and 31 against the oracle (outputs, checkpoints, final state);
+    every head finite."""
+    T, H, D, I = 1 << 20, 32, 128, 1 << 18
+    print("case: B=1 H=32 T=1048576 checkpoint every 262144", flush=True)
+    q, k, v, g, beta, cu, _ = make_inputs_device(T, H, D, seed=461, device=DEV)
+    plan = kda.make_plan(cu, H, D, DEV, I)
+    assert plan.workspace.numel() < 1.2e9
+    o, fin, ck = kda.prefill(q, k, v, g, beta, plan=plan)
+    torch.cuda.synchronize()
+    assert torch.isfinite(fin).all() and torch.isfinite(ck).all()
+    assert torch.equal(ck[3], fin[0])
+    heads = [0, 13, 31]
+    print(f"  oracle heads {heads} over {T} tokens", flush=True)
+    o_ref, f_ref, ck_ref = _sampled_heads_oracle(q, k, v, g, beta, cu, None, heads, ckpt=I)
+    check_outputs(o[:, heads].float().cpu().numpy(), o_ref, cu.numpy(), len(heads))
+    check_states(fin[:, heads].cpu().numpy(), f_ref, "final")
+    check_states(ck[:, heads].cpu().numpy(), ck_ref, "checkpoint")
