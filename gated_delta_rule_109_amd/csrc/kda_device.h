@@ -65,11 +65,9 @@ __device__ __forceinline__ float inv_norm(float sumsq, float eps) {
 }
 
 // ---- bf16 operand packing -----------------------------------------------------
-__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
-  bf16x4 r;
-  r[0] = (__bf16)x[0]; r[1] = (__bf16)x[1]; r[2] = (__bf16)x[2]; r[3] = (__bf16)x[3];
-  return r;
-}
+// Round-to-nearest-even fp32 -> bf16 of four values, as two packed
+// conversions (v_cvt_pk_bf16_f32 takes a pair of values).
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
 __device__ __forceinline__ f32x4 from_bf16x4(bf16x4 x) {
   f32x4 r;
   r[0] = (float)x[0]; r[1] = (float)x[1]; r[2] = (float)x[2]; r[3] = (float)x[3];
