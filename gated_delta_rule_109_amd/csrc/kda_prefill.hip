@@ -1301,7 +1301,13 @@ __global__ __launch_bounds__((ChainCfg<D, TIn, NSL>::kThreads)) void chain_kerne
       // state for this block's update and the next block's T and V
       f32x4 accd[TW];
 #pragma unroll
-      for (int t = 0; t < TW; ++t) accd[t] = acc[t] * pc[t];
+      for (int t = 0; t < TW; ++t) {
+        accd[t] = acc[t] * pc[t];
+        // keeps the products here, under the delta MFMAs (the compiler would
+        // otherwise sink them past the checkpoint branch, in front of the
+        // update's MFMAs); an empty statement, no instruction
+        asm volatile("" : "+v"(accd[t]));
+      }
       read_tv(nslot);
       bf16x4 dh0, dlo0, dh1, dlo1;
       split_bf16(dl[0], dh0, dlo0);
