@@ -84,7 +84,9 @@ constexpr int kBT = kBlockTokens;   // tokens per block (two chunks)
 static_assert(plan::kBT == kBlockTokens, "one block size");
 
 // ---- record layout ----------------------------------------------------------
-// One record per (block, head), stored head-major (record h * total_blocks + b);
+// One record per (block, head) of the current record window, stored
+// head-major (record h * window_blocks + b - c0 for block b of the window
+// [c0, c0 + window_blocks));
 // it is a sequence of 1 KiB fragments (one 16-byte-per-lane wave load each).
 // Two index orders appear in the fragments:
 //  - a 32-deep contraction over key channels (k block p) uses channel
