@@ -642,6 +642,24 @@ def test_prefill_all_sequences_empty():
     _, fin0, _ = kda.prefill(q, q, q, z(0, H, D), z(0, H), cu_seqlens=cu)
     torch.cuda.synchronize()
     assert not fin0.abs().any()
+    # with no blocks (and too many sequence-head pairs for segment states)
+    # the call needs its tables only: a 4 KiB workspace is enough, 16 bytes
+    # are refused
+    H2 = 12
+    q2 = torch.zeros(0, H2, D, dtype=torch.bfloat16, device=DEV)
+    s2 = np.random.default_rng(4).standard_normal((3, H2, D, D)).astype(np.float32)
+    plan = kda.make_plan(cu, H2, D, DEV)
+    for nbytes, ok in ((4096, True), (16, False)):
+        small = kda.PrefillPlan(plan.cu_host, plan.cu_dev, plan.workspace[:nbytes], 0, 0)
+        args = (q2, q2, q2, z(0, H2, D), z(0, H2))
+        if ok:
+            _, fin1, _ = kda.prefill(*args, initial_state=to_dev(s2), plan=small)
+            torch.cuda.synchronize()
+            assert np.array_equal(fin1.cpu().numpy(), s2)
+        else:
+            with pytest.raises(kda.KdaError) as e:
+                kda.prefill(*args, initial_state=to_dev(s2), plan=small)
+            assert e.value.status == kda.KDA_ERR_WORKSPACE
 
 
 def test_decode_large_batch_sampled():
