@@ -3,6 +3,7 @@
 // unless every argument checks out.
 #include "kda.h"
 #include "kda_internal.h"
+#include "kda_plan.h"
 
 #include <float.h>
 #include <limits.h>
@@ -189,18 +190,15 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, int dtype, 
   }
   if (use_scratch) workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
   // (every sequence empty: no records, the tables only)
-  int64_t window = blocks;
+  int64_t window = 1;
   if (blocks == 0) {
     if (workspace_bytes < kda::prefill_layout(num_seqs, 0, H, Dk, 0, false).total) return KDA_ERR_WORKSPACE;
-  } else if (blocks > max_window ||
-             workspace_bytes < kda::prefill_layout(num_seqs, blocks, H, Dk, window, false).total) {
-    const size_t fixed = kda::prefill_layout(num_seqs, blocks, H, Dk, 0, true).total;
-    if (workspace_bytes < fixed) return KDA_ERR_WORKSPACE;
-    window = (int64_t)((workspace_bytes - fixed) / rec_bytes);
+  } else {
+    window = kda::plan::choose_window(blocks, workspace_bytes,
+                                      kda::prefill_layout(num_seqs, blocks, H, Dk, blocks, false).total,
+                                      kda::prefill_layout(num_seqs, blocks, H, Dk, 0, true).total, rec_bytes,
+                                      max_window);
     if (window < 1) return KDA_ERR_WORKSPACE;
-    window = window < max_window ? window : max_window;
-    const int64_t nwin = (blocks + window - 1) / window;
-    window = (blocks + nwin - 1) / nwin;
   }
   if (use_scratch) {
     // the scratch of the device the work runs on: the stream's, which must be
@@ -216,7 +214,7 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, int dtype, 
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
   a.cu_seqlens = cu_seqlens; a.cu_seqlens_host = cu_seqlens_host;
   a.num_seqs = num_seqs; a.H = H; a.D = Dk;
-  a.total_tokens = tokens; a.total_blocks = blocks; a.window_blocks = window > 0 ? window : 1;
+  a.total_tokens = tokens; a.total_blocks = blocks; a.window_blocks = window;
   a.num_checkpoints = nck > 0 ? nck : 0;
   a.scale = scale; a.g_min = g_min;
   a.fe_flags = opt ? opt->flags : 0u; a.fe_eps = opt ? opt->norm_eps : 0.f;

@@ -119,6 +119,22 @@ __host__ __device__ inline void part_segment(int np, int seg, int P, int& b0, in
   b1 = b0 + bps < np ? b0 + bps : np;
 }
 
+// Blocks per record window for a call of blocks >= 1 blocks: all of them if
+// they fit the workspace at once (one_window_bytes: tables and every record)
+// and blocks <= max_window; else as many as fit beside fixed_bytes (tables
+// and carry states) at block_bytes each (a block of every head), at most
+// max_window, evened out over the windows. 0 if not one block fits.
+inline int64_t choose_window(int64_t blocks, uint64_t workspace_bytes, uint64_t one_window_bytes,
+                             uint64_t fixed_bytes, uint64_t block_bytes, int64_t max_window) {
+  if (blocks <= max_window && workspace_bytes >= one_window_bytes) return blocks;
+  if (workspace_bytes < fixed_bytes || block_bytes == 0) return 0;
+  int64_t w = (int64_t)((workspace_bytes - fixed_bytes) / block_bytes);
+  if (w < 1) return 0;
+  w = w < max_window ? w : max_window;
+  const int64_t nwin = (blocks + w - 1) / w;
+  return (blocks + nwin - 1) / nwin;
+}
+
 // Host walk over the windows in order, from the host copy of cu_seqlens
 // (exact per-sequence block counts, so the offsets need no table): calls
 // visit(w, c0, c1, first, count, longest) for every window, with the window's

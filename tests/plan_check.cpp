@@ -11,7 +11,10 @@
 //   - with copies that differ (shifted, shuffled, negative, past the total,
 //     decreasing) every record, row, checkpoint slot and order-table entry
 //     touched stays inside what the host copy sized, and at most one
-//     sequence crosses each window edge.
+//     sequence crosses each window edge;
+// and that the window a call takes from its workspace (choose_window) fits
+// it, respects the largest window, is evened out, and is refused only when
+// not one block fits.
 // The plan kernel's scan is a parallel prefix sum with plan::sat_add, which is
 // associative on nonnegative values, so the sequential prefix here is what it
 // computes.
@@ -19,6 +22,7 @@
 #define __device__
 #include "../gated_delta_rule_109_amd/csrc/kda_plan.h"
 
+#include <algorithm>
 #include <stdio.h>
 #include <stdlib.h>
 #include <vector>
@@ -243,8 +247,43 @@ static long run_case(const std::vector<int32_t>& host, const std::vector<int32_t
   return checks;
 }
 
+// The record window a call takes from its workspace (choose_window): one
+// window when everything fits, else the most blocks that fit beside the
+// tables and carry states, evened out, never past max_window, and 0 only
+// when not one block fits.
+static long check_windows() {
+  long checks = 0;
+  for (int it = 0; it < 200000; ++it) {
+    const int64_t blocks = rint_in(1, 6000);
+    const uint64_t block_bytes = (uint64_t)rint_in(1, 1 << 20);
+    const uint64_t tables = (uint64_t)rint_in(0, 1 << 16), carry = (uint64_t)rint_in(0, 1 << 20);
+    const uint64_t one = tables + (uint64_t)blocks * block_bytes, fixed = tables + carry;
+    const int64_t max_window = it % 3 == 0 ? 65535 : rint_in(1, 8000);
+    const uint64_t ws = it % 5 == 0 ? one : (uint64_t)((double)(rnd() % 1000) / 500.0 * (double)one);
+    const int64_t w = choose_window(blocks, ws, one, fixed, block_bytes, max_window);
+    if (blocks <= max_window && ws >= one) {
+      CHECK(w == blocks, "one window: %lld of %lld", (long long)w, (long long)blocks);
+    } else if (ws < fixed || (ws - fixed) / block_bytes < 1) {
+      CHECK(w == 0, "nothing fits, got %lld", (long long)w);
+    } else {
+      const int64_t raw = std::min<int64_t>((int64_t)((ws - fixed) / block_bytes), max_window);
+      const int64_t nwin = (blocks + w - 1) / w;
+      CHECK(w >= 1 && w <= max_window && w <= raw, "window %lld (raw %lld, max %lld)", (long long)w,
+            (long long)raw, (long long)max_window);
+      CHECK(fixed + (uint64_t)w * block_bytes <= ws, "window %lld does not fit", (long long)w);
+      CHECK(w * (nwin - 1) < blocks && blocks <= w * nwin, "windows of %lld over %lld blocks", (long long)w,
+            (long long)blocks);
+      CHECK(nwin == (blocks + raw - 1) / raw, "evening changed the window count");
+      CHECK(blocks - w * (nwin - 1) > w - nwin, "last window of %lld blocks, others %lld",
+            (long long)(blocks - w * (nwin - 1)), (long long)w);   // evened out
+    }
+    ++checks;
+  }
+  return checks;
+}
+
 int main() {
-  long checks = 0, cases = 0;
+  long checks = check_windows(), cases = 0;
   for (int it = 0; it < 4000; ++it) {
     const int N = rint_in(1, 12);
     const int mode = it % 8;
