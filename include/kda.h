@@ -118,8 +118,10 @@ typedef enum { KDA_GATE_CHANNEL = 0, KDA_GATE_HEAD = 1, KDA_GATE_NONE = 2 } kda_
  *           (its transition M_p);
  *   scan:   S_in(p) = M_{p-1} S_in(p-1) + local(p-1);
  *   pass 2: segments 1 .. P-1 run in full from S_in(p).
- * Each segment holds whole 32-token blocks. It pays when the chain would
- * otherwise leave most compute units idle: few sequences times heads. A
+ * Each segment holds whole 32-token blocks; a call in record windows (see
+ * kda_prefill_workspace_size) splits each window's part of a sequence. It
+ * pays when the chain would otherwise leave most compute units idle: few
+ * sequences times heads. A
  * value of 0 lets the library choose (1 for most shapes); 1 turns it off;
  * 2 .. KDA_MAX_SEGMENTS forces that many segments per sequence. Forcing is
  * accepted only where the workspace holds the segment states:
