@@ -1096,3 +1096,32 @@ def test_million_token_prefill_sampled_heads():
     check_outputs(o[:, heads].float().cpu().numpy(), o_ref, cu.numpy(), len(heads))
     check_states(fin[:, heads].cpu().numpy(), f_ref, "final")
     check_states(ck[:, heads].cpu().numpy(), ck_ref, "checkpoint")
+
+
+@pytest.mark.parametrize("window", [None, 3])
+def test_prefill_over_a_thousand_sequences(window):
+    """3000 short sequences (0 to 49 tokens) x 2 heads at D = 16, with cached
+    states and checkpoints every 16 tokens: the plan kernel's scans run over
+    several 1024-wide chunks and the chain takes the sequences in their given
+    order (past the 1024 it ranks); with windows of 3 blocks there are also
+    more than 1024 windows. Against the oracle, and the windowed call bit for
+    bit the one-window call."""
+    rng = np.random.default_rng(471)
+    lengths = [int(x) for x in rng.integers(0, 50, size=3000)]
+    H, D = 2, 16
+    print(f"case: {len(lengths)} sequences, {sum(lengths)} tokens, windows {window}", flush=True)
+    inp = make_inputs(sum(lengths), H, D, seed=472, lengths=lengths, initial_state=True)
+    q, k, v = (to_dev(x, torch.bfloat16) for x in (inp.q, inp.k, inp.v))
+    g, beta, s0 = to_dev(inp.g), to_dev(inp.beta), to_dev(inp.initial_state)
+    plan = kda.make_plan(inp.cu_seqlens, H, D, DEV, 16, window_blocks=window)
+    o, fin, ck = kda.prefill(q, k, v, g, beta, initial_state=s0, plan=plan)
+    torch.cuda.synchronize()
+    if window is not None:
+        one = kda.prefill(q, k, v, g, beta, cu_seqlens=inp.cu_seqlens, initial_state=s0, ckpt_interval=16)
+        torch.cuda.synchronize()
+        _assert_identical(one, (o, fin, ck), f"windows of {window}")
+        return
+    o_ref, f_ref, ck_ref = oracle(inp, ckpt=16)
+    check_outputs(o.float().cpu().numpy(), o_ref, inp.cu_seqlens, H)
+    check_states(fin.cpu().numpy(), f_ref, "final")
+    check_states(ck.cpu().numpy(), ck_ref, "checkpoint")
