@@ -1125,3 +1125,19 @@ def test_prefill_over_a_thousand_sequences(window):
     check_outputs(o.float().cpu().numpy(), o_ref, inp.cu_seqlens, H)
     check_states(fin.cpu().numpy(), f_ref, "final")
     check_states(ck.cpu().numpy(), ck_ref, "checkpoint")
+
+
+def test_single_sequence_48_heads_two_slice_windows():
+    """One sequence of 24,576 tokens x 48 heads at D = 128: 384 column slices,
+    so the chain runs two slices per workgroup, and the default workspace
+    holds about 1 GiB of records (two windows of 384 blocks). Heads 0 and 47
+    against the oracle; windows of 256 blocks bit for bit the same."""
+    T, H, D = 24576, 48, 128
+    print(f"case: B=1 H={H} T={T} (two-slice workgroups in record windows)", flush=True)
+    q, k, v, g, beta, cu, _ = make_inputs_device(T, H, D, seed=481, device=DEV)
+    one, win = _windowed_pair(q, k, v, g, beta, cu, None, 0, 256)
+    _assert_identical(one, win, "windows of 256")
+    heads = [0, 47]
+    o_ref, f_ref, _ = _sampled_heads_oracle(q, k, v, g, beta, cu, None, heads)
+    check_outputs(one[0][:, heads].float().cpu().numpy(), o_ref, cu.numpy(), len(heads))
+    check_states(one[1][:, heads].cpu().numpy(), f_ref, "final")
