@@ -1141,3 +1141,39 @@ def test_single_sequence_48_heads_two_slice_windows():
     o_ref, f_ref, _ = _sampled_heads_oracle(q, k, v, g, beta, cu, None, heads)
     check_outputs(one[0][:, heads].float().cpu().numpy(), o_ref, cu.numpy(), len(heads))
     check_states(one[1][:, heads].cpu().numpy(), f_ref, "final")
+
+
+def test_windowed_front_end_and_low_floor():
+    """Record windows of 3 blocks with the fused front end (raw q, k, gate and
+    write logits), bit for bit the one-window call; and the low-floor path
+    (g_min = -5, the floor in one 16-token chunk of every block) in windows
+    of 3 blocks with checkpoints every 16 tokens, against the oracle."""
+    lengths = [37, 0, 160, 1, 100, 64, 15, 97]
+    H, D = 3, 128
+    print(f"case: windows with the front end, lengths={lengths}", flush=True)
+    raw = make_inputs(sum(lengths), H, D, seed=491, lengths=lengths, initial_state=True, raw=True)
+    q, k, v = (to_dev(x, torch.bfloat16) for x in (raw.q, raw.k, raw.v))
+    one, win = _windowed_pair(q, k, v, to_dev(raw.g), to_dev(raw.beta), raw.cu_seqlens,
+                              to_dev(raw.initial_state), 32, 3, kda.Options(kda.FE_ALL, FE_EPS, segments=1))
+    _assert_identical(one, win, "front end in windows of 3")
+
+    print("case: windows with the low-floor path, g_min = -5", flush=True)
+    inp = make_inputs(sum(lengths), H, D, seed=492, lengths=lengths, initial_state=True)
+    g = np.zeros_like(inp.g)
+    cu = inp.cu_seqlens
+    for n in range(len(lengths)):
+        t = np.arange(cu[n + 1] - cu[n])
+        first = (t % 32) < 16
+        g[cu[n]:cu[n + 1], :, 0::2] = np.where(first, -5.0, 0.0)[:, None, None]
+        g[cu[n]:cu[n + 1], :, 1::2] = np.where(first, 0.0, -5.0)[:, None, None]
+    g = g.astype(np.float32)
+    plan = kda.make_plan(cu, H, D, DEV, 16, window_blocks=3)
+    o, fin, ck = kda.prefill(to_dev(inp.q, torch.bfloat16), to_dev(inp.k, torch.bfloat16),
+                             to_dev(inp.v, torch.bfloat16), to_dev(g), to_dev(inp.beta),
+                             initial_state=to_dev(inp.initial_state), g_min=-5.0, plan=plan)
+    torch.cuda.synchronize()
+    o_ref, f_ref, ck_ref = reference.prefill(inp.q, inp.k, inp.v, g, inp.beta, cu_seqlens=cu,
+                                             initial_state=inp.initial_state, g_min=-5.0, ckpt_interval=16)
+    check_outputs(o.float().cpu().numpy(), o_ref, cu, H)
+    check_states(fin.cpu().numpy(), f_ref, "final")
+    check_states(ck.cpu().numpy(), ck_ref, "checkpoint")
