@@ -334,8 +334,8 @@ __global__ __launch_bounds__(prep_threads<D>()) void prep_kernel(
   // One LDS area, used twice: P[r][ch] (fp32, rows padded by 16 bytes) and
   // the k rows during phases 1-2; then A and the blocks of T. A is written
   // only after every wave has finished reading P and k, so the two uses never
-  // overlap, and the smaller footprint lets six workgroups share a compute
-  // unit instead of five.
+  // overlap, and the smaller footprint leaves LDS for six workgroups per
+  // compute unit (the registers allow four; six measured no faster).
   constexpr int kPBytes = kBT * (D + 4) * 4;
   constexpr int kKPad = 16 / (int)sizeof(TIn);                   // 16-byte row padding
   constexpr int kKBytes = kBT * (D + kKPad) * (int)sizeof(TIn);
