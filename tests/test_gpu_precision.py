@@ -282,6 +282,8 @@ def _sweep_case_windows(i):
     if sum(c["lengths"]) == 0:
         c["lengths"][0] = 300
     c["window"] = int(rng.choice([1, 2, 3, 5, 8]))
+    if c["segments"] > 1 and N * c["H"] * (c["D"] // 16) > kda.SEGMENT_SLICE_LIMIT:
+        c["segments"] = 0    # the new sequence count must still allow forced segments
     return c
 
 
