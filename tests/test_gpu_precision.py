@@ -9,12 +9,17 @@ the fp64 oracle, every (sequence, head) compared:
   - gates outside [g_min, 0] (both signs, far below the floor), which every
     entry point clamps on load;
   - decay floors below ln 1/2 with half the channels on the floor;
-  - a seeded sweep over lengths, heads, head size, storage type, gate layout,
-    checkpoint interval, initial states and gate scale.
+  - seeded sweeps over lengths, heads, head size, storage type, gate layout,
+    checkpoint interval, initial states, gate scale, floors, segments and
+    record windows, and over decode calls (sequences, tokens, accept
+    lengths, unclamped gates, floors). KDA_SWEEP_EXTRA=n adds n more seeds
+    to every sweep (indices from 1000 on).
 
 Tolerances as in test_gpu_parity.py: outputs 2e-2 and fp32 states 1e-3,
 relative to the largest reference value per (sequence, head).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -28,6 +33,12 @@ from test_gpu_parity import DEV, O_TOL, check_outputs, check_states, rel_err, to
 pytestmark = pytest.mark.gpu
 
 GATE_VALUES = np.array([-5.0, -1.0, -0.3, 0.0, 0.375], np.float32)
+SWEEP_EXTRA = int(os.environ.get("KDA_SWEEP_EXTRA", "0"))
+
+
+def _seeds(n):
+    """Sweep indices: the first n, plus KDA_SWEEP_EXTRA more from 1000 on."""
+    return list(range(n)) + list(range(1000, 1000 + SWEEP_EXTRA))
 
 
 def _options(gate):
@@ -287,6 +298,36 @@ def _sweep_case_windows(i):
     return c
 
 
+def _sweep_case_large(i):
+    """Up to 40 sequences of lognormal lengths (median 200 tokens, up to
+    3000, some empty), up to 8 heads, with floors down to -5, segments and
+    record windows of 1 to 64 blocks drawn independently."""
+    rng = np.random.default_rng(9000 + i)
+    N = int(rng.integers(1, 41))
+    lengths = [int(x) for x in np.clip(np.round(rng.lognormal(np.log(200), 1.2, size=N)), 0, 3000)]
+    lengths = [0 if rng.random() < 0.1 else x for x in lengths]
+    if sum(lengths) == 0:
+        lengths[0] = 77
+    H, D = int(rng.integers(1, 9)), int(rng.choice([16, 128, 128]))
+    segments = int(rng.choice([0, 0, 0, 1, 2, 4]))
+    if segments > 1 and N * H * (D // 16) > kda.SEGMENT_SLICE_LIMIT:
+        segments = 0
+    return dict(
+        lengths=lengths,
+        H=H,
+        D=D,
+        bf16=bool(rng.integers(0, 2)),
+        gate=int(rng.choice([kda.GATE_CHANNEL, kda.GATE_CHANNEL, kda.GATE_HEAD, kda.GATE_NONE])),
+        ckpt=int(rng.choice([0, 16, 32, 48, 80, 256])),
+        initial=bool(rng.integers(0, 2)),
+        g_scale=float(rng.choice([1.0, 1.0 / 16, 1.0 / 256])),
+        g_min=float(rng.choice([LN_HALF, LN_HALF, -1.0, -2.5, -3.0, -5.0])),
+        segments=segments,
+        scale=float(rng.choice([1.0, 0.5])),
+        window=int(rng.choice([0, 0, 1, 4, 16, 64])),
+    )
+
+
 def _run_sweep_case(seed, c):
     """One sweep case through kda_prefill_chunked_ex against the oracle (with
     a workspace for record windows of c["window"] blocks, if given)."""
@@ -319,22 +360,83 @@ def _run_sweep_case(seed, c):
             check_states(ck.cpu().numpy(), ck_ref, "checkpoint")
 
 
-@pytest.mark.parametrize("i", range(20))
+@pytest.mark.parametrize("i", _seeds(20))
 def test_seeded_sweep(i):
     c = _sweep_case(i)
     print(f"case: sweep {i} {c}", flush=True)
     _run_sweep_case(4000 + i, c)
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", _seeds(8))
 def test_seeded_sweep_many_slices(i):
     c = _sweep_case_many_slices(i)
     print(f"case: sweep (many slices) {i} N={len(c['lengths'])} {c}", flush=True)
     _run_sweep_case(4100 + i, c)
 
 
-@pytest.mark.parametrize("i", range(10))
+@pytest.mark.parametrize("i", _seeds(10))
 def test_seeded_sweep_record_windows(i):
     c = _sweep_case_windows(i)
     print(f"case: sweep (record windows) {i} {c}", flush=True)
     _run_sweep_case(4200 + i, c)
+
+
+@pytest.mark.parametrize("i", _seeds(6))
+def test_seeded_sweep_large(i):
+    c = _sweep_case_large(i)
+    print(f"case: sweep (large) {i} N={len(c['lengths'])} tokens={sum(c['lengths'])} {c}", flush=True)
+    _run_sweep_case(4300 + i, c)
+
+
+def _decode_case(i):
+    rng = np.random.default_rng(6000 + i)
+    N, H = int(rng.integers(1, 300)), int(rng.integers(1, 9))
+    T = 1 if rng.random() < 0.25 else int(rng.integers(2, 17))
+    return dict(N=N, T=T, H=H, D=int(rng.choice([16, 128])), bf16=bool(rng.integers(0, 2)),
+                g_min=float(rng.choice([LN_HALF, -1.0, -2.5, -5.0, -8.0])),
+                step=bool(T == 1 and rng.random() < 0.5), unclamped=bool(rng.random() < 0.5),
+                accept=bool(rng.random() < 0.6), seed=int(rng.integers(0, 1 << 30)))
+
+
+@pytest.mark.parametrize("i", _seeds(12))
+def test_seeded_decode_sweep(i):
+    """decode_step (T = 1) or decode_tokens against T oracle token steps:
+    every output, and the committed state after accept[n] tokens (accept
+    drawn from [-2, T + 2], clamped to [0, T] by the entry point)."""
+    c = _decode_case(i)
+    print(f"case: decode sweep {i} {c}", flush=True)
+    N, T, H, D = c["N"], c["T"], c["H"], c["D"]
+    rng = np.random.default_rng(c["seed"])
+    d = make_inputs(N * T, H, D, seed=6500 + i, lengths=[T] * N, initial_state=True, bf16=c["bf16"])
+    g = d.g
+    if c["unclamped"]:
+        g = rng.choice(np.append(GATE_VALUES, np.float32(-9.0)), size=g.shape).astype(np.float32)
+    shp = lambda a: np.ascontiguousarray(a.reshape(N, T, *a.shape[1:]))
+    q, k, v, g, beta = map(shp, (d.q, d.k, d.v, g, d.beta))
+    states = [d.initial_state.astype(np.float64)]
+    o_ref = np.zeros((N, T, H, D))
+    for t in range(T):
+        o_ref[:, t], st = reference.decode(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], states[-1],
+                                           scale=0.5, g_min=c["g_min"])
+        states.append(st)
+    dt = torch.bfloat16 if c["bf16"] else torch.float32
+    state = to_dev(d.initial_state)
+    accept = rng.integers(-2, T + 3, size=N).astype(np.int32) if c["accept"] and not c["step"] else None
+    if c["step"]:
+        o = kda.decode_step(to_dev(q[:, 0], dt), to_dev(k[:, 0], dt), to_dev(v[:, 0], dt), to_dev(g[:, 0]),
+                            to_dev(beta[:, 0]), state, scale=0.5, g_min=c["g_min"])[:, None]
+    else:
+        o = kda.decode_tokens(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), to_dev(g), to_dev(beta), state,
+                              accept=None if accept is None else torch.tensor(accept, device=DEV),
+                              scale=0.5, g_min=c["g_min"])
+    torch.cuda.synchronize()
+    o, S = _host(o), state.cpu().numpy()
+    for n, h in np.ndindex(N, H):
+        err = rel_err(o[n, :, h], o_ref[n, :, h])
+        assert err <= O_TOL, f"o seq {n} head {h}: rel err {err:.3e}"
+    for n in range(N):
+        a = T if accept is None else min(max(int(accept[n]), 0), T)
+        if a == 0:
+            assert np.array_equal(S[n], d.initial_state[n]), f"seq {n}: state changed with accept 0"
+        else:
+            check_states(S[n:n + 1], states[a][n:n + 1], f"state seq {n} after {a}")
