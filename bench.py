@@ -44,6 +44,7 @@ from gated_delta_rule_109_amd.workloads import make_inputs, make_inputs_device, 
 # call); used for roofline.traffic only while it matches the current kernel
 # sources.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "kda_prefill_b1_h32_t131072_hbm_traffic.md")
+VARLEN_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "kda_prefill_varlen16_h32_hbm_traffic.md")
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
@@ -182,6 +183,8 @@ def prefill_record(name, T, H, D, ms, n_seqs=1, init=False, n_ckpt=0, traffic=No
     if flops is not None:
         rec["model_tflops"] = round(flops / (ev_ms * 1e-3) / 1e12, 2)
         rec["model_mfma_frac"] = round(flops / (ev_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+    if traffic is not None:   # counter-measured HBM bytes per call, while they match the sources
+        rec["traffic"] = traffic["bytes_per_call"]
     return rec
 
 
@@ -304,7 +307,7 @@ def bench_varlen(args, dev, flush):
                          max(args.warmup // 5, 2), flush)
     return {"prefill_varlen": prefill_record(
         f"16 packed sequences, {sum(vl)} tokens (longest {max(vl)}), H=32, D=128, cached initial states",
-        sum(vl), H, D, vts, n_seqs=len(vl), init=True)}
+        sum(vl), H, D, vts, n_seqs=len(vl), init=True, traffic=profiling.read_record(VARLEN_TRAFFIC_PROFILE))}
 
 
 def bench_prefill_1m(args, dev, flush):

@@ -81,9 +81,11 @@ def prefill_kernels(heads, blocks, units, num_seqs=None):
     return tuple(out.items())
 
 
-# B = 1, H = 32, T = 131072 (4096 blocks) and T = 8192 (256 blocks)
+# B = 1, H = 32, T = 131072 (4096 blocks) and T = 8192 (256 blocks); 16 packed
+# sequences of 87,687 tokens (2748 blocks), H = 32
 PREFILL_LONG = prefill_kernels(32, 4096, 32)
 PREFILL_8K = prefill_kernels(32, 256, 32)
+PREFILL_VARLEN = prefill_kernels(32, 2748, 16 * 32, num_seqs=16)
 PREFILL_KERNELS = PREFILL_LONG
 # one kda_decode_step over 256 sequences x 32 heads at D = 128 (one workgroup of
 # 256 threads per head)
@@ -93,6 +95,8 @@ WORKLOADS = {
                 "bf16 q/k/v)", "kda_prefill_chunked"),
     "prefill_8k": (PREFILL_8K, "KDA prefill HBM traffic (B=1, H=32, T=8192, D=128, bf16 q/k/v)",
                    "kda_prefill_chunked"),
+    "varlen": (PREFILL_VARLEN, "KDA prefill HBM traffic (16 packed sequences, 87687 tokens, H=32, D=128, "
+               "cached initial states, bf16 q/k/v)", "kda_prefill_chunked"),
     "decode": (DECODE_KERNELS, "KDA decode HBM traffic (256 sequences x 32 heads, D=128, one token, bf16 q/k/v)",
                "kda_decode_step"),
 }
