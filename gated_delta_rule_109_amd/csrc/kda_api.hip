@@ -50,7 +50,6 @@ constexpr float kMinGateFloor = KDA_PREFILL_MIN_G_FLOOR;
 static_assert(KDA_CHUNK * -KDA_PREFILL_MIN_G_FLOOR * 1.4426950408889634f < 120.f,
               "decay span of a chunk");
 
-// Every tensor pointer must be 16-byte aligned (NULL passes).
 // Options: NULL, or known flag bits, a known gate layout and a usable epsilon.
 bool options_ok(const kda_options* opt) {
   if (!opt) return true;
@@ -74,6 +73,7 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, int dtype, 
                         float* checkpoints, void* o, void* workspace, size_t workspace_bytes,
                         bool use_scratch, const kda_options* opt, hipStream_t stream);
 
+// Every tensor pointer must be 16-byte aligned (NULL passes).
 bool aligned16(std::initializer_list<const void*> ps) {
   for (const void* p : ps)
     if ((uintptr_t)p & 15) return false;
