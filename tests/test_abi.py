@@ -159,6 +159,13 @@ def test_prefill_argument_errors(L):
     assert _prefill_status(L, g_min=float("nan")) == E.KDA_ERR_INVALID_ARG
     empty = (ctypes.c_int32 * 1)(0)
     assert _prefill_status(L, N=0, cu_host=ctypes.cast(empty, ctypes.POINTER(ctypes.c_int32))) == E.KDA_OK
+    as_ptr = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_int32))
+    assert _prefill_status(L, N=-1) == E.KDA_ERR_INVALID_ARG
+    assert _prefill_status(L, cu_host=as_ptr((ctypes.c_int32 * 3)(4, 20, 32))) == E.KDA_ERR_INVALID_ARG  # cu[0] != 0
+    # token-heads past INT32_MAX (2^30 tokens x 4 heads): refused before any device work
+    big = (ctypes.c_int32 * 2)(0, 1 << 30)
+    assert _prefill_status(L, N=1, cu_host=as_ptr(big)) == E.KDA_ERR_INVALID_ARG
+    assert _prefill_status(L, N=1, H=1, cu_host=as_ptr(big)) == E.KDA_ERR_WORKSPACE   # within range: sizes next
 
 
 def test_noalloc_prefill_errors_before_any_device_work(L):
