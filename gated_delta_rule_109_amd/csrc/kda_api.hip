@@ -109,6 +109,9 @@ int64_t kda_prefill_num_checkpoints(const int32_t* cu_seqlens_host, int32_t num_
 size_t kda_prefill_workspace_size_window(int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t Dk,
                                          int32_t Dv, int64_t window_blocks) {
   if (num_seqs < 0 || total_tokens < 0 || H <= 0 || !supported_dims(Dk, Dv) || window_blocks <= 0) return 0;
+  // shapes the prefill refuses (token-heads or 16-column slices past INT32_MAX)
+  if (total_tokens > INT32_MAX || total_tokens * H > INT32_MAX || (int64_t)num_seqs * H * (Dv / 16) > INT32_MAX)
+    return 0;
   // sum_n ceil(L_n / 32) <= sum_n (L_n / 32 + 1) for any lengths with this total
   const int64_t max_blocks = total_tokens / kda::kBlockTokens + num_seqs;
   if (max_blocks > INT32_MAX) return 0;

@@ -145,12 +145,14 @@ int64_t kda_prefill_num_checkpoints(const int32_t* cu_seqlens_host, int32_t num_
                                     int32_t ckpt_interval);
 
 /* Bytes of device workspace for kda_prefill_chunked on num_seqs sequences of
- * total_tokens packed tokens with H heads (0 if the arguments are invalid).
- * The workspace holds per-sequence and per-block tables (16 bytes per
- * 32-token block) and the per-block decayed operands of the chunked form
- * ("records": 47 KiB per 32-token block and head at D = 128, about 1.5 KiB per
- * token and head), sized for the most blocks any split of total_tokens into
- * num_seqs sequences can have, total_tokens / 32 + num_seqs. The record space
+ * total_tokens packed tokens with H heads (0 if the arguments are invalid
+ * or describe a call kda_prefill_chunked refuses: total_tokens * H or
+ * num_seqs * H * (Dv / 16) above INT32_MAX). The workspace holds
+ * per-sequence and per-block tables (16 bytes per 32-token block) and the
+ * per-block decayed operands of the chunked form ("records": 47 KiB per
+ * 32-token block and head at D = 128, about 1.5 KiB per token and head),
+ * sized for the most blocks any split of total_tokens into num_seqs
+ * sequences can have, total_tokens / 32 + num_seqs. The record space
  * is capped at KDA_PREFILL_RECORD_CAP_BYTES: a call with more records runs in
  * windows of consecutive blocks, preparing and consuming one window's records
  * at a time, so the workspace stops growing with T there (the tables still

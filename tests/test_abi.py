@@ -121,6 +121,10 @@ def test_workspace_size_windows(L):
     assert kda.workspace_size(1, 64, 2, 16, window_blocks=1) < kda.workspace_size(1, 64, 2, 16)
     assert kda.workspace_size(1, 64, 2, 128, window_blocks=0) == 0
     assert kda.workspace_size(1, 64, 2, 128, window_blocks=-3) == 0
+    # shapes the prefill refuses get no size: token-heads past INT32_MAX
+    assert kda.workspace_size(1, 1 << 30, 4, 128) == 0
+    assert kda.workspace_size(1, 1 << 31, 1, 128) == 0
+    assert kda.workspace_size(1, (1 << 31) - 1, 1, 128) > 0
 
 
 def _prefill_status(L, **over):
